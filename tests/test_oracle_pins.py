@@ -1,0 +1,380 @@
+"""Pins of the CPU oracle to facts fixed outside the oracle itself.
+
+Each test checks the oracle against something it does not compute: a value
+printed on the web page "Random-rotation quantization" (fixtures under
+``tests/golden`` with their citation), a closed form, a library routine
+(scipy's Sylvester Hadamard matrix, numerical integration, numpy's fp16
+conversion), an invariant, or brute force on tiny inputs.  Together they are
+chosen so a dropped term, a wrong sign or index, or a transposed operand
+anywhere in the oracle fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.integrate
+import scipy.linalg
+import scipy.special
+import scipy.stats
+
+import oracle
+
+
+def _read_golden(path):
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, *v = line.split()
+            vals[k] = [float(t) for t in v]
+    return vals
+
+
+def unpack_fields(codes, width, d):
+    """Independent LSB-first unpacker: field i of a row at bits [w*i, w*i+w)."""
+    bits = np.unpackbits(codes, axis=-1, bitorder="little")[..., : width * d]
+    bits = bits.reshape(*codes.shape[:-1], d, width).astype(np.int64)
+    return (bits << np.arange(width)).sum(-1)
+
+
+def dense_rotation(d, seed):
+    """H D as a dense matrix, H from scipy (Sylvester order), D from the oracle."""
+    return scipy.linalg.hadamard(d).astype(np.float64) * oracle.signs(seed, d)[None, :].astype(np.float64)
+
+
+# ---------------------------------------------------------------- generator
+def test_splitmix64_known_answer():
+    # Published first outputs of SplitMix64 started from state 0.
+    assert oracle.splitmix64_stream(0, 3) == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4,
+                                             0x06C45D188009454F]
+    # sign i is the top bit of output i (set -> -1)
+    assert list(oracle.signs(0, 3)) == [-1, 1, 1]
+
+
+def test_signs_deterministic_and_balanced():
+    a = oracle.signs(42, 4096)
+    assert np.array_equal(a, oracle.signs(42, 4096))
+    assert not np.array_equal(a, oracle.signs(43, 4096))
+    assert set(np.unique(a)) <= {-1, 1}
+    frac = np.mean([(oracle.signs(s, 1024) > 0).mean() for s in range(64)])
+    assert abs(frac - 0.5) < 0.01
+    # prefix property: the first d signs do not depend on d
+    assert np.array_equal(oracle.signs(7, 128), oracle.signs(7, 1024)[:128])
+
+
+# ---------------------------------------------------------------- Hadamard
+@pytest.mark.parametrize("d", [1, 2, 4, 8, 16, 32, 64])
+def test_fwht_matches_dense_sylvester(d):
+    rng = np.random.default_rng(d)
+    v = rng.standard_normal((5, d))
+    H = scipy.linalg.hadamard(d).astype(np.float64)
+    np.testing.assert_allclose(oracle.fwht(v), v @ H.T, rtol=0, atol=1e-12)
+
+
+def test_fwht_d2_and_orthogonality():
+    np.testing.assert_array_equal(oracle.fwht(np.eye(2)), [[1, 1], [1, -1]])
+    for d in (8, 64, 256):
+        H = oracle.fwht(np.eye(d))
+        np.testing.assert_array_equal(H @ H.T, d * np.eye(d))          # H H^T = d I exactly
+        P = H / math.sqrt(d)
+        np.testing.assert_allclose(P @ P, np.eye(d), atol=1e-12)        # (H/sqrt d)^2 = I
+
+
+@pytest.mark.parametrize("d", [16, 128, 1024, 4096])
+def test_rotation_preserves_norm(d):
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((8, d)).astype(np.float32)
+    _, norms, y = oracle.quantize(x, 4, 11, want_y=True)
+    nx = np.linalg.norm(x.astype(np.float64), axis=1)
+    # y = H D x / ||x||, so ||y|| = sqrt(d) exactly when Pi is orthogonal
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), math.sqrt(d), rtol=1e-12)
+    np.testing.assert_allclose(norms, nx.astype(np.float32), rtol=0)
+
+
+# ---------------------------------------------------------- rotated marginal
+def test_rotated_coordinate_mean_and_std(golden_dir):
+    """[RRQ 'Why rotation works']: mean 0, std 1/sqrt(d) per coordinate."""
+    g = _read_golden(golden_dir + "/rrq_rotation_stats.txt")
+    d, trials = 64, 4000
+    x = np.zeros((1, d), np.float32)
+    x[0, 5] = 0.6
+    x[0, 40] = 0.8  # unit vector with its energy in two channels
+    xs = np.repeat(x, 1, axis=0)
+    vals = np.stack([oracle.quantize(xs, 1, s, want_y=True)[2][0] / math.sqrt(d) for s in range(trials)])
+    # over seeds, every coordinate of Pi x has mean 0 and variance ||x||^2 / d
+    assert abs(vals.mean()) < 4.0 / math.sqrt(trials * d) * 1.0
+    np.testing.assert_allclose(vals.var(axis=0).mean(), 1.0 / d, rtol=0.03)
+    # page value: std ~0.032 at d ~ 1000; at d = 1024 the exact value is 1/32
+    d2 = 1024
+    rng = np.random.default_rng(3)
+    x2 = rng.standard_normal((64, d2)).astype(np.float32)
+    y2 = oracle.quantize(x2, 1, 5, want_y=True)[2] / math.sqrt(d2)
+    assert abs(y2.std() - g["std"][0]) < 0.0015
+    assert abs(y2.mean() - g["mean"][0]) < 0.002
+
+
+def _beta_marginal_pdf(x, d):
+    # the page's density of one coordinate on the unit sphere (garbled
+    # "\sqrt{\pi},\Gamma" read as sqrt(pi) * Gamma)
+    c = math.exp(math.lgamma(d / 2) - math.lgamma((d - 1) / 2)) / math.sqrt(math.pi)
+    return c * (1.0 - x * x) ** ((d - 3) / 2)
+
+
+@pytest.mark.parametrize("d", [8, 16, 128])
+def test_beta_marginal_ks(d):
+    """Gaussian inputs rotate to a uniform point on the sphere exactly, so one
+    coordinate of Pi x / ||x|| follows the page's Beta marginal."""
+    total, _ = scipy.integrate.quad(_beta_marginal_pdf, -1, 1, args=(d,))
+    assert abs(total - 1.0) < 1e-9
+    rng = np.random.default_rng(d)
+    x = rng.standard_normal((3000, d)).astype(np.float64).astype(np.float32)
+    y = oracle.quantize(x, 2, 99, want_y=True)[2]
+    sample = y[:, d // 3] / math.sqrt(d)
+
+    def cdf(t):
+        t = np.atleast_1d(t)
+        return np.array([scipy.integrate.quad(_beta_marginal_pdf, -1, min(max(v, -1), 1), args=(d,))[0]
+                         for v in t])
+
+    p = scipy.stats.kstest(sample, cdf).pvalue
+    assert p > 1e-3
+
+
+# ---------------------------------------------------------------- codebook
+def test_lloyd_max_page_values(golden_dir):
+    g = _read_golden(golden_dir + "/rrq_codebook.txt")
+    lv1, th1, mse1, _ = oracle.lloyd_max(1)
+    assert abs(lv1[1] - g["sqrt_2_over_pi_1bit"][0]) < 1e-3
+    np.testing.assert_allclose(lv1, [-math.sqrt(2 / math.pi), math.sqrt(2 / math.pi)], atol=1e-13)
+    assert th1[0] == 0.0
+    assert abs(mse1 - (1 - 2 / math.pi)) < 1e-13      # 1-bit Gaussian MSE, closed form
+    lv2, th2, _, _ = oracle.lloyd_max(2)
+    np.testing.assert_allclose(lv2[2:], g["levels_2bit_positive"], atol=1e-3)
+    np.testing.assert_allclose(lv2[:2], -lv2[2:][::-1], atol=0)
+
+
+def test_lloyd_max_textbook_table(golden_dir):
+    g = _read_golden(golden_dir + "/max1960_lloyd_max.txt")
+    for b in (3, 4):
+        lv, th, mse, _ = oracle.lloyd_max(b)
+        np.testing.assert_allclose(lv[1 << (b - 1):], g["levels_%dbit_positive" % b], atol=1.1e-3)
+        assert abs(mse - g["mse_%dbit" % b][0]) < 1e-5
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_lloyd_max_fixed_point_by_quadrature(b):
+    """Centroid and nearest-neighbour conditions, checked by numerical
+    integration rather than the oracle's closed-form cell means."""
+    lv, th, mse, _ = oracle.lloyd_max(b)
+    K = 1 << b
+    edges = np.concatenate([[-np.inf], th, [np.inf]])
+    phi = scipy.stats.norm.pdf
+    dist = 0.0
+    for k in range(K):
+        a, c = edges[k], edges[k + 1]
+        p, _ = scipy.integrate.quad(phi, a, c)
+        m1, _ = scipy.integrate.quad(lambda z: z * phi(z), a, c)
+        assert abs(m1 / p - lv[k]) < 1e-9
+        e, _ = scipy.integrate.quad(lambda z: (z - lv[k]) ** 2 * phi(z), a, c)
+        dist += e
+    np.testing.assert_allclose(th, 0.5 * (lv[1:] + lv[:-1]), atol=1e-15)
+    assert abs(dist - mse) < 1e-9
+    assert np.all(np.diff(lv) > 0)
+
+
+def test_one_bit_mse_monte_carlo():
+    z = np.random.default_rng(7).standard_normal(2_000_000)
+    e = np.mean((z - math.sqrt(2 / math.pi) * np.sign(z)) ** 2)
+    assert abs(e - (1 - 2 / math.pi)) < 2e-3
+
+
+# ---------------------------------------------------------------- encoder
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("d", [8, 16, 32])
+@pytest.mark.parametrize("dt", [np.float32, np.float16])
+def test_quantize_bruteforce(bits, d, dt):
+    rng = np.random.default_rng(bits * 100 + d)
+    x = (rng.standard_normal((40, d)) * 3).astype(dt)
+    seed = 1234 + d
+    codes, norms = oracle.quantize(x, bits, seed)
+    lv, _, _, _ = oracle.lloyd_max(bits)
+    xd = x.astype(np.float64)
+    nx = np.linalg.norm(xd, axis=1)
+    y = xd @ dense_rotation(d, seed).T / nx[:, None]
+    brute = np.argmin(np.abs(y[..., None] - lv[None, None, :]), axis=-1)
+    got = unpack_fields(codes, bits, d)
+    np.testing.assert_array_equal(got, brute)
+    np.testing.assert_array_equal(norms, nx.astype(np.float32))
+
+
+def test_quantize_zero_vector_and_ties():
+    d = 16
+    x = np.zeros((2, d), np.float32)
+    for bits in (1, 2, 4):
+        codes, norms = oracle.quantize(x, bits, 3)
+        assert np.all(unpack_fields(codes, bits, d) == (1 << bits) // 2)
+        assert np.all(norms == 0)
+        out = oracle.dequantize(codes, norms, d, bits, 3)
+        assert np.all(out == 0)
+    # a vector whose rotation has exact zeros: y = 0 goes up to code K/2
+    x = np.zeros((1, d), np.float32)
+    s = oracle.signs(3, d)
+    x[0, 0] = s[0]
+    x[0, 1] = s[1]          # H D x = H (e0 + e1): half the coordinates are 0
+    codes, _ = oracle.quantize(x, 2, 3)
+    c = unpack_fields(codes, 2, d)[0]
+    y = oracle.fwht(np.array([[1.0, 1.0] + [0.0] * (d - 2)]))[0]
+    assert np.all(c[y == 0] == 2)
+
+
+def test_fp16_codec_against_numpy():
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = allbits.view(np.float16).astype(np.float64)
+    ours = np.array([oracle.f16_to_f64(int(b)) for b in allbits])
+    finite = np.isfinite(ref)
+    np.testing.assert_array_equal(ours[finite], ref[finite])
+    assert np.all(np.isnan(ours[np.isnan(ref)]))
+    rng = np.random.default_rng(0)
+    v = np.concatenate([rng.standard_normal(3000) * s for s in (1e-7, 1e-5, 1, 100, 3e4)]
+                       + [np.array([65504.0, 65519.99, 65520.0, 2.0 ** -25, 2.0 ** -24 * 1.5, -0.0])])
+    ours = np.array([oracle.f64_to_f16(float(t)) for t in v], dtype=np.uint16)
+    np.testing.assert_array_equal(ours, v.astype(np.float16).view(np.uint16))
+
+
+# ---------------------------------------------------------------- decoders
+@pytest.mark.parametrize("bits", [1, 2, 4])
+def test_dequantize_dense_and_rotated_domain_error(bits):
+    d, seed = 64, 77
+    rng = np.random.default_rng(bits)
+    x = rng.standard_normal((20, d)).astype(np.float32)
+    codes, norms = oracle.quantize(x, bits, seed)
+    lv, _, _, _ = oracle.lloyd_max(bits)
+    c = lv[unpack_fields(codes, bits, d)]
+    R = dense_rotation(d, seed)                      # H D
+    xt = (c * (norms.astype(np.float64)[:, None] / d)) @ R   # D H z = (H D)^T z
+    got = oracle.dequantize(codes, norms, d, bits, seed).astype(np.float64)
+    np.testing.assert_allclose(got, xt, rtol=0, atol=1e-6 * np.abs(xt).max())
+    # ||x - x~|| in the original domain equals ||Pi x - y^|| in the rotated one
+    xd = x.astype(np.float64)
+    Pi = R / math.sqrt(d)
+    yhat = c * norms.astype(np.float64)[:, None] / math.sqrt(d)
+    np.testing.assert_allclose(np.linalg.norm(xd - xt, axis=1),
+                               np.linalg.norm(xd @ Pi.T - yhat, axis=1), rtol=1e-9)
+    f16 = oracle.dequantize(codes, norms, d, bits, seed, np.float16)
+    np.testing.assert_array_equal(f16, xt.astype(np.float16))
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_gaussian_distortion_matches_lloyd_max(bits):
+    """For Gaussian inputs Pi x / ||x|| is uniform on the sphere and the
+    normalized MSE approaches D_b (d large)."""
+    d = 1024
+    x = np.random.default_rng(bits).standard_normal((200, d)).astype(np.float32)
+    codes, norms = oracle.quantize(x, bits, 5)
+    xt = oracle.dequantize(codes, norms, d, bits, 5).astype(np.float64)
+    xd = x.astype(np.float64)
+    nmse = np.mean(np.sum((xd - xt) ** 2, 1) / np.sum(xd ** 2, 1))
+    _, _, mse, _ = oracle.lloyd_max(bits)
+    assert abs(nmse / mse - 1) < 0.03
+
+
+@pytest.mark.parametrize("unbiased", [False, True])
+def test_drive_closed_forms(unbiased):
+    d, seed = 256, 21
+    rng = np.random.default_rng(4)
+    x = (rng.standard_t(3, size=(30, d))).astype(np.float32)
+    b, S = oracle.sign_quantize(x, unbiased, seed)
+    xd = x.astype(np.float64)
+    Pi = dense_rotation(d, seed) / math.sqrt(d)
+    Rx = xd @ Pi.T
+    np.testing.assert_array_equal(unpack_fields(b, 1, d), (Rx >= 0).astype(np.int64))
+    l1 = np.abs(Rx).sum(1)
+    S_ref = (xd ** 2).sum(1) / l1 if unbiased else l1 / d
+    np.testing.assert_allclose(S, S_ref.astype(np.float32), rtol=1e-6)
+    xh = oracle.sign_dequantize(b, S, d, seed).astype(np.float64)
+    S64 = S.astype(np.float64)
+    sigma = np.where(Rx >= 0, 1.0, -1.0)
+    np.testing.assert_allclose(xh, (S64[:, None] * sigma) @ Pi, rtol=0, atol=1e-6 * np.abs(xh).max())
+    if unbiased:
+        # <x, x^> = S ||Rx||_1 = ||x||^2
+        np.testing.assert_allclose((xd * xh).sum(1), (xd ** 2).sum(1), rtol=2e-6)
+    else:
+        # ||x - x^||^2 = ||x||^2 - ||Rx||_1^2 / d
+        np.testing.assert_allclose(((xd - xh) ** 2).sum(1), (xd ** 2).sum(1) - l1 ** 2 / d, rtol=2e-5)
+
+
+def test_drive_unbiased_mean_over_seeds():
+    d, trials = 32, 3000
+    x = np.random.default_rng(9).standard_normal((1, d)).astype(np.float32)
+    acc = np.zeros(d)
+    for s in range(trials):
+        b, S = oracle.sign_quantize(x, True, 1000 + s)
+        acc += oracle.sign_dequantize(b, S, d, 1000 + s)[0]
+    err = np.linalg.norm(acc / trials - x[0]) / np.linalg.norm(x[0])
+    assert err < 4.0 / math.sqrt(trials) * math.sqrt(d) / 4
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_residual_chain_closed_forms(bits):
+    d, seed = 128, 31
+    rng = np.random.default_rng(bits + 50)
+    x = rng.standard_normal((25, d)).astype(np.float32)
+    x[:, 7] *= 30
+    codes, sg, norms, rs = oracle.residual_quantize(x, bits, seed)
+    c1, n1 = oracle.quantize(x, bits - 1, seed)
+    np.testing.assert_array_equal(codes, c1)          # stage 1 = (b-1)-bit encoder
+    np.testing.assert_array_equal(norms, n1)
+    lv, _, _, _ = oracle.lloyd_max(bits - 1)
+    xd = x.astype(np.float64)
+    R = dense_rotation(d, seed)
+    nx = np.linalg.norm(xd, axis=1)
+    cz = lv[unpack_fields(codes, bits - 1, d)]
+    r = (xd @ R.T - nx[:, None] * cz) / math.sqrt(d)    # Pi (x - x~)
+    np.testing.assert_array_equal(unpack_fields(sg, 1, d), (r >= 0).astype(np.int64))
+    Sr = (r ** 2).sum(1) / np.abs(r).sum(1)
+    np.testing.assert_allclose(rs, Sr.astype(np.float32), rtol=1e-6)
+    xh = oracle.residual_dequantize(codes, sg, norms, rs, d, bits, seed).astype(np.float64)
+    r2, r1 = (r ** 2).sum(1), np.abs(r).sum(1)
+    np.testing.assert_allclose(((xd - xh) ** 2).sum(1), r2 * (d * r2 / r1 ** 2 - 1), rtol=1e-4)
+    # forcing the stage-1 codes to the oracle's own gives identical results
+    f = oracle.residual_quantize(x, bits, seed, forced_codes=codes)
+    for a, b in zip(f, (codes, sg, norms, rs)):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_residual_chain_removes_inner_product_shrinkage():
+    """[RRQ 'Bias vs unbiasedness']: MSE codes shrink inner products by about
+    1 - D_b; the residual chain is close to unbiased (diagnostic, loose)."""
+    d, n = 256, 400
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    q = rng.standard_normal((n, d))
+    xd = x.astype(np.float64)
+    true = (q * xd).sum(1)
+    ratios_mse, ratios_res = [], []
+    for s in range(6):
+        c, nr = oracle.quantize(x, 2, 300 + s)
+        xt = oracle.dequantize(c, nr, d, 2, 300 + s).astype(np.float64)
+        ratios_mse.append(((q * xt).sum(1) * true).sum() / (true ** 2).sum())
+        c3, s3, n3, r3 = oracle.residual_quantize(x, 3, 300 + s)
+        xh = oracle.residual_dequantize(c3, s3, n3, r3, d, 3, 300 + s).astype(np.float64)
+        ratios_res.append(((q * xh).sum(1) * true).sum() / (true ** 2).sum())
+    _, _, D2, _ = oracle.lloyd_max(2)
+    assert abs(np.mean(ratios_mse) - (1 - D2)) < 0.03
+    assert abs(np.mean(ratios_res) - 1.0) < abs(np.mean(ratios_mse) - 1.0)
+
+
+def test_score_equals_dense_definition():
+    d, bits, seed = 128, 4, 46
+    rng = np.random.default_rng(8)
+    keys = rng.standard_normal((50, d)).astype(np.float32)
+    q = rng.standard_normal((7, d)).astype(np.float32)
+    codes, norms = oracle.quantize(keys, bits, seed)
+    dense = oracle.score_dense(q, codes, norms, d, bits, seed)
+    lv, _, _, _ = oracle.lloyd_max(bits)
+    xt = (lv[unpack_fields(codes, bits, d)] * norms.astype(np.float64)[:, None] / d) @ dense_rotation(d, seed)
+    np.testing.assert_allclose(dense, q.astype(np.float64) @ xt.T, rtol=0, atol=1e-12 * np.abs(dense).max())
+    fast = oracle.score(q, codes, norms, d, bits, seed)
+    np.testing.assert_allclose(fast, dense, rtol=2e-7, atol=1e-9 * np.abs(dense).max())
