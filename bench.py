@@ -1,0 +1,266 @@
+"""Benchmark: RHT 4-bit quantize + dequantize of a KV-cache block on one MI355X.
+
+Workload: K and V, each 32 layers x 8 KV heads x 32768 tokens x d = 128 fp16
+(n = 8,388,608 vectors each; N(0,1) with one seeded outlier channel x20 and
+per-vector log-normal(0, 0.5) norms), randomized Hadamard transform + 4-bit
+N(0,1) Lloyd-Max codes + one fp32 norm per vector, then decode back to fp16.
+One step = quantize K, quantize V, dequantize K, dequantize V; inputs are
+resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is vectors per second through the whole step
+(every vector is encoded and decoded once per step).  `roofline` is for the
+slower of the two kernels, from HIP events on the stream the kernels run on;
+algorithmic bytes are 256 B in + 64 B codes + 4 B norm per vector for the
+encoder and the same 324 B for the decoder.  `cpu_baseline` times the oracle
+(single thread) on a bounded sample of the same rows.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BYTES_PER_VECTOR = 128 * 2 + 64 + 4  # fp16 row + 4-bit codes + fp32 norm
+COPY_BYTES = 8388608 * BYTES_PER_VECTOR // 2  # plain copy moving one launch's bytes
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ("rht_kernels.hip", "rht_api.cpp", "rht_internal.h"):
+        with open(os.path.join(ROOT, "rotation_vector_quantization_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch from committed rocprofv3 PMC summaries, only if
+    they were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic_c2_kv.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def traffic_from(fetch_dir, write_dir):
+    """Build profiles/traffic_c2_kv.json from two rocprofv3 --pmc runs of this
+    script (FETCH_SIZE, then WRITE_SIZE; csv output).  Counters are KiB per
+    dispatch; each is scaled by the factor that maps the plain copy kernel's
+    reading to its known byte count (COPY_BYTES read and written)."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for row in csv.DictReader(fh):
+                    if row.get("Counter_Name") != counter:
+                        continue
+                    name = row.get("Kernel_Name", "")
+                    vals.setdefault(name, []).append(float(row["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+
+    def pick(vals, key):
+        hits = [v for k, v in vals.items() if key in k]
+        if not hits:
+            raise SystemExit("no %s dispatches in the counter files" % key)
+        allv = [x for h in hits for x in h]
+        return sum(allv) / len(allv)
+
+    copy_key = "copy"  # torch's elementwise copy kernel
+    f_copy, w_copy = pick(fetch, copy_key) * 1024, pick(write, copy_key) * 1024
+    kf, kw = COPY_BYTES / f_copy, COPY_BYTES / w_copy
+    rec = {"source_digest": source_digest(), "copy_bytes_each_way": COPY_BYTES,
+           "fetch_scale": kf, "write_scale": kw, "kernels": {}}
+    for key in ("k_quantize", "k_dequantize"):
+        fb, wb = pick(fetch, key) * 1024 * kf, pick(write, key) * 1024 * kw
+        rec["kernels"][key] = {"fetch_bytes": fb, "write_bytes": wb, "hbm_bytes_per_launch": fb + wb,
+                               "algorithmic_bytes_per_launch": 8388608 * BYTES_PER_VECTOR}
+    out = os.path.join(ROOT, "profiles", "traffic_c2_kv.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+def cpu_baseline(rows):
+    import oracle
+    import testdata
+
+    w = testdata.WORKLOADS["c2k"]
+    x = testdata.generate(w, 0, rows)
+    t0 = time.perf_counter()
+    codes, norms = oracle.quantize(x, w.bits, w.rot_seed)
+    oracle.dequantize(codes, norms, w.d, w.bits, w.rot_seed, np.float16)
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "vectors/s", "cores": 1, "kind": "oracle",
+            "sample": "first %d K vectors of the KV-cache block, quantize + dequantize, "
+                      "single-threaded fp64 oracle (%.1f s)" % (rows, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-rows", type=int, default=1 << 20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_c2_kv.json from rocprofv3 PMC runs and exit")
+    args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: every vector is independent, and the multi-GPU "
+              "split (shard the vectors, replicate seed and codebook) is not built; use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import rotation_vector_quantization_amd as rht
+    import testdata
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rht.load()
+
+    wk, wv = testdata.WORKLOADS["c2k"], testdata.WORKLOADS["c2v"]
+    n, d, bits = wk.n, wk.d, wk.bits
+    print("generating K and V (%d x %d fp16 each)" % (n, d), file=sys.stderr, flush=True)
+    xk = torch.from_numpy(testdata.generate(wk)).to(dev)
+    xv = torch.from_numpy(testdata.generate(wv)).to(dev)
+    ck = torch.empty((n, d * bits // 8), dtype=torch.uint8, device=dev)
+    cv = torch.empty_like(ck)
+    nk = torch.empty((n,), dtype=torch.float32, device=dev)
+    nv = torch.empty_like(nk)
+    yk = torch.empty((n, d), dtype=torch.float16, device=dev)
+    yv = torch.empty_like(yk)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    def q(x, c, nr, w):
+        rht.rht_quantize(x.data_ptr(), rht.F16, n, d, bits, rht.SCALE_NORM, w.rot_seed,
+                         c.data_ptr(), nr.data_ptr(), sh)
+
+    def dq(c, nr, y, w):
+        rht.rht_dequantize(c.data_ptr(), nr.data_ptr(), n, d, bits, rht.SCALE_NORM, w.rot_seed,
+                           y.data_ptr(), rht.F16, sh)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        q(xk, ck, nk, wk)
+        q(xv, cv, nv, wv)
+        if ev is not None:
+            ev[1].record(stream)
+        dq(ck, nk, yk, wk)
+        dq(cv, nv, yv, wv)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+    q_ms = np.array([e[0].elapsed_time(e[1]) for e in evs]) / 2.0  # per launch
+    dq_ms = np.array([e[1].elapsed_time(e[2]) for e in evs]) / 2.0
+    # practical ceiling: a plain device copy moving the same bytes as one launch
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = c0.elapsed_time(c1) / 10
+    copy_gbs = 2 * COPY_BYTES / (copy_ms / 1e3) / 1e9
+    del src, dst
+
+    vectors_per_step = 2 * n
+    value = vectors_per_step / (ms_step / 1e3)
+
+    per_launch_bytes = n * BYTES_PER_VECTOR
+    kern = {"quantize": float(q_ms.mean()), "dequantize": float(dq_ms.mean())}
+    dom = max(kern, key=kern.get)
+    achieved = per_launch_bytes / (kern[dom] / 1e3) / 1e9
+    kname = {"quantize": "k_quantize", "dequantize": "k_dequantize"}[dom]
+    traffic = load_traffic(kname)
+
+    out = {
+        "metric": "vectors/s + achieved HBM GB/s (% of peak), RHT 4-bit quant/dequant d=128",
+        "value": value,
+        "unit": "vectors/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "KV-cache block: K and V, each 32 layers x 8 heads x 32768 tokens x d=128 "
+                        "fp16; RHT + 4-bit Lloyd-Max quantize, then dequantize to fp16",
+            "vectors_per_tensor": n, "d": d, "bits": bits, "io_dtype": "f16",
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+        },
+        "per_direction": {
+            "quantize": {"ms_per_launch": kern["quantize"],
+                         "vectors_per_s": n / (kern["quantize"] / 1e3),
+                         "GB_per_s": per_launch_bytes / (kern["quantize"] / 1e3) / 1e9,
+                         "frac_of_peak": per_launch_bytes / (kern["quantize"] / 1e3) / 1e9 / HBM_PEAK_GBS},
+            "dequantize": {"ms_per_launch": kern["dequantize"],
+                           "vectors_per_s": n / (kern["dequantize"] / 1e3),
+                           "GB_per_s": per_launch_bytes / (kern["dequantize"] / 1e3) / 1e9,
+                           "frac_of_peak": per_launch_bytes / (kern["dequantize"] / 1e3) / 1e9 / HBM_PEAK_GBS},
+        },
+        "copy_ceiling": {"GB_per_s": copy_gbs, "frac_of_peak": copy_gbs / HBM_PEAK_GBS,
+                         "bytes": 2 * COPY_BYTES, "kernel": "torch device copy"},
+        "wall_s_timed_region": wall,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("timing the CPU oracle on %d vectors" % args.cpu_rows, file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

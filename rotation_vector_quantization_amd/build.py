@@ -1,0 +1,51 @@
+"""Build librht.so in-tree: hipcc for gfx950, no JIT, no torch extension."""
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "librht.so")
+ARCH = os.environ.get("RHT_OFFLOAD_ARCH", "gfx950")
+
+# Packed fp32 instructions stay off: hipcc -O3 would otherwise form
+# v_pk_add/mul/fma_f32 from scalar float code.
+DEVICE_FLAGS = ["-O3", "-fPIC", "-std=c++17", "--offload-arch=" + ARCH,
+                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall"]
+HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines()
+                    if "is not a recognized feature for this target" not in l)
+    if r.returncode != 0:
+        raise RuntimeError("build failed: %s\n%s" % (" ".join(cmd), out))
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = [
+        ["hipcc"] + DEVICE_FLAGS + ["-c", os.path.join(CSRC, "rht_kernels.hip"),
+                                    "-o", os.path.join(BUILD, "rht_kernels.o")],
+        ["hipcc"] + HOST_FLAGS + ["-c", os.path.join(CSRC, "rht_api.cpp"),
+                                  "-o", os.path.join(BUILD, "rht_api.o")],
+    ]
+    with concurrent.futures.ThreadPoolExecutor(len(jobs)) as ex:
+        for out in ex.map(_run, jobs):
+            if verbose and out.strip():
+                print(out)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    _run(["hipcc", "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp,
+          os.path.join(BUILD, "rht_kernels.o"), os.path.join(BUILD, "rht_api.o")])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,309 @@
+// rht_api.cpp -- the C ABI of librht (declared in include/rht.h): argument
+// validation, the host-side codebook and rotation signs, and kernel dispatch.
+//
+// The codebook is the N(0,1) Lloyd-Max quantizer named on the web page
+// "Random-rotation quantization" ("History", EDEN item: computed once for the
+// standard normal; 1 bit +-sqrt(2/pi), 2 bits +-0.453, +-1.510).  It is solved
+// here on the positive half-line (the density is even, so the quantizer is
+// antisymmetric with 0 as its middle threshold), in double, then rounded to
+// fp32 for the kernels.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/rht.h"
+#include "rht_internal.h"
+
+namespace rht {
+namespace {
+
+struct FloatBook {
+    float lev[16];
+    float thr[16];
+};
+
+FloatBook g_books[5];
+std::once_flag g_books_once;
+
+// Upper-tail probability and density of N(0,1).
+double upper_tail(double t) { return std::isinf(t) ? 0.0 : 0.5 * std::erfc(t / std::sqrt(2.0)); }
+double density(double t) { return std::isinf(t) ? 0.0 : std::exp(-0.5 * t * t) / std::sqrt(2.0 * M_PI); }
+
+// Positive half of the 2^bits-level Lloyd-Max quantizer: h = 2^(bits-1)
+// levels p[0] < ... < p[h-1] with cells [b_j, b_{j+1}), b_0 = 0, b_h = inf,
+// b_j = (p[j-1] + p[j]) / 2.  Each level is its cell's conditional mean,
+// (density(b_j) - density(b_{j+1})) / (tail(b_j) - tail(b_{j+1})).
+void solve_half(int bits, double *p) {
+    const int h = 1 << (bits - 1);
+    for (int j = 0; j < h; ++j) p[j] = (j + 0.5) * 2.5 / h;
+    for (int it = 0; it < 200000; ++it) {
+        double edges[9];
+        edges[0] = 0.0;
+        for (int j = 1; j < h; ++j) edges[j] = 0.5 * (p[j - 1] + p[j]);
+        edges[h] = INFINITY;
+        double change = 0.0;
+        for (int j = 0; j < h; ++j) {
+            const double mass = upper_tail(edges[j]) - upper_tail(edges[j + 1]);
+            const double c = (density(edges[j]) - density(edges[j + 1])) / mass;
+            change = std::fmax(change, std::fabs(c - p[j]));
+            p[j] = c;
+        }
+        if (change < 1e-15) break;
+    }
+}
+
+void build_books() {
+    for (int bits = 1; bits <= 4; ++bits) {
+        const int h = 1 << (bits - 1), K = 2 * h;
+        double p[8];
+        solve_half(bits, p);
+        FloatBook &fb = g_books[bits];
+        std::memset(&fb, 0, sizeof(fb));
+        for (int j = 0; j < h; ++j) {
+            fb.lev[h + j] = (float)p[j];
+            fb.lev[h - 1 - j] = (float)-p[j];
+        }
+        fb.thr[h - 1] = 0.0f;
+        for (int j = 1; j < h; ++j) {
+            const float t = (float)(0.5 * (p[j - 1] + p[j]));
+            fb.thr[h - 1 + j] = t;
+            fb.thr[h - 1 - j] = -t;
+        }
+        (void)K;
+    }
+}
+
+const FloatBook &book(int bits) {
+    std::call_once(g_books_once, build_books);
+    return g_books[bits];
+}
+
+// Signs of D: top bit of the i-th SplitMix64 output (Steele, Lea, Flood 2014)
+// from state `seed`; a set bit means -1.
+void sign_words(uint64_t seed, int d, uint32_t *words) {
+    std::memset(words, 0, sizeof(uint32_t) * (size_t)((d + 31) / 32));
+    uint64_t state = seed;
+    for (int i = 0; i < d; ++i) {
+        state += 0x9E3779B97F4A7C15ULL;
+        uint64_t z = state;
+        z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+        z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+        z ^= z >> 31;
+        if (z >> 63) words[i >> 5] |= 1u << (i & 31);
+    }
+}
+
+bool pow2_dim(int32_t d) { return d >= kMinD && d <= kMaxD && (d & (d - 1)) == 0; }
+bool aligned(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Coordinate-to-lane layout of the MSE kernels: 1 (default) interleaves the
+// lanes of a vector in chunks that own one code word each; 0 gives every lane
+// one contiguous run.  RHT_LAYOUT overrides it (a tuning knob).
+int layout_choice() {
+    static const int v = [] {
+        const char *e = std::getenv("RHT_LAYOUT");
+        return e ? std::atoi(e) : 1;
+    }();
+    return v;
+}
+
+rht_status launched(hipError_t e) { return e == hipSuccess ? RHT_OK : RHT_E_DEVICE; }
+
+std::atomic<int> g_cu[64];
+
+}  // namespace
+
+int blocks_per_cu_cap() {
+    static const int v = [] {
+        const char *e = std::getenv("RHT_BLOCKS_PER_CU");
+        return e ? std::atoi(e) : 0;
+    }();
+    return v;
+}
+
+int device_cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = g_cu[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        g_cu[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+}  // namespace rht
+
+using namespace rht;
+
+extern "C" {
+
+int32_t rht_abi_version(void) { return RHT_ABI_VERSION; }
+
+const char *rht_status_str(rht_status s) {
+    switch (s) {
+    case RHT_OK: return "ok";
+    case RHT_E_NULL: return "null pointer";
+    case RHT_E_DIM: return "unsupported dimension d";
+    case RHT_E_BITS: return "unsupported bit width";
+    case RHT_E_DTYPE: return "unknown element type";
+    case RHT_E_MODE: return "unknown mode or mode/bits mismatch";
+    case RHT_E_ALIGN: return "device pointer not 16-byte aligned";
+    case RHT_E_COUNT: return "negative count or m out of range";
+    case RHT_E_DEVICE: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+rht_status rht_codebook(int32_t bits, float *levels, float *thresholds) {
+    if (bits < 1 || bits > 4) return RHT_E_BITS;
+    const FloatBook &b = book(bits);
+    const int K = 1 << bits;
+    if (levels) std::memcpy(levels, b.lev, sizeof(float) * (size_t)K);
+    if (thresholds) std::memcpy(thresholds, b.thr, sizeof(float) * (size_t)(K - 1));
+    return RHT_OK;
+}
+
+rht_status rht_signs(uint64_t seed, int32_t d, int8_t *signs) {
+    if (!signs) return RHT_E_NULL;
+    if (d < 1 || d > (1 << 20)) return RHT_E_DIM;
+    uint32_t *w = new uint32_t[(size_t)(d + 31) / 32];
+    sign_words(seed, d, w);
+    for (int i = 0; i < d; ++i) signs[i] = ((w[i >> 5] >> (i & 31)) & 1u) ? (int8_t)-1 : (int8_t)1;
+    delete[] w;
+    return RHT_OK;
+}
+
+rht_status rht_quantize(const void *x, rht_dtype xt, int64_t n, int32_t d, int32_t bits,
+                        rht_mode mode, uint64_t seed, uint8_t *codes, float *scale, void *stream) {
+    if (n < 0) return RHT_E_COUNT;
+    if (!pow2_dim(d)) return RHT_E_DIM;
+    if (bits < 1 || bits > 4) return RHT_E_BITS;
+    if (mode != RHT_SCALE_NORM && mode != RHT_SCALE_SIGN_BIASED && mode != RHT_SCALE_SIGN_UNBIASED)
+        return RHT_E_MODE;
+    if (mode != RHT_SCALE_NORM && bits != 1) return RHT_E_MODE;
+    if (xt != RHT_F32 && xt != RHT_F16) return RHT_E_DTYPE;
+    if (n == 0) return RHT_OK;
+    if (!x || !codes || !scale) return RHT_E_NULL;
+    if (!aligned(x) || !aligned(codes) || !aligned(scale)) return RHT_E_ALIGN;
+
+    QuantArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.x = x;
+    a.codes = codes;
+    a.scale = scale;
+    a.n = n;
+    const FloatBook &b = book(bits);
+    std::memcpy(a.lev, b.lev, sizeof(a.lev));
+    std::memcpy(a.thr, b.thr, sizeof(a.thr));
+    sign_words(seed, d, a.dsign);
+    const Kind kind = mode == RHT_SCALE_NORM ? kMse : (mode == RHT_SCALE_SIGN_BIASED ? kDriveBiased : kDriveUnbiased);
+    return launched(launch_quantize(d, xt == RHT_F16, bits, kind, layout_choice(), a, (hipStream_t)stream));
+}
+
+rht_status rht_dequantize(const uint8_t *codes, const float *scale, int64_t n, int32_t d,
+                          int32_t bits, rht_mode mode, uint64_t seed, void *y, rht_dtype yt,
+                          void *stream) {
+    if (n < 0) return RHT_E_COUNT;
+    if (!pow2_dim(d)) return RHT_E_DIM;
+    if (bits < 1 || bits > 4) return RHT_E_BITS;
+    if (mode != RHT_SCALE_NORM && mode != RHT_SCALE_SIGN_BIASED && mode != RHT_SCALE_SIGN_UNBIASED)
+        return RHT_E_MODE;
+    if (mode != RHT_SCALE_NORM && bits != 1) return RHT_E_MODE;
+    if (yt != RHT_F32 && yt != RHT_F16) return RHT_E_DTYPE;
+    if (n == 0) return RHT_OK;
+    if (!codes || !scale || !y) return RHT_E_NULL;
+    if (!aligned(codes) || !aligned(scale) || !aligned(y)) return RHT_E_ALIGN;
+
+    DequantArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.codes = codes;
+    a.scale = scale;
+    a.y = y;
+    a.n = n;
+    std::memcpy(a.lev, book(bits).lev, sizeof(a.lev));
+    sign_words(seed, d, a.dsign);
+    const Kind kind = mode == RHT_SCALE_NORM ? kMse : (mode == RHT_SCALE_SIGN_BIASED ? kDriveBiased : kDriveUnbiased);
+    return launched(launch_dequantize(d, yt == RHT_F16, bits, kind, layout_choice(), a, (hipStream_t)stream));
+}
+
+rht_status rht_residual_quantize(const void *x, rht_dtype xt, int64_t n, int32_t d, int32_t bits,
+                                 uint64_t seed, uint8_t *codes, uint8_t *signs, float *norms,
+                                 float *res_scale, void *stream) {
+    if (n < 0) return RHT_E_COUNT;
+    if (!pow2_dim(d)) return RHT_E_DIM;
+    if (bits < 2 || bits > 4) return RHT_E_BITS;
+    if (xt != RHT_F32 && xt != RHT_F16) return RHT_E_DTYPE;
+    if (n == 0) return RHT_OK;
+    if (!x || !codes || !signs || !norms || !res_scale) return RHT_E_NULL;
+    if (!aligned(x) || !aligned(codes) || !aligned(signs) || !aligned(norms) || !aligned(res_scale))
+        return RHT_E_ALIGN;
+
+    QuantArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.x = x;
+    a.codes = codes;
+    a.signs = signs;
+    a.scale = norms;
+    a.res_scale = res_scale;
+    a.n = n;
+    const FloatBook &b = book(bits - 1);
+    std::memcpy(a.lev, b.lev, sizeof(a.lev));
+    std::memcpy(a.thr, b.thr, sizeof(a.thr));
+    sign_words(seed, d, a.dsign);
+    return launched(launch_quantize(d, xt == RHT_F16, bits, kResidual, 0, a, (hipStream_t)stream));
+}
+
+rht_status rht_residual_dequantize(const uint8_t *codes, const uint8_t *signs, const float *norms,
+                                   const float *res_scale, int64_t n, int32_t d, int32_t bits,
+                                   uint64_t seed, void *y, rht_dtype yt, void *stream) {
+    if (n < 0) return RHT_E_COUNT;
+    if (!pow2_dim(d)) return RHT_E_DIM;
+    if (bits < 2 || bits > 4) return RHT_E_BITS;
+    if (yt != RHT_F32 && yt != RHT_F16) return RHT_E_DTYPE;
+    if (n == 0) return RHT_OK;
+    if (!codes || !signs || !norms || !res_scale || !y) return RHT_E_NULL;
+    if (!aligned(codes) || !aligned(signs) || !aligned(norms) || !aligned(res_scale) || !aligned(y))
+        return RHT_E_ALIGN;
+
+    DequantArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.codes = codes;
+    a.signs = signs;
+    a.scale = norms;
+    a.res_scale = res_scale;
+    a.y = y;
+    a.n = n;
+    std::memcpy(a.lev, book(bits - 1).lev, sizeof(a.lev));
+    sign_words(seed, d, a.dsign);
+    return launched(launch_dequantize(d, yt == RHT_F16, bits, kResidual, 0, a, (hipStream_t)stream));
+}
+
+rht_status rht_score(const float *q, int32_t m, const uint8_t *codes, const float *norms, int64_t n,
+                     int32_t d, int32_t bits, uint64_t seed, float *logits, void *stream) {
+    if (n < 0 || m < 0 || m > 64) return RHT_E_COUNT;
+    if (d != 64 && d != 128 && d != 256) return RHT_E_DIM;
+    if (bits < 1 || bits > 4) return RHT_E_BITS;
+    if (n == 0 || m == 0) return RHT_OK;
+    if (!q || !codes || !norms || !logits) return RHT_E_NULL;
+    if (!aligned(q) || !aligned(codes) || !aligned(norms) || !aligned(logits)) return RHT_E_ALIGN;
+
+    ScoreArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.m = m;
+    a.codes = codes;
+    a.norms = norms;
+    a.logits = logits;
+    a.n = n;
+    std::memcpy(a.lev, book(bits).lev, sizeof(a.lev));
+    sign_words(seed, d, a.dsign);
+    return launched(launch_score(d, bits, a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// rht_internal.h -- shared between the ABI layer (rht_api.cpp) and the HIP
+// kernels (rht_kernels.hip).  Not installed, not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rht {
+
+constexpr int kMinD = 32;
+constexpr int kMaxD = 4096;
+
+// What a quantize launch computes.
+enum Kind : int {
+    kMse = 0,        // b-bit Lloyd-Max codes + ||x||
+    kDriveBiased,    // 1-bit signs + ||Pi x||_1 / d
+    kDriveUnbiased,  // 1-bit signs + ||x||^2 / ||Pi x||_1
+    kResidual,       // (b-1)-bit codes + residual signs + ||x|| + S_r
+};
+
+// Kernel arguments are passed by value (well under the 4 KiB kernarg limit).
+// Codebook and rotation signs travel with every launch, so the library keeps
+// no device state.
+struct QuantArgs {
+    const void *x;
+    uint8_t *codes;      // MSE / stage-1 codes, or the DRIVE sign bits
+    uint8_t *signs;      // residual sign plane
+    float *scale;        // ||x|| (MSE, residual) or S (DRIVE)
+    float *res_scale;    // S_r (residual)
+    int64_t n;
+    float lev[16];       // fp32 Lloyd-Max levels of the code width
+    float thr[16];       // fp32 thresholds (2^cb - 1 used)
+    uint32_t dsign[kMaxD / 32];  // bit i set <=> D_ii = -1
+};
+
+struct DequantArgs {
+    const uint8_t *codes;
+    const uint8_t *signs;
+    const float *scale;
+    const float *res_scale;
+    void *y;
+    int64_t n;
+    float lev[16];
+    uint32_t dsign[kMaxD / 32];
+};
+
+struct ScoreArgs {
+    const float *q;
+    const uint8_t *codes;
+    const float *norms;
+    float *logits;
+    int64_t n;
+    int m;
+    float lev[16];
+    uint32_t dsign[kMaxD / 32];
+};
+
+// Launchers.  `layout` selects the coordinate-to-lane mapping of the MSE
+// kernels (0: each lane owns a contiguous run of the row; 1: the lanes of a
+// vector interleave in chunks of 32/bits coordinates, one code word each);
+// the DRIVE and residual kernels always use contiguous runs.
+// Return hipErrorInvalidValue when no kernel exists for the combination.
+hipError_t launch_quantize(int d, bool f16, int bits, Kind kind, int layout, const QuantArgs &a,
+                           hipStream_t s);
+hipError_t launch_dequantize(int d, bool f16out, int bits, Kind kind, int layout,
+                             const DequantArgs &a, hipStream_t s);
+hipError_t launch_score(int d, int bits, const ScoreArgs &a, hipStream_t s);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+// Upper bound on resident blocks per CU used to size grids (0 = occupancy
+// limit); read once from RHT_BLOCKS_PER_CU, a launch-shape tuning knob.
+int blocks_per_cu_cap();
+
+}  // namespace rht

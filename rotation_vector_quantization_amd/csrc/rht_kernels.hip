@@ -1,0 +1,881 @@
+// rht_kernels.hip -- HIP kernels for randomized-Hadamard vector quantization
+// on CDNA4 (gfx950, wave64).
+//
+// Method: web page "Random-rotation quantization" (brain.bigb.es): rotate each
+// vector by Pi = H D / sqrt(d) (randomized Hadamard transform, "Why rotation
+// works"; fast Walsh-Hadamard transform, page "TurboQuant and per-layer
+// outlier-aware K", section "TurboQuant 2026"), quantize every rotated
+// coordinate with one fixed N(0,1) Lloyd-Max codebook ("History", EDEN item),
+// decode with Pi^T ("intro", step 3); DRIVE sign codes, the residual chain and
+// rotated-domain scoring as in "History" and "Three decoders, one rotation".
+//
+// Register layout.  A vector of D coordinates is spread over LPV lanes of one
+// wavefront, E = D / LPV coordinates per lane, held in fp32 registers for the
+// whole transform.  Lane q of a vector owns the coordinates
+//     e(q, r) = ((r / G) * LPV + q) * G + (r % G),   r = 0 .. E-1,
+// i.e. groups of G consecutive coordinates.  G = E gives each lane one
+// contiguous run (coalesced code stores); G = 8 interleaves 16-byte fp16
+// chunks across the lanes of a vector (coalesced element loads).
+// The Hadamard transform is a product of one butterfly stage per index bit, in
+// any order: the stages on the register-index bits run in registers, the
+// stages on the lane bits run across lanes.  A cross-lane stage is
+//     v <- v + m * partner(v),  m = +1 on the lower lane, -1 on the upper one,
+// which leaves the upper lane holding the negated value; after all lane stages
+// lane q holds (-1)^popcount(q) times the true coordinate, and that factor is
+// folded into the per-vector scale.
+//
+// Signs D: with fp16 input the sign flip, the fp16 -> fp32 conversion and the
+// first butterfly stage are one v_dot2_f32_f16 per output (products by +-1
+// and the sum of two fp16 values are exact in fp32).
+//
+// Nearest level: y16 = 16 y is mapped to a cell of a 256-entry LDS table
+// (cell k covers y16 in about [k-40.5, k-39)); the entry holds the code of the
+// cell's lower end and the one scaled threshold that may fall inside the cell,
+// so the code is base + [y16 >= T].  The final decision compares fp32 y16 with
+// the exact scaled fp32 threshold (scaling by 16 is exact).
+#include "rht_internal.h"
+
+namespace rht {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kWaves = kBlock / 64;
+
+__host__ __device__ constexpr int lanes_per_vec(int d) { return d >= 4096 ? 64 : d / 32; }
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63u; }
+
+// Value of v in lane (lane ^ M); M < lanes of one vector.
+template <int M>
+__device__ __forceinline__ float xlane(float v) {
+    const int iv = __builtin_bit_cast(int, v);
+    int r;
+    if constexpr (M == 1)
+        r = __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true);   // quad_perm:[1,0,3,2]
+    else if constexpr (M == 2)
+        r = __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true);   // quad_perm:[2,3,0,1]
+    else if constexpr (M == 8)
+        r = __builtin_amdgcn_mov_dpp(iv, 0x128, 0xF, 0xF, true);  // row_ror:8
+    else if constexpr (M == 4 || M == 16)
+        r = __builtin_amdgcn_ds_swizzle(iv, (M << 10) | 0x1F);    // bit mode, xor M
+    else
+        r = __builtin_amdgcn_ds_bpermute((int)((lane_id() ^ M) << 2), iv);
+    return __builtin_bit_cast(float, r);
+}
+
+// Sum over the LPV lanes of a vector (every lane gets the total).
+template <int LPV>
+__device__ __forceinline__ float vec_sum(float s) {
+    if constexpr (LPV > 1) s += xlane<1>(s);
+    if constexpr (LPV > 2) s += xlane<2>(s);
+    if constexpr (LPV > 4) s += xlane<4>(s);
+    if constexpr (LPV > 8) s += xlane<8>(s);
+    if constexpr (LPV > 16) s += xlane<16>(s);
+    if constexpr (LPV > 32) s += xlane<32>(s);
+    return s;
+}
+
+// Butterfly stages on register-index bits FIRST.. of E registers.
+template <int E, int FIRST>
+__device__ __forceinline__ void fwht_regs(float (&v)[E]) {
+#pragma unroll
+    for (int h = 1 << FIRST; h < E; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < E; i += 2 * h) {
+#pragma unroll
+            for (int j = i; j < i + h; ++j) {
+                const float a = v[j], b = v[j + h];
+                v[j] = a + b;
+                v[j + h] = a - b;
+            }
+        }
+    }
+}
+
+// v[r] += m * v[r ^ lane M] for every register.  Partners reachable by DPP
+// (xor 1, 2: quad_perm; xor 8: row_ror:8) use one v_fmac_f32_dpp per
+// register.  The hardware needs two wait states between a VALU write of a
+// VGPR and a DPP read of it, and the compiler cannot see into the asm, so each
+// group of eight starts with s_nop 1; inside a group every instruction reads
+// only its own destination, written before the group.
+#define RHT_FMAC_DPP8(CTRL)                                                         \
+    asm("s_nop 1\n\t"                                                               \
+        "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"        \
+        "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"        \
+        "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"        \
+        "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"        \
+        "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"        \
+        "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"        \
+        "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"        \
+        "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"              \
+        : "+v"(v[r]), "+v"(v[r + 1]), "+v"(v[r + 2]), "+v"(v[r + 3]), "+v"(v[r + 4]), \
+          "+v"(v[r + 5]), "+v"(v[r + 6]), "+v"(v[r + 7])                             \
+        : "v"(m))
+
+template <int M, int E>
+__device__ __forceinline__ void xstage(float (&v)[E], uint32_t q) {
+    const float m = (q & M) ? -1.0f : 1.0f;
+    if constexpr ((M == 1 || M == 2 || M == 8) && E % 8 == 0) {
+#pragma unroll
+        for (int r = 0; r < E; r += 8) {
+            if constexpr (M == 1)
+                RHT_FMAC_DPP8("quad_perm:[1,0,3,2]");
+            else if constexpr (M == 2)
+                RHT_FMAC_DPP8("quad_perm:[2,3,0,1]");
+            else
+                RHT_FMAC_DPP8("row_ror:8");
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < E; ++r) v[r] = fmaf(xlane<M>(v[r]), m, v[r]);
+    }
+}
+
+// Butterfly stages on the lane bits; afterwards lane q holds (-1)^popcount(q)
+// times the transform.
+template <int LPV, int E>
+__device__ __forceinline__ void fwht_lanes(float (&v)[E], uint32_t q) {
+    if constexpr (LPV > 1) xstage<1>(v, q);
+    if constexpr (LPV > 2) xstage<2>(v, q);
+    if constexpr (LPV > 4) xstage<4>(v, q);
+    if constexpr (LPV > 8) xstage<8>(v, q);
+    if constexpr (LPV > 16) xstage<16>(v, q);
+    if constexpr (LPV > 32) xstage<32>(v, q);
+}
+
+__device__ __forceinline__ float lane_factor(uint32_t q) {
+    return (__builtin_popcount(q) & 1) ? -1.0f : 1.0f;
+}
+
+// Bit r of the result = sign bit of the coordinate held in register r.
+template <int D, int G>
+__device__ __forceinline__ uint64_t lane_sign_bits(const uint32_t *dsign, uint32_t q) {
+    constexpr int LPV = lanes_per_vec(D), E = D / LPV, NG = E / G;
+    uint64_t m = 0;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        const uint32_t e0 = (gi * LPV + q) * G;
+        uint64_t bits;
+        if constexpr (G >= 32) {
+            bits = 0;
+#pragma unroll
+            for (int w = 0; w < G / 32; ++w) bits |= (uint64_t)dsign[e0 / 32 + w] << (32 * w);
+        } else {
+            bits = (dsign[e0 >> 5] >> (e0 & 31)) & ((1u << G) - 1u);
+        }
+        m |= bits << (gi * G);
+    }
+    return m;
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
+                                  false);
+}
+
+// Raw input words a lane holds for one vector: E fp16 (E/2 words) or E fp32.
+template <int D, bool F16>
+struct Raw {
+    static constexpr int E = D / lanes_per_vec(D);
+    static constexpr int W = F16 ? E / 2 : E;
+};
+
+// Load the E coordinates lane q owns of vector `vec` (zeros if !valid).
+template <int D, int G, bool F16>
+__device__ __forceinline__ void load_raw(const void *x, int64_t vec, bool valid, uint32_t q,
+                                         uint32_t (&raw)[Raw<D, F16>::W]) {
+    constexpr int LPV = lanes_per_vec(D), E = D / LPV, NG = E / G;
+    constexpr int EPC = F16 ? 8 : 4;  // elements per 16-byte chunk
+    static_assert(G % EPC == 0, "groups are whole 16-byte chunks");
+    const uint4 *row = reinterpret_cast<const uint4 *>(static_cast<const char *>(x) + vec * D * (F16 ? 2 : 4));
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+        for (int c = 0; c < G / EPC; ++c) {
+            uint4 t = make_uint4(0, 0, 0, 0);
+            if (valid) t = row[((gi * LPV + q) * G) / EPC + c];
+            const int p = (gi * G + EPC * c) / (F16 ? 2 : 1);
+            raw[p] = t.x;
+            raw[p + 1] = t.y;
+            raw[p + 2] = t.z;
+            raw[p + 3] = t.w;
+        }
+    }
+}
+
+// Per-lane sign words for stage0: fp16 -> packed (s_2p, s_2p+1) as +-1.0 fp16;
+// fp32 -> sign-bit masks.
+template <int D, bool F16>
+__device__ __forceinline__ void sign_words(uint64_t lsign, uint32_t (&sw)[Raw<D, F16>::W]) {
+#pragma unroll
+    for (int p = 0; p < Raw<D, F16>::W; ++p) {
+        if constexpr (F16)
+            sw[p] = ((uint32_t)(lsign >> (2 * p)) & 1u ? 0xBC00u : 0x3C00u) |
+                    (((uint32_t)(lsign >> (2 * p + 1)) & 1u ? 0xBC00u : 0x3C00u) << 16);
+        else
+            sw[p] = ((uint32_t)(lsign >> p) & 1u) << 31;
+    }
+}
+
+// Apply D and (fp16) the first butterfly stage; return the lane's sum x_i^2.
+template <int D, bool F16>
+__device__ __forceinline__ float stage0(const uint32_t (&raw)[Raw<D, F16>::W],
+                                        const uint32_t (&sw)[Raw<D, F16>::W],
+                                        float (&v)[D / lanes_per_vec(D)]) {
+    constexpr int W = Raw<D, F16>::W;
+    float ss = 0.0f, ss2 = 0.0f;
+#pragma unroll
+    for (int p = 0; p < W; ++p) {
+        if constexpr (F16) {
+            v[2 * p] = dot2(raw[p], sw[p], 0.0f);
+            v[2 * p + 1] = dot2(raw[p], sw[p] ^ 0x80000000u, 0.0f);
+            if (p & 1)
+                ss2 = dot2(raw[p], raw[p], ss2);
+            else
+                ss = dot2(raw[p], raw[p], ss);
+        } else {
+            const float f = __builtin_bit_cast(float, raw[p]);
+            if (p & 1)
+                ss2 = fmaf(f, f, ss2);
+            else
+                ss = fmaf(f, f, ss);
+            v[p] = __builtin_bit_cast(float, raw[p] ^ sw[p]);
+        }
+    }
+    return ss + ss2;
+}
+
+template <int D, int G, bool F16>
+__device__ __forceinline__ float load_signed(const void *x, int64_t vec, bool valid, uint32_t q,
+                                             uint64_t lsign, float (&v)[D / lanes_per_vec(D)]) {
+    uint32_t raw[Raw<D, F16>::W], sw[Raw<D, F16>::W];
+    load_raw<D, G, F16>(x, vec, valid, q, raw);
+    sign_words<D, F16>(lsign, sw);
+    return stage0<D, F16>(raw, sw, v);
+}
+
+// Nearest-level table for y16 = 16 * y.  Cell k holds the y16 values with
+// round(y16 + OFF) == k; its entry is (scaled threshold that may lie in the
+// cell or +inf, code at the cell's low end).  Each entry is built for the
+// widened window [k - OFF - 0.75, k - OFF + 1.25), so it stays right whatever
+// the rounding of the index; windows are 2 wide and scaled thresholds are at
+// least 4 apart (16 x the smallest N(0,1) Lloyd-Max gap), so a window holds at
+// most one threshold.
+template <int NCELL, int OFF>
+__device__ __forceinline__ void build_lut(uint2 *lut, const float *thr, int nthr) {
+    for (int k = threadIdx.x; k < NCELL; k += kBlock) {
+        const float lo = k == 0 ? -INFINITY : (float)(k - OFF) - 0.75f;
+        const float hi = k == NCELL - 1 ? INFINITY : (float)(k - OFF) + 1.25f;
+        uint32_t base = 0;
+        float t_in = INFINITY;
+        for (int j = 0; j < nthr; ++j) {
+            const float t = 16.0f * thr[j];
+            if (t < lo)
+                ++base;
+            else if (t < hi && t_in == INFINITY)
+                t_in = t;
+        }
+        lut[k] = make_uint2(__builtin_bit_cast(uint32_t, t_in), base);
+    }
+}
+
+// |y16| <= 16 sqrt(d) (|(H D x)_i| <= ||x||_1 <= sqrt(d) ||x||), so for d <= 128
+// a 512-cell table centred on 0 needs no clamp; larger d clamp into 256 cells.
+template <int D>
+struct Lut {
+    static constexpr bool kClamp = D > 128;
+    static constexpr int kCells = kClamp ? 256 : 512;
+    static constexpr int kOff = kClamp ? 40 : 256;
+};
+
+template <int D>
+__device__ __forceinline__ uint32_t nearest_code(const uint2 *lut, float y16) {
+    // adding 2^23 + OFF leaves round(y16 + OFF) in the low mantissa bits
+    int b = __builtin_bit_cast(int, y16 + (8388608.0f + (float)Lut<D>::kOff));
+    if constexpr (Lut<D>::kClamp) b = min(max(b, 0x4B000000), 0x4B000000 + Lut<D>::kCells - 1);
+    const uint2 e = lut[b - 0x4B000000];
+    return e.y + (y16 >= __builtin_bit_cast(float, e.x) ? 1u : 0u);
+}
+
+// Pack one code of width CB at group-local position t (LSB-first).
+template <int CB, int WPG>
+__device__ __forceinline__ void put_code(uint32_t (&w)[WPG], int t, uint32_t code) {
+    const int p = t * CB, i = p / 32, sh = p % 32;
+    w[i] |= code << sh;
+    if (sh + CB > 32) w[i + 1] |= code >> (32 - sh);
+}
+
+template <int CB, int WPG>
+__device__ __forceinline__ uint32_t get_code(const uint32_t (&w)[WPG], int t) {
+    const int p = t * CB, i = p / 32, sh = p % 32;
+    uint32_t c = w[i] >> sh;
+    if (sh + CB > 32) c |= w[i + 1] << (32 - sh);
+    return c & ((1u << CB) - 1u);
+}
+
+template <int WPG>
+__device__ __forceinline__ void store_words(uint32_t *dst, const uint32_t (&w)[WPG]) {
+    if constexpr (WPG == 4) {
+        *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else if constexpr (WPG == 2) {
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < WPG; ++i) dst[i] = w[i];
+    }
+}
+
+template <int WPG>
+__device__ __forceinline__ void load_words(const uint32_t *src, uint32_t (&w)[WPG]) {
+    if constexpr (WPG == 4) {
+        const uint4 t = *reinterpret_cast<const uint4 *>(src);
+        w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+    } else if constexpr (WPG == 2) {
+        const uint2 t = *reinterpret_cast<const uint2 *>(src);
+        w[0] = t.x; w[1] = t.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < WPG; ++i) w[i] = src[i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Encoder.  KIND selects the code: MSE (BITS-bit codes + ||x||), DRIVE (1-bit
+// signs + S), residual chain (BITS-1 bit codes + sign plane + ||x|| + S_r).
+template <int D, int G, bool F16, int BITS, int KIND>
+__global__ __launch_bounds__(kBlock) void k_quantize(const QuantArgs a) {
+    constexpr int LPV = lanes_per_vec(D), E = D / LPV, NG = E / G;
+    constexpr int VPW = 64 / LPV, VPB = kWaves * VPW;
+    constexpr bool DRIVE = (KIND == kDriveBiased || KIND == kDriveUnbiased);
+    constexpr int CB = KIND == kResidual ? BITS - 1 : (DRIVE ? 1 : BITS);
+    constexpr int WPG = G * CB / 32;
+    static_assert(G * CB % 32 == 0, "a group's codes fill whole words");
+    static_assert(KIND != kResidual || G % 32 == 0, "residual sign words need 32-coordinate groups");
+    constexpr int ROWW = D * CB / 32;  // code words per row
+
+    __shared__ uint2 lut[Lut<D>::kCells];
+    __shared__ float slev[16];
+    if constexpr (!DRIVE) {
+        build_lut<Lut<D>::kCells, Lut<D>::kOff>(lut, a.thr, (1 << CB) - 1);
+        if (threadIdx.x < 16) slev[threadIdx.x] = a.lev[threadIdx.x];
+        __syncthreads();
+    }
+
+    const uint32_t lane = lane_id(), q = lane % LPV, slot = lane / LPV, wave = threadIdx.x >> 6;
+    const uint64_t lsign = lane_sign_bits<D, G>(a.dsign, q);
+    const float fq = lane_factor(q);
+    const float sqrt_d = __builtin_sqrtf((float)D);
+
+    uint32_t sw[Raw<D, F16>::W], raw[Raw<D, F16>::W];
+    sign_words<D, F16>(lsign, sw);
+    const int64_t stride = (int64_t)gridDim.x * VPB;
+    {
+        const int64_t vec = (int64_t)blockIdx.x * VPB + wave * VPW + slot;
+        load_raw<D, G, F16>(a.x, vec, vec < a.n, q, raw);
+    }
+    for (int64_t v0 = (int64_t)blockIdx.x * VPB; v0 < a.n; v0 += stride) {
+        const int64_t vec = v0 + wave * VPW + slot;
+        const bool valid = vec < a.n;
+        float v[E];
+        float ss = stage0<D, F16>(raw, sw, v);
+        // the next vector's loads are in flight while this one is transformed
+        load_raw<D, G, F16>(a.x, vec + stride, vec + stride < a.n, q, raw);
+        fwht_regs<E, F16 ? 1 : 0>(v);
+        fwht_lanes<LPV>(v, q);
+        ss = vec_sum<LPV>(ss);
+
+        if constexpr (DRIVE) {
+            // bit_i = [(H D x)_i >= 0]; the register holds fq * (H D x)_i
+            uint32_t w[NG][WPG];
+            float l1 = 0.0f;
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+                for (int i = 0; i < WPG; ++i) w[gi][i] = 0u;
+#pragma unroll
+                for (int t = 0; t < G; ++t) {
+                    const float h = v[gi * G + t] * fq;
+                    l1 += fabsf(h);
+                    put_code<1, WPG>(w[gi], t, h >= 0.0f ? 1u : 0u);
+                }
+            }
+            l1 = vec_sum<LPV>(l1);  // sum |H D x|_i = sqrt(d) ||Pi x||_1
+            float S;
+            if constexpr (KIND == kDriveBiased)
+                S = l1 / ((float)D * sqrt_d);
+            else
+                S = l1 > 0.0f ? ss * sqrt_d / l1 : 0.0f;
+            if (valid) {
+                uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes) + vec * ROWW;
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) store_words<WPG>(dst + (gi * LPV + q) * WPG, w[gi]);
+                if (q == 0) a.scale[vec] = S;
+            }
+        } else {
+            const float nrm = sqrtf(ss);
+            const float inv16 = ss > 0.0f ? fq * (16.0f / nrm) : 0.0f;
+            uint32_t w[NG][WPG];
+            uint32_t sw[NG][KIND == kResidual ? G / 32 : 1];
+            float r2 = 0.0f, r1 = 0.0f;
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+                for (int i = 0; i < WPG; ++i) w[gi][i] = 0u;
+                if constexpr (KIND == kResidual) {
+#pragma unroll
+                    for (int i = 0; i < G / 32; ++i) sw[gi][i] = 0u;
+                }
+#pragma unroll
+                for (int t = 0; t < G; ++t) {
+                    const float hv = v[gi * G + t];
+                    const uint32_t code = nearest_code<D>(lut, hv * inv16);
+                    put_code<CB, WPG>(w[gi], t, code);
+                    if constexpr (KIND == kResidual) {
+                        // residual in the H D x domain: rho = h - ||x|| c[code]
+                        const float rho = fmaf(-nrm, slev[code], hv * fq);
+                        r2 = fmaf(rho, rho, r2);
+                        r1 += fabsf(rho);
+                        sw[gi][t / 32] |= (rho >= 0.0f ? 1u : 0u) << (t % 32);
+                    }
+                }
+            }
+            float sr = 0.0f;
+            if constexpr (KIND == kResidual) {
+                r2 = vec_sum<LPV>(r2);
+                r1 = vec_sum<LPV>(r1);
+                // S_r = ||r||^2 / ||r||_1 with r = rho / sqrt(d)
+                sr = r1 > 0.0f ? r2 / (sqrt_d * r1) : 0.0f;
+            }
+            if (valid) {
+                uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes) + vec * ROWW;
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) store_words<WPG>(dst + (gi * LPV + q) * WPG, w[gi]);
+                if constexpr (KIND == kResidual) {
+                    uint32_t *sd = reinterpret_cast<uint32_t *>(a.signs) + vec * (D / 32);
+#pragma unroll
+                    for (int gi = 0; gi < NG; ++gi)
+                        store_words<G / 32>(sd + (gi * LPV + q) * (G / 32), sw[gi]);
+                    if (q == 0) a.res_scale[vec] = sr;
+                }
+                if (q == 0) a.scale[vec] = nrm;
+            }
+        }
+    }
+}
+
+// Codes (and residual signs) and scales lane q needs for vector `vec`;
+// zeros past the end.
+template <int D, int G, int BITS, int KIND>
+__device__ __forceinline__ void fetch_codes(const DequantArgs &a, int64_t vec, uint32_t q,
+                                            uint32_t (&w)[D / lanes_per_vec(D) / G][G * (KIND == kResidual ? BITS - 1 : ((KIND == kDriveBiased || KIND == kDriveUnbiased) ? 1 : BITS)) / 32],
+                                            uint32_t (&sw)[D / lanes_per_vec(D) / G][KIND == kResidual ? G / 32 : 1],
+                                            float &sc, float &rs) {
+    constexpr int LPV = lanes_per_vec(D), E = D / LPV, NG = E / G;
+    constexpr bool DRIVE = (KIND == kDriveBiased || KIND == kDriveUnbiased);
+    constexpr int CB = KIND == kResidual ? BITS - 1 : (DRIVE ? 1 : BITS);
+    constexpr int WPG = G * CB / 32;
+    constexpr int ROWW = D * CB / 32;
+    if (vec < a.n) {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(a.codes) + vec * ROWW;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) load_words<WPG>(src + (gi * LPV + q) * WPG, w[gi]);
+        if constexpr (KIND == kResidual) {
+            const uint32_t *ss = reinterpret_cast<const uint32_t *>(a.signs) + vec * (D / 32);
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) load_words<G / 32>(ss + (gi * LPV + q) * (G / 32), sw[gi]);
+            rs = a.res_scale[vec];
+        }
+        sc = a.scale[vec];
+    } else {
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+            for (int i = 0; i < WPG; ++i) w[gi][i] = 0u;
+            if constexpr (KIND == kResidual) {
+#pragma unroll
+                for (int i = 0; i < G / 32; ++i) sw[gi][i] = 0u;
+            }
+        }
+        sc = 0.0f;
+        rs = 0.0f;
+    }
+    (void)E;
+}
+
+// ---------------------------------------------------------------------------
+// Decoder: x^ = D H z with z = c[code] (scaled by ||x|| / d afterwards), z =
+// +-1 (DRIVE, scaled by S / sqrt(d)), or z = c[code] ||x|| / d + S_r sigma /
+// sqrt(d) (residual chain).
+template <int D, int G, bool F16OUT, int BITS, int KIND>
+__global__ __launch_bounds__(kBlock) void k_dequantize(const DequantArgs a) {
+    constexpr int LPV = lanes_per_vec(D), E = D / LPV, NG = E / G;
+    constexpr int VPW = 64 / LPV, VPB = kWaves * VPW;
+    constexpr bool DRIVE = (KIND == kDriveBiased || KIND == kDriveUnbiased);
+    constexpr int CB = KIND == kResidual ? BITS - 1 : (DRIVE ? 1 : BITS);
+    constexpr int WPG = G * CB / 32;
+    constexpr int ROWW = D * CB / 32;
+    static_assert(G * CB % 32 == 0, "a group's codes fill whole words");
+
+    // 4-bit codes are decoded a byte (two codes) at a time from a 256-entry
+    // table of level pairs; other widths use the 2^CB-entry level table.
+    constexpr bool PAIRS = (CB == 4 && KIND == kMse);
+    __shared__ float slev[16];
+    __shared__ float2 spair[PAIRS ? 256 : 1];
+    if (threadIdx.x < 16) slev[threadIdx.x] = a.lev[threadIdx.x];
+    if constexpr (PAIRS) spair[threadIdx.x] = make_float2(a.lev[threadIdx.x & 15], a.lev[threadIdx.x >> 4]);
+    __syncthreads();
+
+    const uint32_t lane = lane_id(), q = lane % LPV, slot = lane / LPV, wave = threadIdx.x >> 6;
+    const uint64_t lsign = lane_sign_bits<D, G>(a.dsign, q);
+    const float fq = lane_factor(q);
+    const float inv_sqrt_d = 1.0f / __builtin_sqrtf((float)D);
+    // sign-bit masks of D for the output words (fp16 pairs or single fp32)
+    constexpr int NM = F16OUT ? E / 2 : E;
+    uint32_t omask[NM];
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+        if constexpr (F16OUT)
+            omask[i] = (((uint32_t)(lsign >> (2 * i)) & 1u) << 15) | (((uint32_t)(lsign >> (2 * i + 1)) & 1u) << 31);
+        else
+            omask[i] = ((uint32_t)(lsign >> i) & 1u) << 31;
+    }
+
+    uint32_t w[NG][WPG];
+    uint32_t sw[NG][KIND == kResidual ? G / 32 : 1];
+    float sc = 0.0f, rs = 0.0f;
+    const int64_t stride = (int64_t)gridDim.x * VPB;
+    fetch_codes<D, G, BITS, KIND>(a, (int64_t)blockIdx.x * VPB + wave * VPW + slot, q, w, sw, sc, rs);
+    for (int64_t v0 = (int64_t)blockIdx.x * VPB; v0 < a.n; v0 += stride) {
+        const int64_t vec = v0 + wave * VPW + slot;
+        const bool valid = vec < a.n;
+        float v[E];
+        float alpha;
+        if constexpr (DRIVE) {
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+                for (int t = 0; t < G; ++t) v[gi * G + t] = get_code<1, WPG>(w[gi], t) ? 1.0f : -1.0f;
+            alpha = fq * sc * inv_sqrt_d;
+        } else if constexpr (KIND == kResidual) {
+            const float a0 = sc * (1.0f / D), s0 = rs * inv_sqrt_d;
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+                for (int t = 0; t < G; ++t) {
+                    const float sgn = (sw[gi][t / 32] >> (t % 32)) & 1u ? s0 : -s0;
+                    v[gi * G + t] = fmaf(slev[get_code<CB, WPG>(w[gi], t)], a0, sgn);
+                }
+            alpha = fq;
+        } else if constexpr (PAIRS) {
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+                for (int i = 0; i < WPG; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float2 l2 = spair[(w[gi][i] >> (8 * j)) & 0xFFu];
+                        v[gi * G + 8 * i + 2 * j] = l2.x;
+                        v[gi * G + 8 * i + 2 * j + 1] = l2.y;
+                    }
+            alpha = fq * sc * (1.0f / D);
+        } else {
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+                for (int t = 0; t < G; ++t) v[gi * G + t] = slev[get_code<CB, WPG>(w[gi], t)];
+            alpha = fq * sc * (1.0f / D);
+        }
+        // the next vector's codes load while this one is decoded
+        fetch_codes<D, G, BITS, KIND>(a, vec + stride, q, w, sw, sc, rs);
+        fwht_regs<E, 0>(v);
+        fwht_lanes<LPV>(v, q);
+        if (valid) {
+            if constexpr (F16OUT) {
+                uint4 *row = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.y) + vec * D);
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+                    for (int c = 0; c < G / 8; ++c) {
+                        uint32_t o[4];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const int r = gi * G + 8 * c + 2 * k;
+                            const _Float16 lo = (_Float16)(v[r] * alpha);
+                            const _Float16 hi = (_Float16)(v[r + 1] * alpha);
+                            const uint32_t pk = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                                                ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+                            o[k] = pk ^ omask[r / 2];
+                        }
+                        row[((gi * LPV + q) * G) / 8 + c] = make_uint4(o[0], o[1], o[2], o[3]);
+                    }
+                }
+            } else {
+                uint4 *row = reinterpret_cast<uint4 *>(static_cast<float *>(a.y) + vec * D);
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+                    for (int c = 0; c < G / 4; ++c) {
+                        uint32_t o[4];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const int r = gi * G + 4 * c + k;
+                            o[k] = __builtin_bit_cast(uint32_t, v[r] * alpha) ^ omask[r];
+                        }
+                        row[((gi * LPV + q) * G) / 4 + c] = make_uint4(o[0], o[1], o[2], o[3]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Scoring on the codes in the rotated domain: logits = Qt * C^T scaled per key,
+// Qt = (H D Q^T)^T formed once per block into LDS, C[k][i] = c[code_{k,i}].
+// The contraction runs on v_mfma_f32_32x32x2_f32: per wave a 64-query x
+// 32-key tile (two 32x32 accumulators sharing the key operand).
+template <int D, int BITS>
+__global__ __launch_bounds__(kBlock) void k_score(const ScoreArgs a) {
+    constexpr int LPV = lanes_per_vec(D), E = D / LPV, VPW = 64 / LPV, VPB = kWaves * VPW;
+    constexpr int QS = 96;  // LDS row stride of the transposed queries (bank spread)
+    constexpr int ROWW = D * BITS / 32;
+    __shared__ float qt[D * QS];
+    __shared__ float slev[16];
+
+    const uint32_t lane = lane_id(), q = lane % LPV, slot = lane / LPV, wave = threadIdx.x >> 6;
+    if (threadIdx.x < 16) slev[threadIdx.x] = a.lev[threadIdx.x];
+    {
+        const uint64_t lsign = lane_sign_bits<D, E>(a.dsign, q);
+        const float fq = lane_factor(q);
+        for (int j0 = 0; j0 < 64; j0 += VPB) {
+            const int j = j0 + wave * VPW + slot;
+            const bool valid = j < a.m;
+            float v[E];
+            load_signed<D, E, false>(a.q, j, valid, q, lsign, v);
+            fwht_regs<E, 0>(v);
+            fwht_lanes<LPV>(v, q);
+            if (j < 64) {
+#pragma unroll
+                for (int r = 0; r < E; ++r) qt[(q * E + r) * QS + j] = v[r] * fq;
+            }
+        }
+    }
+    __syncthreads();
+
+    const uint32_t col = lane & 31u, par = lane >> 5;
+    const int64_t ntiles = (a.n + 31) / 32;
+    for (int64_t tile = (int64_t)blockIdx.x * kWaves + wave; tile < ntiles;
+         tile += (int64_t)gridDim.x * kWaves) {
+        const int64_t key = tile * 32 + col;
+        const bool valid = key < a.n;
+        uint32_t w[ROWW];
+        if (valid) {
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(a.codes) + key * ROWW;
+            load_words<ROWW>(src, w);
+        } else {
+#pragma unroll
+            for (int i = 0; i < ROWW; ++i) w[i] = 0u;
+        }
+        floatx16 acc0 = {}, acc1 = {};
+#pragma unroll
+        for (int s = 0; s < D / 2; ++s) {
+            const uint32_t c0 = get_code<BITS, ROWW>(w, 2 * s), c1 = get_code<BITS, ROWW>(w, 2 * s + 1);
+            const float b = slev[par ? c1 : c0];
+            const int i = 2 * s + par;
+            const float a0 = qt[i * QS + col], a1 = qt[i * QS + 32 + col];
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b, acc1, 0, 0, 0);
+        }
+        if (valid) {
+            const float sc = a.norms[key] * (1.0f / D);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = 8 * (r / 4) + 4 * par + (r % 4);
+                if (row < a.m) a.logits[(int64_t)row * a.n + key] = acc0[r] * sc;
+                if (row + 32 < a.m) a.logits[(int64_t)(row + 32) * a.n + key] = acc1[r] * sc;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch helpers.  Grids are sized to what is resident at once (CUs x
+// blocks per CU from the occupancy calculator), so every block of the
+// grid-stride loop gets the same share and there is no partial last wave.
+template <int D>
+constexpr int vecs_per_block() { return kWaves * (64 / lanes_per_vec(D)); }
+
+template <typename K>
+int resident_blocks(K kernel) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    return per_cu;
+}
+
+// Fewer, longer-lived blocks measured faster than a full-occupancy grid: the
+// streaming loads are prefetched one vector ahead in every wave, and HBM
+// write throughput drops with many concurrent writers.
+constexpr int kDefaultBlocksPerCU = 3;
+
+inline int grid_for(int64_t n, int vpb, int per_cu) {
+    const int cap_env = blocks_per_cu_cap();
+    const int cap_cu = cap_env > 0 ? cap_env : kDefaultBlocksPerCU;
+    if (per_cu > cap_cu) per_cu = cap_cu;
+    const int64_t want = (n + vpb - 1) / vpb;
+    const int64_t cap = (int64_t)device_cu_count() * per_cu;
+    return (int)(want < cap ? (want > 0 ? want : 1) : cap);
+}
+
+template <int D, int G, bool F16, int BITS, int KIND>
+hipError_t run_q(const QuantArgs &a, hipStream_t s) {
+    static const int per_cu = resident_blocks(k_quantize<D, G, F16, BITS, KIND>);
+    hipLaunchKernelGGL((k_quantize<D, G, F16, BITS, KIND>), dim3(grid_for(a.n, vecs_per_block<D>(), per_cu)),
+                       dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int D, int G, bool F16, int BITS, int KIND>
+hipError_t run_dq(const DequantArgs &a, hipStream_t s) {
+    static const int per_cu = resident_blocks(k_dequantize<D, G, F16, BITS, KIND>);
+    hipLaunchKernelGGL((k_dequantize<D, G, F16, BITS, KIND>),
+                       dim3(grid_for(a.n, vecs_per_block<D>(), per_cu)), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t quant_d(bool f16, int bits, Kind kind, int layout, const QuantArgs &a, hipStream_t s) {
+    constexpr int E = D / lanes_per_vec(D);
+    switch (kind) {
+    case kMse:
+        // chunked layout: one 32-bit code word per lane-group (G = 32 / bits)
+        if (layout == 1) {
+            switch (bits) {
+            case 1: return f16 ? run_q<D, 32, true, 1, kMse>(a, s) : run_q<D, 32, false, 1, kMse>(a, s);
+            case 2: return f16 ? run_q<D, 16, true, 2, kMse>(a, s) : run_q<D, 16, false, 2, kMse>(a, s);
+            case 4: return f16 ? run_q<D, 8, true, 4, kMse>(a, s) : run_q<D, 8, false, 4, kMse>(a, s);
+            }
+        }
+        switch (bits) {
+        case 1: return f16 ? run_q<D, E, true, 1, kMse>(a, s) : run_q<D, E, false, 1, kMse>(a, s);
+        case 2: return f16 ? run_q<D, E, true, 2, kMse>(a, s) : run_q<D, E, false, 2, kMse>(a, s);
+        case 3: return f16 ? run_q<D, E, true, 3, kMse>(a, s) : run_q<D, E, false, 3, kMse>(a, s);
+        case 4: return f16 ? run_q<D, E, true, 4, kMse>(a, s) : run_q<D, E, false, 4, kMse>(a, s);
+        }
+        break;
+    case kDriveBiased:
+        return f16 ? run_q<D, E, true, 1, kDriveBiased>(a, s) : run_q<D, E, false, 1, kDriveBiased>(a, s);
+    case kDriveUnbiased:
+        return f16 ? run_q<D, E, true, 1, kDriveUnbiased>(a, s)
+                   : run_q<D, E, false, 1, kDriveUnbiased>(a, s);
+    case kResidual:
+        switch (bits) {
+        case 2: return f16 ? run_q<D, E, true, 2, kResidual>(a, s) : run_q<D, E, false, 2, kResidual>(a, s);
+        case 3: return f16 ? run_q<D, E, true, 3, kResidual>(a, s) : run_q<D, E, false, 3, kResidual>(a, s);
+        case 4: return f16 ? run_q<D, E, true, 4, kResidual>(a, s) : run_q<D, E, false, 4, kResidual>(a, s);
+        }
+        break;
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int D>
+hipError_t dequant_d(bool f16, int bits, Kind kind, int layout, const DequantArgs &a, hipStream_t s) {
+    constexpr int E = D / lanes_per_vec(D);
+    switch (kind) {
+    case kMse:
+        if (layout == 1) {
+            switch (bits) {
+            case 1: return f16 ? run_dq<D, 32, true, 1, kMse>(a, s) : run_dq<D, 32, false, 1, kMse>(a, s);
+            case 2: return f16 ? run_dq<D, 16, true, 2, kMse>(a, s) : run_dq<D, 16, false, 2, kMse>(a, s);
+            case 4: return f16 ? run_dq<D, 8, true, 4, kMse>(a, s) : run_dq<D, 8, false, 4, kMse>(a, s);
+            }
+        }
+        switch (bits) {
+        case 1: return f16 ? run_dq<D, E, true, 1, kMse>(a, s) : run_dq<D, E, false, 1, kMse>(a, s);
+        case 2: return f16 ? run_dq<D, E, true, 2, kMse>(a, s) : run_dq<D, E, false, 2, kMse>(a, s);
+        case 3: return f16 ? run_dq<D, E, true, 3, kMse>(a, s) : run_dq<D, E, false, 3, kMse>(a, s);
+        case 4: return f16 ? run_dq<D, E, true, 4, kMse>(a, s) : run_dq<D, E, false, 4, kMse>(a, s);
+        }
+        break;
+    case kDriveBiased:
+    case kDriveUnbiased:
+        return f16 ? run_dq<D, E, true, 1, kDriveBiased>(a, s) : run_dq<D, E, false, 1, kDriveBiased>(a, s);
+    case kResidual:
+        switch (bits) {
+        case 2: return f16 ? run_dq<D, E, true, 2, kResidual>(a, s) : run_dq<D, E, false, 2, kResidual>(a, s);
+        case 3: return f16 ? run_dq<D, E, true, 3, kResidual>(a, s) : run_dq<D, E, false, 3, kResidual>(a, s);
+        case 4: return f16 ? run_dq<D, E, true, 4, kResidual>(a, s) : run_dq<D, E, false, 4, kResidual>(a, s);
+        }
+        break;
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int D, int BITS>
+hipError_t run_score(const ScoreArgs &a, hipStream_t s) {
+    const int64_t tiles = (a.n + 31) / 32;
+    int64_t blocks = (tiles + kWaves - 1) / kWaves;
+    const int64_t cap = (int64_t)device_cu_count() * 2;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL((k_score<D, BITS>), dim3((int)blocks), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t score_d(int bits, const ScoreArgs &a, hipStream_t s) {
+    switch (bits) {
+    case 1: return run_score<D, 1>(a, s);
+    case 2: return run_score<D, 2>(a, s);
+    case 3: return run_score<D, 3>(a, s);
+    case 4: return run_score<D, 4>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_quantize(int d, bool f16, int bits, Kind kind, int layout, const QuantArgs &a,
+                           hipStream_t s) {
+    switch (d) {
+    case 32: return quant_d<32>(f16, bits, kind, layout, a, s);
+    case 64: return quant_d<64>(f16, bits, kind, layout, a, s);
+    case 128: return quant_d<128>(f16, bits, kind, layout, a, s);
+    case 256: return quant_d<256>(f16, bits, kind, layout, a, s);
+    case 512: return quant_d<512>(f16, bits, kind, layout, a, s);
+    case 1024: return quant_d<1024>(f16, bits, kind, layout, a, s);
+    case 2048: return quant_d<2048>(f16, bits, kind, layout, a, s);
+    case 4096: return quant_d<4096>(f16, bits, kind, layout, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_dequantize(int d, bool f16out, int bits, Kind kind, int layout,
+                             const DequantArgs &a, hipStream_t s) {
+    switch (d) {
+    case 32: return dequant_d<32>(f16out, bits, kind, layout, a, s);
+    case 64: return dequant_d<64>(f16out, bits, kind, layout, a, s);
+    case 128: return dequant_d<128>(f16out, bits, kind, layout, a, s);
+    case 256: return dequant_d<256>(f16out, bits, kind, layout, a, s);
+    case 512: return dequant_d<512>(f16out, bits, kind, layout, a, s);
+    case 1024: return dequant_d<1024>(f16out, bits, kind, layout, a, s);
+    case 2048: return dequant_d<2048>(f16out, bits, kind, layout, a, s);
+    case 4096: return dequant_d<4096>(f16out, bits, kind, layout, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_score(int d, int bits, const ScoreArgs &a, hipStream_t s) {
+    switch (d) {
+    case 64: return score_d<64>(bits, a, s);
+    case 128: return score_d<128>(bits, a, s);
+    case 256: return score_d<256>(bits, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace rht

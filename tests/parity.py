@@ -1,0 +1,107 @@
+"""Comparison rules shared by the GPU parity tests (GPU result vs CPU oracle).
+
+* Codes / sign bits: bit-exact, except that a coordinate may differ by exactly
+  one level when the oracle's fp64 normalized value y lies within 1e-5 *
+  max(1, |t|) of the decision threshold t between the two codes.  Such
+  near-threshold mismatches are counted and must stay below 1e-6 of all codes
+  (at least one is tolerated when 1e-6 of the count is below one code).
+* Norms: relative 1e-6.  Scales S, S_r: relative 1e-5.
+* Reconstructions and scores are compared on identical code bytes (the oracle
+  decodes the GPU's codes), per row and globally, relative L2 <= 1e-5 for fp32
+  outputs and 2e-3 for fp16 outputs.
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import os
+
+import numpy as np
+
+NEAR_REL = 1e-5
+MAX_NEAR_FRAC = 1e-6
+NORM_RTOL = 1e-6
+SCALE_RTOL = 1e-5
+RECON_F32 = 1e-5
+RECON_F16 = 2e-3
+SCORE_TOL = 1e-5
+
+
+def unpack(codes: np.ndarray, width: int, d: int) -> np.ndarray:
+    bits = np.unpackbits(np.ascontiguousarray(codes), axis=-1, bitorder="little")[..., : width * d]
+    bits = bits.reshape(*codes.shape[:-1], d, width).astype(np.int16)
+    return (bits << np.arange(width, dtype=np.int16)).sum(-1).astype(np.int16)
+
+
+def threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def chunked(fn, n: int, parts: int | None = None):
+    """Run fn(lo, hi) over row ranges in threads (the oracle releases the GIL)."""
+    parts = parts or threads()
+    edges = np.linspace(0, n, parts + 1).astype(np.int64)
+    with concurrent.futures.ThreadPoolExecutor(parts) as ex:
+        return list(ex.map(lambda i: fn(int(edges[i]), int(edges[i + 1])), range(parts)))
+
+
+def check_codes(gpu: np.ndarray, ref: np.ndarray, y_of_rows, thresholds: np.ndarray,
+                what: str) -> int:
+    """gpu/ref: unpacked int codes [n][d].  y_of_rows(rows) -> fp64 y for those
+    rows.  thresholds[k] separates code k and k+1.  Returns the number of
+    near-threshold mismatches; raises on any other mismatch."""
+    diff = gpu != ref
+    nmis = int(diff.sum())
+    if nmis == 0:
+        return 0
+    rows = np.unique(np.nonzero(diff)[0])
+    y = y_of_rows(rows)
+    g, r = gpu[rows], ref[rows]
+    bad = []
+    near = 0
+    for i, j in zip(*np.nonzero(g != r)):
+        lo = min(int(g[i, j]), int(r[i, j]))
+        if abs(int(g[i, j]) - int(r[i, j])) != 1:
+            bad.append((rows[i], j, int(g[i, j]), int(r[i, j]), y[i, j]))
+            continue
+        t = float(thresholds[lo])
+        if abs(y[i, j] - t) <= NEAR_REL * max(1.0, abs(t)):
+            near += 1
+        else:
+            bad.append((rows[i], j, int(g[i, j]), int(r[i, j]), y[i, j]))
+    assert not bad, "%s: %d code mismatches away from a threshold, e.g. %s" % (what, len(bad), bad[:5])
+    total = gpu.size
+    assert near <= max(1, MAX_NEAR_FRAC * total), \
+        "%s: %d near-threshold mismatches in %d codes" % (what, near, total)
+    return near
+
+
+def rel_l2(a: np.ndarray, b: np.ndarray, axis=None):
+    a = a.astype(np.float64)
+    b = b.astype(np.float64)
+    num = np.sqrt(((a - b) ** 2).sum(axis=axis))
+    den = np.sqrt((b ** 2).sum(axis=axis))
+    return num / np.maximum(den, 1e-300)
+
+
+def check_recon(gpu: np.ndarray, ref: np.ndarray, tol: float, what: str):
+    ref64 = ref.astype(np.float64)
+    nz = (ref64 ** 2).sum(1) > 0
+    per_row = rel_l2(gpu[nz], ref[nz], axis=1)
+    glob = rel_l2(gpu, ref)
+    assert per_row.size == 0 or per_row.max() <= tol, \
+        "%s: worst row rel L2 %.3g > %.1g (row %d)" % (what, per_row.max(), tol,
+                                                     np.nonzero(nz)[0][per_row.argmax()])
+    assert glob <= tol, "%s: global rel L2 %.3g > %.1g" % (what, glob, tol)
+    # rows whose reference is exactly zero must decode to exactly zero
+    assert np.all(gpu[~nz] == 0), "%s: zero rows not decoded to zero" % what
+    return float(glob), float(per_row.max()) if per_row.size else 0.0
+
+
+def check_rel(gpu: np.ndarray, ref: np.ndarray, rtol: float, what: str):
+    gpu = gpu.astype(np.float64)
+    ref = ref.astype(np.float64)
+    err = np.abs(gpu - ref) / np.maximum(np.abs(ref), 1e-30)
+    err[(ref == 0) & (gpu == 0)] = 0
+    assert err.max() <= rtol, "%s: max rel err %.3g > %.1g at %d (gpu %r ref %r)" % (
+        what, err.max(), rtol, err.argmax(), gpu.flat[err.argmax()], ref.flat[err.argmax()])
+    return float(err.max())

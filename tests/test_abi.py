@@ -1,0 +1,112 @@
+"""Host-side checks of the C ABI that need no GPU: every symbol declared in
+include/rht.h is exported, the host helpers agree with the oracle, and argument
+validation returns the documented status before anything touches a device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import rotation_vector_quantization_amd as rht
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rht.h")
+
+OK, E_NULL, E_DIM, E_BITS, E_DTYPE, E_MODE, E_ALIGN, E_COUNT, E_DEVICE = range(9)
+FAKE = 0x10000  # never dereferenced: validation fails (or n == 0) before any use
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rht.library_path()):
+        pytest.fail("librht.so is not built; run __graft_entry__.build() first")
+    return rht.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rht_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 9, names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version(lib):
+    assert rht.rht_abi_version() == 1
+    for s in range(9):
+        assert isinstance(rht.rht_status_str(s), str) and rht.rht_status_str(s)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_codebook_matches_oracle(lib, bits):
+    lv, th = rht.rht_codebook(bits)
+    olv, oth, _, _ = oracle.lloyd_max(bits)
+    # library (own solver, fp32) vs oracle rounded to fp32: within 1 ulp
+    ulp_l = np.spacing(np.abs(olv).astype(np.float32))
+    assert np.all(np.abs(lv - olv.astype(np.float32)) <= ulp_l)
+    oth32 = oth.astype(np.float32)
+    ulp_t = np.spacing(np.maximum(np.abs(oth32), np.float32(1e-30)))
+    assert np.all(np.abs(th - oth32) <= ulp_t)
+    assert th[len(th) // 2] == 0.0
+    assert np.all(lv == -lv[::-1])
+
+
+@pytest.mark.parametrize("seed,d", [(0, 3), (42, 128), (2 ** 64 - 1, 4096), (12345, 1000)])
+def test_signs_match_oracle(lib, seed, d):
+    np.testing.assert_array_equal(rht.rht_signs(seed, d), oracle.signs(seed, d))
+
+
+def _q(lib, x=FAKE, xt=0, n=1, d=128, bits=4, mode=0, codes=FAKE, scale=FAKE):
+    return lib.rht_quantize(x, xt, n, d, bits, mode, 1, codes, scale, None)
+
+
+def test_quantize_validation_order(lib):
+    assert _q(lib, n=-1, d=100) == E_COUNT
+    for d in (0, 16, 100, 8192, -128):
+        assert _q(lib, d=d) == E_DIM
+    for b in (0, 5, -1):
+        assert _q(lib, bits=b) == E_BITS
+    assert _q(lib, mode=3) == E_MODE
+    assert _q(lib, mode=1, bits=2) == E_MODE
+    assert _q(lib, mode=2, bits=4) == E_MODE
+    assert _q(lib, xt=2) == E_DTYPE
+    assert _q(lib, n=0, x=0, codes=0, scale=0) == OK          # no-op, pointers unused
+    assert _q(lib, x=0) == E_NULL
+    assert _q(lib, codes=0) == E_NULL
+    assert _q(lib, scale=0) == E_NULL
+    assert _q(lib, x=FAKE + 8) == E_ALIGN
+    assert _q(lib, scale=FAKE + 4) == E_ALIGN
+
+
+def test_other_entry_points_validate(lib):
+    L = lib
+    assert L.rht_dequantize(FAKE, FAKE, 1, 128, 4, 0, 1, FAKE, 5, None) == E_DTYPE
+    assert L.rht_dequantize(FAKE, FAKE, 1, 128, 2, 1, 1, FAKE, 0, None) == E_MODE
+    assert L.rht_dequantize(0, FAKE, 1, 128, 4, 0, 1, FAKE, 0, None) == E_NULL
+    assert L.rht_dequantize(FAKE, FAKE, 0, 128, 4, 0, 1, 0, 0, None) == OK
+    assert L.rht_residual_quantize(FAKE, 0, 1, 128, 1, 1, FAKE, FAKE, FAKE, FAKE, None) == E_BITS
+    assert L.rht_residual_quantize(FAKE, 0, 1, 128, 5, 1, FAKE, FAKE, FAKE, FAKE, None) == E_BITS
+    assert L.rht_residual_quantize(FAKE, 0, 1, 96, 3, 1, FAKE, FAKE, FAKE, FAKE, None) == E_DIM
+    assert L.rht_residual_quantize(FAKE, 0, 1, 128, 3, 1, FAKE, 0, FAKE, FAKE, None) == E_NULL
+    assert L.rht_residual_dequantize(FAKE, FAKE, FAKE, FAKE + 2, 1, 256, 3, 1, FAKE, 1, None) == E_ALIGN
+    assert L.rht_score(FAKE, 65, FAKE, FAKE, 1, 128, 4, 1, FAKE, None) == E_COUNT
+    assert L.rht_score(FAKE, -1, FAKE, FAKE, 1, 128, 4, 1, FAKE, None) == E_COUNT
+    assert L.rht_score(FAKE, 8, FAKE, FAKE, 1, 512, 4, 1, FAKE, None) == E_DIM
+    assert L.rht_score(FAKE, 8, FAKE, FAKE, 1, 128, 0, 1, FAKE, None) == E_BITS
+    assert L.rht_score(0, 0, 0, 0, 5, 128, 4, 1, 0, None) == OK
+    assert L.rht_codebook(0, None, None) == E_BITS
+    assert L.rht_signs(1, 8, None) == E_NULL
+    assert L.rht_signs(1, 0, FAKE) == E_DIM
+
+
+def test_binding_rejects_cpu_tensors(lib):
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        rht.quantize(torch.zeros(4, 128), 4, 1)
