@@ -14,8 +14,11 @@ ARCH = os.environ.get("RHT_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 instructions stay off: hipcc -O3 would otherwise form
 # v_pk_add/mul/fma_f32 from scalar float code.
+# MFMA accumulators are kept in ordinary VGPRs (the results feed VALU code
+# directly instead of going through v_accvgpr_read).
 DEVICE_FLAGS = ["-O3", "-fPIC", "-std=c++17", "--offload-arch=" + ARCH,
-                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall"]
+                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form", "-Wall"]
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall"]
 
 

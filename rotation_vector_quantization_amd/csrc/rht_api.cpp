@@ -117,6 +117,14 @@ std::atomic<int> g_cu[64];
 
 }  // namespace
 
+bool hadamard_on_mfma() {
+    static const bool v = [] {
+        const char *e = std::getenv("RHT_HADAMARD");
+        return !(e && std::strcmp(e, "valu") == 0);
+    }();
+    return v;
+}
+
 int blocks_per_cu_cap() {
     static const int v = [] {
         const char *e = std::getenv("RHT_BLOCKS_PER_CU");

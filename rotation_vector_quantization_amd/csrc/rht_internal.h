@@ -73,4 +73,8 @@ int device_cu_count();
 // limit); read once from RHT_BLOCKS_PER_CU, a launch-shape tuning knob.
 int blocks_per_cu_cap();
 
+// Whether the d = 128, fp16, 4-bit MSE kernels run the H_32 factor of the
+// transform on MFMA (default) or as register/DPP butterflies (RHT_HADAMARD=valu).
+bool hadamard_on_mfma();
+
 }  // namespace rht
