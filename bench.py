@@ -96,6 +96,98 @@ def traffic_from(fetch_dir, write_dir):
     print(json.dumps(rec, indent=1))
 
 
+def time_launches(torch, stream, fn, sets, iters=20, warmup=3):
+    """Average ms per call of fn(set_index) over `iters` calls cycling through
+    `sets` buffer sets, timed with HIP events on `stream`."""
+    for i in range(warmup):
+        fn(i % sets)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(iters):
+        fn(i % sets)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def other_workloads(torch, rht, dev, stream):
+    """The other hot-path rows, each at its full workload size: DRIVE 1-bit
+    (65536 x 1024 fp32, both scales), the residual chain (2^20 x 256 fp16,
+    2+1 bits) and rotated-domain scoring (131072 4-bit keys x 64 queries).
+    Working sets under 512 MB are rotated over several buffer sets so the
+    256 MB Infinity Cache cannot serve repeats."""
+    import testdata
+
+    sh = stream.cuda_stream
+    out = {}
+
+    def hbm(name, units, unit, bytes_per_unit, ms):
+        gbs = units * bytes_per_unit / (ms / 1e3) / 1e9
+        return {"ms_per_launch": ms, unit + "_per_s": units / (ms / 1e3), "bytes_per_" + unit: bytes_per_unit,
+                "GB_per_s": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS, "bound": "hbm"}
+
+    # DRIVE, C3: two input sets (2 x 256 MiB)
+    w3 = testdata.WORKLOADS["c3"]
+    xs = [torch.from_numpy(testdata.generate(w3)).to(dev)]
+    xs.append(torch.roll(xs[0], 1, 0))
+    n3, d3 = w3.n, w3.d
+    b3 = [torch.empty((n3, d3 // 8), dtype=torch.uint8, device=dev) for _ in range(2)]
+    s3 = [torch.empty((n3,), dtype=torch.float32, device=dev) for _ in range(2)]
+    y3 = [torch.empty((n3, d3), dtype=torch.float32, device=dev) for _ in range(2)]
+    per3 = d3 * 4 + d3 // 8 + 4
+    for mode, tag in ((rht.SCALE_SIGN_BIASED, "biased"), (rht.SCALE_SIGN_UNBIASED, "unbiased")):
+        qms = time_launches(torch, stream, lambda i: rht.rht_quantize(
+            xs[i].data_ptr(), rht.F32, n3, d3, 1, mode, w3.rot_seed, b3[i].data_ptr(), s3[i].data_ptr(), sh), 2)
+        dms = time_launches(torch, stream, lambda i: rht.rht_dequantize(
+            b3[i].data_ptr(), s3[i].data_ptr(), n3, d3, 1, mode, w3.rot_seed, y3[i].data_ptr(), rht.F32, sh), 2)
+        out["drive_" + tag] = {"workload": "65536 x 1024 fp32 Student-t, 1-bit signs + S, decode to fp32",
+                               "quantize": hbm("q", n3, "chunk", per3, qms),
+                               "dequantize": hbm("d", n3, "chunk", per3, dms)}
+    del xs, b3, s3, y3
+
+    # residual chain, C4: 512 MiB input, one set suffices
+    w4 = testdata.WORKLOADS["c4"]
+    x4 = torch.from_numpy(testdata.generate(w4)).to(dev)
+    n4, d4, bt = w4.n, w4.d, w4.bits
+    c4 = torch.empty((n4, (bt - 1) * d4 // 8), dtype=torch.uint8, device=dev)
+    g4 = torch.empty((n4, d4 // 8), dtype=torch.uint8, device=dev)
+    nr4 = torch.empty((n4,), dtype=torch.float32, device=dev)
+    r4 = torch.empty_like(nr4)
+    y4 = torch.empty((n4, d4), dtype=torch.float16, device=dev)
+    per4 = d4 * 2 + (bt - 1) * d4 // 8 + d4 // 8 + 8
+    qms = time_launches(torch, stream, lambda i: rht.rht_residual_quantize(
+        x4.data_ptr(), rht.F16, n4, d4, bt, w4.rot_seed, c4.data_ptr(), g4.data_ptr(), nr4.data_ptr(),
+        r4.data_ptr(), sh), 1)
+    dms = time_launches(torch, stream, lambda i: rht.rht_residual_dequantize(
+        c4.data_ptr(), g4.data_ptr(), nr4.data_ptr(), r4.data_ptr(), n4, d4, bt, w4.rot_seed, y4.data_ptr(),
+        rht.F16, sh), 1)
+    out["residual"] = {"workload": "16 x 65536 x 256 fp16, 5 outlier channels x30, 2-bit + 1-bit residual sign",
+                       "quantize": hbm("q", n4, "vector", per4, qms), "dequantize": hbm("d", n4, "vector", per4, dms)}
+    del x4, c4, g4, nr4, r4, y4
+
+    # scoring, C5: 16 key/logit sets (16 x 42.5 MB) rotated
+    wk, wq = testdata.WORKLOADS["c5k"], testdata.WORKLOADS["c5q"]
+    keys = torch.from_numpy(testdata.generate(wk)).to(dev)
+    q = torch.from_numpy(testdata.generate(wq)).to(dev)
+    nk, d5, b5, m = wk.n, wk.d, wk.bits, wq.n
+    c5, n5 = rht.quantize(keys, b5, wk.rot_seed)
+    sets = 16
+    cs = [c5.clone() for _ in range(sets)]
+    ns = [n5.clone() for _ in range(sets)]
+    ls = [torch.empty((m, nk), dtype=torch.float32, device=dev) for _ in range(sets)]
+    sms = time_launches(torch, stream, lambda i: rht.rht_score(
+        q.data_ptr(), m, cs[i].data_ptr(), ns[i].data_ptr(), nk, d5, b5, wk.rot_seed, ls[i].data_ptr(), sh), sets)
+    flops = 2.0 * m * nk * d5
+    sbytes = nk * (d5 * b5 // 8 + 4) + m * d5 * 4 + m * nk * 4
+    tfs = flops / (sms / 1e3) / 1e12
+    out["score"] = {"workload": "131072 keys d=128 4-bit codes + norms, 64 fp32 queries, fp32 logits",
+                    "ms_per_launch": sms, "keys_per_s": nk / (sms / 1e3), "TFLOP_per_s": tfs,
+                    "frac_of_fp32_mfma_peak": tfs / 157.3, "GB_per_s": sbytes / (sms / 1e3) / 1e9,
+                    "bound": "mfma fp32 (157.3 TFLOP/s)"}
+    return out
+
+
 def cpu_baseline(rows):
     import oracle
     import testdata
@@ -118,6 +210,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-rows", type=int, default=1 << 20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip timing the DRIVE, residual and scoring workloads")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_c2_kv.json from rocprofv3 PMC runs and exit")
     args = ap.parse_args()
@@ -256,6 +350,11 @@ def main():
         "wall_s_timed_region": wall,
         "cpu_baseline": None,
     }
+    if not args.no_other_workloads:
+        del xk, xv, ck, cv, nk, nv, yk, yv
+        torch.cuda.empty_cache()
+        print("timing the DRIVE, residual and scoring workloads", file=sys.stderr, flush=True)
+        out["other_workloads"] = other_workloads(torch, rht, dev, stream)
     if not args.no_cpu_baseline:
         print("timing the CPU oracle on %d vectors" % args.cpu_rows, file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args.cpu_rows)
