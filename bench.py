@@ -33,7 +33,8 @@ COPY_BYTES = 8388608 * BYTES_PER_VECTOR // 2  # plain copy moving one launch's b
 
 def source_digest():
     h = hashlib.sha256()
-    for f in ("rht_kernels.hip", "rht_api.cpp", "rht_internal.h"):
+    # the sources the timed d = 128 kernels are compiled from
+    for f in ("rht_kv128.hip", "rht_device.h"):
         with open(os.path.join(ROOT, "rotation_vector_quantization_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -96,19 +97,34 @@ def traffic_from(fetch_dir, write_dir):
     print(json.dumps(rec, indent=1))
 
 
-def time_launches(torch, stream, fn, sets, iters=20, warmup=3):
-    """Average ms per call of fn(set_index) over `iters` calls cycling through
-    `sets` buffer sets, timed with HIP events on `stream`."""
-    for i in range(warmup):
-        fn(i % sets)
+def time_launches(torch, stream, fn, sets, iters=20, warm_ms=50.0):
+    """Per-launch times (ms) of fn(set_index), cycling through `sets` buffer
+    sets, from HIP events recorded on `stream` between launches.  The kernel
+    first runs untimed for about warm_ms of GPU time, so clocks that dropped
+    during host-side set-up have ramped up again."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     e0.record(stream)
-    for i in range(iters):
+    for i in range(3):
         fn(i % sets)
     e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / iters
+    est = max(e0.elapsed_time(e1) / 3, 1e-3)
+    for i in range(min(int(warm_ms / est), 5000)):
+        fn(i % sets)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(iters):
+        fn(i % sets)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(iters)])
+
+
+def stats(ms):
+    """mean / median / min / max of per-launch times in ms."""
+    return {"ms_per_launch": float(np.mean(ms)), "ms_median": float(np.median(ms)),
+            "ms_min": float(np.min(ms)), "ms_max": float(np.max(ms))}
 
 
 def other_workloads(torch, rht, dev, stream):
@@ -122,10 +138,12 @@ def other_workloads(torch, rht, dev, stream):
     sh = stream.cuda_stream
     out = {}
 
-    def hbm(name, units, unit, bytes_per_unit, ms):
+    def hbm(name, units, unit, bytes_per_unit, times):
+        st = stats(times)
+        ms = st["ms_median"]
         gbs = units * bytes_per_unit / (ms / 1e3) / 1e9
-        return {"ms_per_launch": ms, unit + "_per_s": units / (ms / 1e3), "bytes_per_" + unit: bytes_per_unit,
-                "GB_per_s": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS, "bound": "hbm"}
+        return dict(st, **{unit + "_per_s": units / (ms / 1e3), "bytes_per_" + unit: bytes_per_unit,
+                           "GB_per_s": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS, "bound": "hbm"})
 
     # DRIVE, C3: two input sets (2 x 256 MiB)
     w3 = testdata.WORKLOADS["c3"]
@@ -180,11 +198,13 @@ def other_workloads(torch, rht, dev, stream):
         q.data_ptr(), m, cs[i].data_ptr(), ns[i].data_ptr(), nk, d5, b5, wk.rot_seed, ls[i].data_ptr(), sh), sets)
     flops = 2.0 * m * nk * d5
     sbytes = nk * (d5 * b5 // 8 + 4) + m * d5 * 4 + m * nk * 4
+    st = stats(sms)
+    sms = st["ms_median"]
     tfs = flops / (sms / 1e3) / 1e12
-    out["score"] = {"workload": "131072 keys d=128 4-bit codes + norms, 64 fp32 queries, fp32 logits",
-                    "ms_per_launch": sms, "keys_per_s": nk / (sms / 1e3), "TFLOP_per_s": tfs,
-                    "frac_of_fp32_mfma_peak": tfs / 157.3, "GB_per_s": sbytes / (sms / 1e3) / 1e9,
-                    "bound": "mfma fp32 (157.3 TFLOP/s)"}
+    out["score"] = dict(st, **{"workload": "131072 keys d=128 4-bit codes + norms, 64 fp32 queries, fp32 logits",
+                               "keys_per_s": nk / (sms / 1e3), "TFLOP_per_s": tfs,
+                               "frac_of_fp32_mfma_peak": tfs / 157.3, "GB_per_s": sbytes / (sms / 1e3) / 1e9,
+                               "bound": "mfma fp32 (157.3 TFLOP/s)"})
     return out
 
 
@@ -207,7 +227,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--cpu-rows", type=int, default=1 << 20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
@@ -257,22 +277,20 @@ def main():
                            y.data_ptr(), rht.F16, sh)
 
     def step(ev=None):
+        calls = (lambda: q(xk, ck, nk, wk), lambda: q(xv, cv, nv, wv),
+                 lambda: dq(ck, nk, yk, wk), lambda: dq(cv, nv, yv, wv))
         if ev is not None:
             ev[0].record(stream)
-        q(xk, ck, nk, wk)
-        q(xv, cv, nv, wv)
-        if ev is not None:
-            ev[1].record(stream)
-        dq(ck, nk, yk, wk)
-        dq(cv, nv, yv, wv)
-        if ev is not None:
-            ev[2].record(stream)
+        for i, call in enumerate(calls):
+            call()
+            if ev is not None:
+                ev[i + 1].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -283,8 +301,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / args.steps
-    q_ms = np.array([e[0].elapsed_time(e[1]) for e in evs]) / 2.0  # per launch
-    dq_ms = np.array([e[1].elapsed_time(e[2]) for e in evs]) / 2.0
+    # per launch: [quantize K, quantize V, dequantize K, dequantize V] of every step
+    per = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])
+    q_ms = per[:, 0:2].ravel()
+    dq_ms = per[:, 2:4].ravel()
     # practical ceiling: a plain device copy moving the same bytes as one launch
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -300,6 +320,12 @@ def main():
     copy_ms = c0.elapsed_time(c1) / 10
     copy_gbs = 2 * COPY_BYTES / (copy_ms / 1e3) / 1e9
     del src, dst
+
+    def direction(ms):
+        st = stats(ms)
+        gbs = per_launch_bytes / (st["ms_per_launch"] / 1e3) / 1e9
+        return dict(st, vectors_per_s=n / (st["ms_per_launch"] / 1e3), GB_per_s=gbs,
+                    frac_of_peak=gbs / HBM_PEAK_GBS)
 
     vectors_per_step = 2 * n
     value = vectors_per_step / (ms_step / 1e3)
@@ -335,16 +361,9 @@ def main():
             "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
         },
-        "per_direction": {
-            "quantize": {"ms_per_launch": kern["quantize"],
-                         "vectors_per_s": n / (kern["quantize"] / 1e3),
-                         "GB_per_s": per_launch_bytes / (kern["quantize"] / 1e3) / 1e9,
-                         "frac_of_peak": per_launch_bytes / (kern["quantize"] / 1e3) / 1e9 / HBM_PEAK_GBS},
-            "dequantize": {"ms_per_launch": kern["dequantize"],
-                           "vectors_per_s": n / (kern["dequantize"] / 1e3),
-                           "GB_per_s": per_launch_bytes / (kern["dequantize"] / 1e3) / 1e9,
-                           "frac_of_peak": per_launch_bytes / (kern["dequantize"] / 1e3) / 1e9 / HBM_PEAK_GBS},
-        },
+        "per_direction": {k: direction(v) for k, v in (("quantize", q_ms), ("dequantize", dq_ms))},
+        "per_tensor": {k: direction(per[:, i]) for i, k in enumerate(
+            ("quantize_K", "quantize_V", "dequantize_K", "dequantize_V"))},
         "copy_ceiling": {"GB_per_s": copy_gbs, "frac_of_peak": copy_gbs / HBM_PEAK_GBS,
                          "bytes": 2 * COPY_BYTES, "kernel": "torch device copy"},
         "wall_s_timed_region": wall,

@@ -33,19 +33,21 @@ def _run(cmd):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    jobs = [
-        ["hipcc"] + DEVICE_FLAGS + ["-c", os.path.join(CSRC, "rht_kernels.hip"),
-                                    "-o", os.path.join(BUILD, "rht_kernels.o")],
-        ["hipcc"] + HOST_FLAGS + ["-c", os.path.join(CSRC, "rht_api.cpp"),
-                                  "-o", os.path.join(BUILD, "rht_api.o")],
-    ]
-    with concurrent.futures.ThreadPoolExecutor(len(jobs)) as ex:
+    jobs, objs = [], []
+    for src in sorted(os.listdir(CSRC)):
+        stem, ext = os.path.splitext(src)
+        if ext not in (".hip", ".cpp"):
+            continue
+        obj = os.path.join(BUILD, stem + ".o")
+        flags = DEVICE_FLAGS if ext == ".hip" else HOST_FLAGS
+        jobs.append(["hipcc"] + flags + ["-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    with concurrent.futures.ThreadPoolExecutor(min(len(jobs), 8)) as ex:
         for out in ex.map(_run, jobs):
             if verbose and out.strip():
                 print(out)
     tmp = LIB + ".tmp%d" % os.getpid()
-    _run(["hipcc", "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp,
-          os.path.join(BUILD, "rht_kernels.o"), os.path.join(BUILD, "rht_api.o")])
+    _run(["hipcc", "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs)
     os.replace(tmp, LIB)
     return LIB
 

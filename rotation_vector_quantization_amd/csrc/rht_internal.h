@@ -66,6 +66,11 @@ hipError_t launch_dequantize(int d, bool f16out, int bits, Kind kind, int layout
                              const DequantArgs &a, hipStream_t s);
 hipError_t launch_score(int d, int bits, const ScoreArgs &a, hipStream_t s);
 
+// The d = 128, fp16, 4-bit MSE encoder and decoder with the H_32 factor on
+// MFMA (launch_quantize / launch_dequantize pick them for that case).
+hipError_t launch_quantize_kv128(const QuantArgs &a, hipStream_t s);
+hipError_t launch_dequantize_kv128(const DequantArgs &a, hipStream_t s);
+
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 

@@ -33,20 +33,10 @@
 // cell's lower end and the one scaled threshold that may fall inside the cell,
 // so the code is base + [y16 >= T].  The final decision compares fp32 y16 with
 // the exact scaled fp32 threshold (scaling by 16 is exact).
-#include "rht_internal.h"
+#include "rht_device.h"
 
 namespace rht {
 namespace {
-
-constexpr int kBlock = 256;
-constexpr int kWaves = kBlock / 64;
-
-__host__ __device__ constexpr int lanes_per_vec(int d) { return d >= 4096 ? 64 : d / 32; }
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63u; }
 
 // Value of v in lane (lane ^ M); M < lanes of one vector.
 template <int M>
@@ -171,11 +161,6 @@ __device__ __forceinline__ uint64_t lane_sign_bits(const uint32_t *dsign, uint32
     return m;
 }
 
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
-                                  false);
-}
-
 // Raw input words a lane holds for one vector: E fp16 (E/2 words) or E fp32.
 template <int D, bool F16>
 struct Raw {
@@ -257,15 +242,11 @@ __device__ __forceinline__ float load_signed(const void *x, int64_t vec, uint32_
     return stage0<D, F16>(raw, sw, v);
 }
 
-// Nearest-level table for y16 = 16 * y.  Cell k holds the y16 values with
-// round(y16 + OFF) == k; its entry is (scaled threshold that may lie in the
-// cell or +inf, code at the cell's low end).  Each entry is built for the
-// widened window [k - OFF - 0.75, k - OFF + 1.25), so it stays right whatever
-// the rounding of the index; windows are 2 wide and scaled thresholds are at
-// least 4 apart (16 x the smallest N(0,1) Lloyd-Max gap), so a window holds at
-// most one threshold.
+// The same table with the two candidate levels attached, for encoders that
+// also need c[code]: entry (threshold, base code, 16 c[base], 16 c[base + 1]).
 template <int NCELL, int OFF>
-__device__ __forceinline__ void build_lut(uint2 *lut, const float *thr, int nthr) {
+__device__ __forceinline__ void build_lut_lev(u32x4_t *lut, const float *thr, const float *lev,
+                                              int nthr) {
     for (int k = threadIdx.x; k < NCELL; k += kBlock) {
         const float lo = k == 0 ? -INFINITY : (float)(k - OFF) - 0.75f;
         const float hi = k == NCELL - 1 ? INFINITY : (float)(k - OFF) + 1.25f;
@@ -278,26 +259,22 @@ __device__ __forceinline__ void build_lut(uint2 *lut, const float *thr, int nthr
             else if (t < hi && t_in == INFINITY)
                 t_in = t;
         }
-        lut[k] = make_uint2(__builtin_bit_cast(uint32_t, t_in), base);
+        const uint32_t up = base < (uint32_t)nthr ? base + 1 : base;
+        lut[k] = u32x4_t{__builtin_bit_cast(uint32_t, t_in), base,
+                         __builtin_bit_cast(uint32_t, 16.0f * lev[base]),
+                         __builtin_bit_cast(uint32_t, 16.0f * lev[up])};
     }
 }
 
-// |y16| <= 16 sqrt(d) (|(H D x)_i| <= ||x||_1 <= sqrt(d) ||x||), so for d <= 128
-// a 512-cell table centred on 0 needs no clamp; larger d clamp into 256 cells.
+// nearest_code on the level-carrying table; also returns l16 = 16 c[code].
 template <int D>
-struct Lut {
-    static constexpr bool kClamp = D > 128;
-    static constexpr int kCells = kClamp ? 256 : 512;
-    static constexpr int kOff = kClamp ? 40 : 256;
-};
-
-template <int D>
-__device__ __forceinline__ uint32_t nearest_code(const uint2 *lut, float y16) {
-    // adding 2^23 + OFF leaves round(y16 + OFF) in the low mantissa bits
+__device__ __forceinline__ uint32_t nearest_code_lev(const u32x4_t *lut, float y16, float &l16) {
     int b = __builtin_bit_cast(int, y16 + (8388608.0f + (float)Lut<D>::kOff));
     if constexpr (Lut<D>::kClamp) b = min(max(b, 0x4B000000), 0x4B000000 + Lut<D>::kCells - 1);
-    const uint2 e = lut[b - 0x4B000000];
-    return e.y + (y16 >= __builtin_bit_cast(float, e.x) ? 1u : 0u);
+    const u32x4_t e = lut[b - 0x4B000000];
+    const bool up = y16 >= __builtin_bit_cast(float, e[0]);
+    l16 = __builtin_bit_cast(float, up ? e[3] : e[2]);
+    return e[1] + (up ? 1u : 0u);
 }
 
 // Pack one code of width CB at group-local position t (LSB-first).
@@ -343,6 +320,62 @@ __device__ __forceinline__ void load_words(const uint32_t *src, uint32_t (&w)[WP
 }
 
 // ---------------------------------------------------------------------------
+// LDS staging for the contiguous-run layout (G = E).  A wave's VPW rows are one
+// contiguous tile of 64 * RC 16-byte chunks, RC = chunks per lane run; lane L
+// owns tile chunks L*RC .. L*RC+RC-1.  Global traffic moves the tile in
+// coalesced order (instruction k, lane l: chunk 64k + l); inside LDS chunk c
+// of lane L's run sits at L*RC + (c ^ g(L)), g(L) = (L / (16/RC)) mod RC, so
+// both the coalesced side and the per-lane run side touch 16 distinct bank
+// groups per 16 lanes.
+template <int D, bool F16>
+struct RunStage {
+    static constexpr int E = D / lanes_per_vec(D);
+    static constexpr int ESZ = F16 ? 2 : 4;
+    static constexpr int RC = E * ESZ / 16;  // 16-byte chunks per lane run
+    static constexpr int CPR = D * ESZ / 16; // chunks per row
+    static constexpr bool kOk = RC >= 2 && RC <= 16;
+    static __device__ __forceinline__ uint32_t pos(uint32_t L, uint32_t c) {
+        return L * RC + (c ^ ((L / (16 / RC)) % RC));
+    }
+};
+
+// Coalesced global loads of the wave tile whose first row is row0 (rows past
+// the end read the last row): stg[k] = tile chunk 64k + lane.
+template <int D, bool F16>
+__device__ __forceinline__ void tile_load(const void *x, int64_t row0, int64_t n, uint32_t lane,
+                                          u32x4_t (&stg)[RunStage<D, F16>::RC]) {
+    using S = RunStage<D, F16>;
+#pragma unroll
+    for (int k = 0; k < S::RC; ++k) {
+        const uint32_t T = 64u * k + lane;
+        int64_t row = row0 + T / S::CPR;
+        row = row < n ? row : n - 1;
+        stg[k] = reinterpret_cast<const u32x4_t *>(static_cast<const char *>(x) + row * D * S::ESZ)[T % S::CPR];
+    }
+}
+
+// Hand the coalesced chunks to their owners: stg (coalesced order) -> LDS ->
+// raw (this lane's run, register order).
+template <int D, bool F16>
+__device__ __forceinline__ void tile_to_run(u32x4_t *buf, const u32x4_t (&stg)[RunStage<D, F16>::RC],
+                                            uint32_t lane, uint32_t (&raw)[Raw<D, F16>::W]) {
+    using S = RunStage<D, F16>;
+#pragma unroll
+    for (int k = 0; k < S::RC; ++k) {
+        const uint32_t T = 64u * k + lane;
+        buf[S::pos(T / S::RC, T % S::RC)] = stg[k];
+    }
+#pragma unroll
+    for (int c = 0; c < S::RC; ++c) {
+        const u32x4_t t = buf[S::pos(lane, c)];
+        raw[4 * c] = t[0];
+        raw[4 * c + 1] = t[1];
+        raw[4 * c + 2] = t[2];
+        raw[4 * c + 3] = t[3];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Encoder.  KIND selects the code: MSE (BITS-bit codes + ||x||), DRIVE (1-bit
 // signs + S), residual chain (BITS-1 bit codes + sign plane + ||x|| + S_r).
 template <int D, int G, bool F16, int BITS, int KIND>
@@ -356,11 +389,14 @@ __global__ __launch_bounds__(kBlock) void k_quantize(const QuantArgs a) {
     static_assert(KIND != kResidual || G % 32 == 0, "residual sign words need 32-coordinate groups");
     constexpr int ROWW = D * CB / 32;  // code words per row
 
-    __shared__ uint2 lut[Lut<D>::kCells];
-    __shared__ float slev[16];
-    if constexpr (!DRIVE) {
+    constexpr bool RES = KIND == kResidual;
+    __shared__ uint2 lut[DRIVE || RES ? 1 : Lut<D>::kCells];
+    __shared__ u32x4_t lutl[RES ? Lut<D>::kCells : 1];
+    if constexpr (RES) {
+        build_lut_lev<Lut<D>::kCells, Lut<D>::kOff>(lutl, a.thr, a.lev, (1 << CB) - 1);
+        __syncthreads();
+    } else if constexpr (!DRIVE) {
         build_lut<Lut<D>::kCells, Lut<D>::kOff>(lut, a.thr, (1 << CB) - 1);
-        if (threadIdx.x < 16) slev[threadIdx.x] = a.lev[threadIdx.x];
         __syncthreads();
     }
 
@@ -369,20 +405,34 @@ __global__ __launch_bounds__(kBlock) void k_quantize(const QuantArgs a) {
     const float fq = lane_factor(q);
     const float sqrt_d = __builtin_sqrtf((float)D);
 
+    // contiguous runs (G = E) go through the LDS tile for coalesced loads;
+    // not the residual encoder, whose VALU work already bounds it and which
+    // loses more to the staging instructions and registers than it gains
+    constexpr bool STAGE = (G == E) && RunStage<D, F16>::kOk && KIND != kResidual;
+    using RS = RunStage<D, F16>;
+    __shared__ u32x4_t sbuf[STAGE ? kWaves * 64 * RS::RC : 1];
+    u32x4_t stg[STAGE ? RS::RC : 1];
     uint32_t sw[Raw<D, F16>::W], raw[Raw<D, F16>::W];
     sign_words<D, F16>(lsign, sw);
     const int64_t stride = (int64_t)gridDim.x * VPB;
     {
         const int64_t vec = (int64_t)blockIdx.x * VPB + wave * VPW + slot;
-        load_raw<D, G, F16>(a.x, vec < a.n ? vec : a.n - 1, q, raw);
+        if constexpr (STAGE)
+            tile_load<D, F16>(a.x, (int64_t)blockIdx.x * VPB + wave * VPW, a.n, lane, stg);
+        else
+            load_raw<D, G, F16>(a.x, vec < a.n ? vec : a.n - 1, q, raw);
     }
     for (int64_t v0 = (int64_t)blockIdx.x * VPB; v0 < a.n; v0 += stride) {
         const int64_t vec = v0 + wave * VPW + slot;
         const bool valid = vec < a.n;
         float v[E];
+        if constexpr (STAGE) tile_to_run<D, F16>(sbuf + wave * 64 * RS::RC, stg, lane, raw);
         float ss = stage0<D, F16>(raw, sw, v);
         // the next vector's loads are in flight while this one is transformed
-        load_raw<D, G, F16>(a.x, vec + stride < a.n ? vec + stride : a.n - 1, q, raw);
+        if constexpr (STAGE)
+            tile_load<D, F16>(a.x, v0 + stride + wave * VPW, a.n, lane, stg);
+        else
+            load_raw<D, G, F16>(a.x, vec + stride < a.n ? vec + stride : a.n - 1, q, raw);
         fwht_regs<E, F16 ? 1 : 0>(v);
         fwht_lanes<LPV>(v, q);
         ss = vec_sum<LPV>(ss);
@@ -418,36 +468,45 @@ __global__ __launch_bounds__(kBlock) void k_quantize(const QuantArgs a) {
             const float nrm = sqrtf(ss);
             const float inv16 = ss > 0.0f ? fq * (16.0f / nrm) : 0.0f;
             uint32_t w[NG][WPG];
-            uint32_t sw[NG][KIND == kResidual ? G / 32 : 1];
+            uint32_t sw[NG][RES ? G / 32 : 1];
             float r2 = 0.0f, r1 = 0.0f;
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
 #pragma unroll
                 for (int i = 0; i < WPG; ++i) w[gi][i] = 0u;
-                if constexpr (KIND == kResidual) {
+                if constexpr (RES) {
+                    // residual in units of y16: rho16 = y16 - 16 c[code] = 16 (h - ||x|| c) / ||x||.
+                    // Sign bits enter at the bottom of a shifted word, highest t first,
+                    // as 1 = negative; the word is inverted afterwards.
 #pragma unroll
-                    for (int i = 0; i < G / 32; ++i) sw[gi][i] = 0u;
-                }
+                    for (int i = 0; i < G / 32; ++i) {
+                        uint32_t neg = 0u;
 #pragma unroll
-                for (int t = 0; t < G; ++t) {
-                    const float hv = v[gi * G + t];
-                    const uint32_t code = nearest_code<D>(lut, hv * inv16);
-                    put_code<CB, WPG>(w[gi], t, code);
-                    if constexpr (KIND == kResidual) {
-                        // residual in the H D x domain: rho = h - ||x|| c[code]
-                        const float rho = fmaf(-nrm, slev[code], hv * fq);
-                        r2 = fmaf(rho, rho, r2);
-                        r1 += fabsf(rho);
-                        sw[gi][t / 32] |= (rho >= 0.0f ? 1u : 0u) << (t % 32);
+                        for (int t = 32 * i + 31; t >= 32 * i; --t) {
+                            const float y16 = v[gi * G + t] * inv16;
+                            float l16;
+                            const uint32_t code = nearest_code_lev<D>(lutl, y16, l16);
+                            put_code<CB, WPG>(w[gi], t, code);
+                            const float rho = y16 - l16;
+                            r2 = fmaf(rho, rho, r2);
+                            r1 += fabsf(rho);
+                            neg = (neg << 1) | (__builtin_bit_cast(uint32_t, rho) >> 31);
+                        }
+                        // a zero vector has residual 0 everywhere, whose sign bit is +1
+                        sw[gi][i] = ss > 0.0f ? ~neg : 0xFFFFFFFFu;
                     }
+                } else {
+#pragma unroll
+                    for (int t = 0; t < G; ++t)
+                        put_code<CB, WPG>(w[gi], t, nearest_code<D>(lut, v[gi * G + t] * inv16));
                 }
             }
             float sr = 0.0f;
-            if constexpr (KIND == kResidual) {
+            if constexpr (RES) {
                 r2 = vec_sum<LPV>(r2);
                 r1 = vec_sum<LPV>(r1);
-                // S_r = ||r||^2 / ||r||_1 with r = rho / sqrt(d)
-                sr = r1 > 0.0f ? r2 / (sqrt_d * r1) : 0.0f;
+                // S_r = ||r||^2 / ||r||_1 with r = rho / sqrt(d) = (||x|| / 16) rho16 / sqrt(d)
+                sr = r1 > 0.0f ? (nrm * (1.0f / 16.0f)) * (r2 / (sqrt_d * r1)) : 0.0f;
             }
             if (valid) {
                 uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes) + vec * ROWW;
@@ -521,6 +580,9 @@ __global__ __launch_bounds__(kBlock) void k_dequantize(const DequantArgs a) {
     const float inv_sqrt_d = 1.0f / __builtin_sqrtf((float)D);
     // sign-bit masks of D for the output words (fp16 pairs or single fp32)
     constexpr int NM = F16OUT ? E / 2 : E;
+    constexpr bool STAGE = (G == E) && RunStage<D, F16OUT>::kOk;
+    using RS = RunStage<D, F16OUT>;
+    __shared__ u32x4_t sbuf[STAGE ? kWaves * 64 * RS::RC : 1];
     uint32_t omask[NM];
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
@@ -579,7 +641,37 @@ __global__ __launch_bounds__(kBlock) void k_dequantize(const DequantArgs a) {
         fetch_codes<D, G, BITS, KIND>(a, vec + stride, q, w, sw, sc, rs);
         fwht_regs<E, 0>(v);
         fwht_lanes<LPV>(v, q);
-        if (valid) {
+        if constexpr (STAGE) {
+            // run chunks -> LDS tile -> coalesced global stores
+            u32x4_t *buf = sbuf + wave * 64 * RS::RC;
+#pragma unroll
+            for (int c = 0; c < RS::RC; ++c) {
+                uint32_t o[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    if constexpr (F16OUT) {
+                        const int r = 8 * c + 2 * k;
+                        const _Float16 lo = (_Float16)(v[r] * alpha);
+                        const _Float16 hi = (_Float16)(v[r + 1] * alpha);
+                        o[k] = ((uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16)) ^ omask[r / 2];
+                    } else {
+                        const int r = 4 * c + k;
+                        o[k] = __builtin_bit_cast(uint32_t, v[r] * alpha) ^ omask[r];
+                    }
+                }
+                buf[RS::pos(lane, c)] = u32x4_t{o[0], o[1], o[2], o[3]};
+            }
+            const int64_t row0 = v0 + wave * VPW;
+            char *ybase = static_cast<char *>(a.y);
+#pragma unroll
+            for (int k = 0; k < RS::RC; ++k) {
+                const uint32_t T = 64u * k + lane;
+                const u32x4_t val = buf[RS::pos(T / RS::RC, T % RS::RC)];
+                const int64_t row = row0 + T / RS::CPR;
+                if (row < a.n) reinterpret_cast<u32x4_t *>(ybase + row * D * RS::ESZ)[T % RS::CPR] = val;
+            }
+        } else if (valid) {
             if constexpr (F16OUT) {
                 uint4 *row = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.y) + vec * D);
 #pragma unroll
@@ -682,347 +774,8 @@ __global__ __launch_bounds__(kBlock) void k_score(const ScoreArgs a) {
     }
 }
 
-// ---------------------------------------------------------------------------
-// Hadamard-as-GEMM variant for d = 128 (fp16 data, 4-bit codes).
-//
-// H_128 = H_4 (x) H_32 over the coordinate split e = 32 a + b (Sylvester
-// entries (-1)^popcount(e & e') factor over the two bit groups).  The H_32
-// factor runs on v_mfma_f32_32x32x16_f16 with the 32 vectors of a wave as the
-// N dimension; the H_4 factor is two butterfly stages in registers.  Lane l
-// serves vector j = l % 32 with half h = l / 32; in the K step (a', kk) it
-// supplies coordinates 32 a' + 16 h + 8 kk + t, t = 0..7 (16 bytes of fp16).
-// Output row i of a 32x32 tile is mapped to b = pi(i) so that the lane holds
-// b = 16 h + r in accumulator register r: the lane ends up with 16
-// consecutive coordinates per block a, i.e. whole 64-bit code words.
-// Products of fp16 values and +-1 are exact; accumulation is fp32.
-
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-// b = pi(i) for the accumulator row i = 8 (r / 4) + 4 h + r % 4  ->  16 h + r.
-__device__ __forceinline__ uint32_t acc_row_to_b(uint32_t i) {
-    return 16u * ((i >> 2) & 1u) + 4u * (i >> 3) + (i & 3u);
-}
-
-__device__ __forceinline__ floatx16 mfma16(u32x4_t a, u32x4_t b, floatx16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
-                                                  __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
-}
-
-// Operand A for K step kk: A[i][k] = H_32[pi(i)][16 (k / 8) + 8 kk + k % 8], times
-// the sign s_{32 a' + that coordinate} when `dsign` is given.
-__device__ __forceinline__ u32x4_t hadamard_operand(uint32_t lane, int ap, int kk, const uint32_t *dsign) {
-    const uint32_t pb = acc_row_to_b(lane & 31u), h = lane >> 5;
-    uint32_t w[4];
-#pragma unroll
-    for (int t = 0; t < 8; t += 2) {
-        uint32_t half2 = 0;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const uint32_t b = 16u * h + 8u * kk + t + u;
-            uint32_t neg = __builtin_popcount(pb & b) & 1u;
-            if (dsign) {
-                const uint32_t e = 32u * ap + b;
-                neg ^= (dsign[e >> 5] >> (e & 31)) & 1u;
-            }
-            half2 |= (neg ? 0xBC00u : 0x3C00u) << (16 * u);
-        }
-        w[t / 2] = half2;
-    }
-    return u32x4_t{w[0], w[1], w[2], w[3]};
-}
-
-// Operand A for the decoder's K step m, whose K slots carry the fp16 hi and lo
-// parts of four coordinates: slot t of half h is coordinate 16 h + 4 m +
-// {0,1,0,1,2,3,2,3}[t] (hi parts in t = 0,1,4,5, lo parts in t = 2,3,6,7).
-__device__ __forceinline__ u32x4_t hadamard_operand_hilo(uint32_t lane, int m) {
-    const uint32_t pb = acc_row_to_b(lane & 31u), h = lane >> 5;
-    uint32_t w[4];
-#pragma unroll
-    for (int t = 0; t < 8; t += 2) {
-        uint32_t half2 = 0;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int tt = t + u;
-            const uint32_t b = 16u * h + 4u * m + (uint32_t)((tt & 1) + 2 * (tt >> 2));
-            half2 |= ((__builtin_popcount(pb & b) & 1u) ? 0xBC00u : 0x3C00u) << (16 * u);
-        }
-        w[t / 2] = half2;
-    }
-    return u32x4_t{w[0], w[1], w[2], w[3]};
-}
-
-// H_4 across the four accumulators, in place: c[a] <- sum_a' (-1)^popcount(a & a') c[a'].
-__device__ __forceinline__ void hadamard4(floatx16 (&c)[4]) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const float u0 = c[0][r] + c[1][r], u1 = c[0][r] - c[1][r];
-        const float u2 = c[2][r] + c[3][r], u3 = c[2][r] - c[3][r];
-        c[0][r] = u0 + u2;
-        c[2][r] = u0 - u2;
-        c[1][r] = u1 + u3;
-        c[3][r] = u1 - u3;
-    }
-}
-
-// LDS staging for the d = 128 MFMA kernels.  A wave works on a tile of 32
-// rows.  Global traffic is coalesced: each load/store instruction of a wave
-// moves one contiguous KiB (four 256-byte fp16 rows, or sixteen 64-byte code
-// rows).  Inside LDS, the 16-byte chunk c of tile row r sits at chunk position
-// c ^ (r mod 16) (fp16 rows) or c ^ (r mod 4) (code rows), so the per-lane
-// reads and writes of the MFMA layout (one row per lane) hit distinct banks.
-typedef __attribute__((address_space(3))) void lds_void;
-
-constexpr int kRowsPerWave = 32;
-constexpr int kTileBytes = kRowsPerWave * 256;   // fp16 rows of one wave
-constexpr int kCodeTileBytes = kRowsPerWave * 64;
-
-__device__ __forceinline__ uint32_t x_chunk(uint32_t r, uint32_t c) { return 16u * r + (c ^ (r & 15u)); }
-__device__ __forceinline__ uint32_t c_chunk(uint32_t r, uint32_t c) { return 4u * r + (c ^ (r & 3u)); }
-
-// Direct global -> LDS copy of the 32 fp16 rows starting at row0 (rows past
-// the end repeat the last row).  Instruction k fills LDS chunks 64k .. 64k+63.
-__device__ __forceinline__ void stage_rows(const uint16_t *x, int64_t row0, int64_t n, char *lds_tile,
-                                           uint32_t lane) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const uint32_t r = 4u * k + (lane >> 4), pos = lane & 15u;
-        const int64_t row = row0 + r < n ? row0 + r : n - 1;
-        const uint4 *src = reinterpret_cast<const uint4 *>(x + row * 128) + (pos ^ (r & 15u));
-        __builtin_amdgcn_global_load_lds(src, (lds_void *)(lds_tile + 1024 * k), 16, 0, 0);
-    }
-}
-
-// One tile of the encoder: read the staged rows from `tile`, transform,
-// quantize, write codes and norms.  `next` is the other staging buffer; the
-// following tile's rows are copied into it while this one is processed.
-__device__ __forceinline__ void quantize_tile128(const QuantArgs &a, const uint2 *lut, const u32x4_t (&A)[4][2],
-                                                 const char *tile, char *next, char *ct, int64_t v0,
-                                                 int64_t v0_next, uint32_t lane) {
-    constexpr int D = 128;
-    const uint32_t j = lane & 31u, h = lane >> 5;
-    u32x4_t raw[4][2];
-#pragma unroll
-    for (int ap = 0; ap < 4; ++ap)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-            raw[ap][kk] = *reinterpret_cast<const u32x4_t *>(tile + 16 * x_chunk(j, 4 * ap + 2 * h + kk));
-    stage_rows(static_cast<const uint16_t *>(a.x), v0_next, a.n, next, lane);
-    float ss = 0.0f, ss2 = 0.0f;
-    floatx16 c[4];
-#pragma unroll
-    for (int ap = 0; ap < 4; ++ap) {
-        c[ap] = floatx16{};
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            c[ap] = mfma16(A[ap][kk], raw[ap][kk], c[ap]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (q & 1)
-                    ss2 = dot2(raw[ap][kk][q], raw[ap][kk][q], ss2);
-                else
-                    ss = dot2(raw[ap][kk][q], raw[ap][kk][q], ss);
-            }
-        }
-    }
-    ss += ss2;
-    ss += __shfl_xor(ss, 32);
-    const float nrm = sqrtf(ss);
-    const float inv16 = ss > 0.0f ? 16.0f / nrm : 0.0f;
-    hadamard4(c);
-#pragma unroll
-    for (int ap = 0; ap < 4; ++ap) {
-        uint32_t w0 = 0u, w1 = 0u;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) w0 |= nearest_code<D>(lut, c[ap][r] * inv16) << (4 * r);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) w1 |= nearest_code<D>(lut, c[ap][r + 8] * inv16) << (4 * r);
-        // code bytes 16 ap + 8 h .. +8 of row j: half of 16-byte chunk ap
-        *reinterpret_cast<uint2 *>(ct + 16 * c_chunk(j, ap) + 8 * h) = make_uint2(w0, w1);
-    }
-    const int64_t vec = v0 + j;
-    if (h == 0 && vec < a.n) a.scale[vec] = nrm;
-    // coalesced code stores: instruction k covers tile rows 16k .. 16k+15
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const uint32_t r = 16u * k + (lane >> 2), cc = lane & 3u;
-        const uint4 val = *reinterpret_cast<const uint4 *>(ct + 16 * c_chunk(r, cc));
-        if (v0 + r < a.n) reinterpret_cast<uint4 *>(a.codes + (v0 + r) * 64)[cc] = val;
-    }
-}
-
-__global__ __launch_bounds__(kBlock) void k_quantize_mfma128(const QuantArgs a) {
-    constexpr int D = 128, VPB = kWaves * kRowsPerWave;
-    __shared__ uint2 lut[Lut<D>::kCells];
-    // two staging buffers as separate objects so the compiler can tell the
-    // copy into one from the reads of the other
-    __shared__ __attribute__((aligned(16))) char xbuf0[kWaves][kTileBytes];
-    __shared__ __attribute__((aligned(16))) char xbuf1[kWaves][kTileBytes];
-    __shared__ __attribute__((aligned(16))) char cbuf[kWaves][kCodeTileBytes];
-    build_lut<Lut<D>::kCells, Lut<D>::kOff>(lut, a.thr, 15);
-    __syncthreads();
-
-    const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
-    u32x4_t A[4][2];
-#pragma unroll
-    for (int ap = 0; ap < 4; ++ap)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) A[ap][kk] = hadamard_operand(lane, ap, kk, a.dsign);
-
-    const int64_t stride = (int64_t)gridDim.x * VPB;
-    const int64_t first = (int64_t)blockIdx.x * VPB + wave * kRowsPerWave;
-    const int64_t limit = a.n + wave * kRowsPerWave;  // a block iteration runs while its first row < n
-    stage_rows(static_cast<const uint16_t *>(a.x), first, a.n, xbuf0[wave], lane);
-    for (int64_t v0 = first; v0 < limit; v0 += 2 * stride) {
-        quantize_tile128(a, lut, A, xbuf0[wave], xbuf1[wave], cbuf[wave], v0, v0 + stride, lane);
-        if (v0 + stride >= limit) break;
-        quantize_tile128(a, lut, A, xbuf1[wave], xbuf0[wave], cbuf[wave], v0 + stride, v0 + 2 * stride, lane);
-    }
-}
-
-// Direct global -> LDS copy of the 32 code rows at row0 (2 KiB; rows past the
-// end repeat the last row).
-__device__ __forceinline__ void stage_codes(const uint8_t *codes, int64_t row0, int64_t n, char *tile,
-                                            uint32_t lane) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const uint32_t r = 16u * k + (lane >> 2), pos = lane & 3u;
-        const int64_t row = row0 + r < n ? row0 + r : n - 1;
-        const uint4 *src = reinterpret_cast<const uint4 *>(codes + row * 64) + (pos ^ (r & 3u));
-        __builtin_amdgcn_global_load_lds(src, (lds_void *)(tile + 1024 * k), 16, 0, 0);
-    }
-}
-
-// One tile of the decoder: codes from the staged `tile`, the next tile's codes
-// copied into `next` meanwhile, output transposed through `yt` into coalesced
-// stores.
-__device__ __forceinline__ void dequantize_tile128(const DequantArgs &a, const uint2 *tab, const u32x4_t (&A)[4],
-                                                   const uint32_t (&om)[4][8], const char *tile, char *next,
-                                                   char *yt, int64_t v0, int64_t v0_next, uint32_t lane,
-                                                   float &scale) {
-    constexpr int D = 128;
-    const uint32_t j = lane & 31u, h = lane >> 5;
-    uint2 cw[4];
-#pragma unroll
-    for (int ap = 0; ap < 4; ++ap)  // code bytes 16 ap + 8 h .. +8 of row j
-        cw[ap] = *reinterpret_cast<const uint2 *>(tile + 16 * c_chunk(j, ap) + 8 * h);
-    const float alpha = scale * (1.0f / D);
-    // the next tile's codes (LDS) and scales (registers) load during this one
-    stage_codes(a.codes, v0_next, a.n, next, lane);
-    const int64_t vnext = v0_next + j;
-    scale = a.scale[vnext < a.n ? vnext : a.n - 1];
-    floatx16 c[4];
-#pragma unroll
-    for (int ap = 0; ap < 4; ++ap) {
-        c[ap] = floatx16{};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            // code bytes 2m, 2m+1 of the chunk: coordinates 32 ap + 16 h + 4m .. +3
-            const uint32_t wd = m < 2 ? cw[ap].x : cw[ap].y;
-            const uint2 e0 = tab[(wd >> (16 * (m & 1))) & 0xFFu];
-            const uint2 e1 = tab[(wd >> (16 * (m & 1) + 8)) & 0xFFu];
-            c[ap] = mfma16(A[m], u32x4_t{e0.x, e0.y, e1.x, e1.y}, c[ap]);
-        }
-    }
-    hadamard4(c);
-#pragma unroll
-    for (int ap = 0; ap < 4; ++ap) {
-        uint32_t o[8];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const _Float16 lo = (_Float16)(c[ap][2 * p] * alpha);
-            const _Float16 hi = (_Float16)(c[ap][2 * p + 1] * alpha);
-            o[p] = ((uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                    ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16)) ^ om[ap][p];
-        }
-        // fp16 bytes 64 ap + 32 h .. +32 of row j: chunks 4 ap + 2 h, +1
-        *reinterpret_cast<uint4 *>(yt + 16 * x_chunk(j, 4 * ap + 2 * h)) = make_uint4(o[0], o[1], o[2], o[3]);
-        *reinterpret_cast<uint4 *>(yt + 16 * x_chunk(j, 4 * ap + 2 * h + 1)) = make_uint4(o[4], o[5], o[6], o[7]);
-    }
-    // coalesced stores: instruction k covers tile rows 4k .. 4k+3
-    uint16_t *y = static_cast<uint16_t *>(a.y);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const uint32_t r = 4u * k + (lane >> 4), cc = lane & 15u;
-        const uint4 val = *reinterpret_cast<const uint4 *>(yt + 16 * x_chunk(r, cc));
-        if (v0 + r < a.n) reinterpret_cast<uint4 *>(y + (v0 + r) * D)[cc] = val;
-    }
-}
-
-__global__ __launch_bounds__(kBlock) void k_dequantize_mfma128(const DequantArgs a) {
-    constexpr int VPB = kWaves * kRowsPerWave;
-    // per code byte: (hi parts, lo parts) of its two levels as packed fp16
-    __shared__ uint2 tab[256];
-    __shared__ __attribute__((aligned(16))) char cbuf0[kWaves][kCodeTileBytes];
-    __shared__ __attribute__((aligned(16))) char cbuf1[kWaves][kCodeTileBytes];
-    __shared__ __attribute__((aligned(16))) char ybuf[kWaves][kTileBytes];
-    {
-        const uint32_t v = threadIdx.x;
-        const float c0 = a.lev[v & 15u], c1 = a.lev[v >> 4];
-        const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
-        const _Float16 l0 = (_Float16)(c0 - (float)h0), l1 = (_Float16)(c1 - (float)h1);
-        tab[v] = make_uint2((uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16),
-                            (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16));
-    }
-    __syncthreads();
-
-    const uint32_t lane = lane_id(), h = lane >> 5, wave = threadIdx.x >> 6;
-    u32x4_t A[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) A[m] = hadamard_operand_hilo(lane, m);
-    // D applied to the output: packed fp16 sign masks for coordinates 32 a + 16 h + r
-    uint32_t om[4][8];
-#pragma unroll
-    for (int ap = 0; ap < 4; ++ap)
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const uint32_t e = 32u * ap + 16u * h + 2u * p;
-            om[ap][p] = (((a.dsign[e >> 5] >> (e & 31)) & 1u) << 15) |
-                        (((a.dsign[(e + 1) >> 5] >> ((e + 1) & 31)) & 1u) << 31);
-        }
-
-    const int64_t stride = (int64_t)gridDim.x * VPB;
-    const int64_t first = (int64_t)blockIdx.x * VPB + wave * kRowsPerWave;
-    const int64_t limit = a.n + wave * kRowsPerWave;
-    stage_codes(a.codes, first, a.n, cbuf0[wave], lane);
-    const int64_t vfirst = first + (lane & 31u);
-    float scale = a.scale[vfirst < a.n ? vfirst : a.n - 1];
-    for (int64_t v0 = first; v0 < limit; v0 += 2 * stride) {
-        dequantize_tile128(a, tab, A, om, cbuf0[wave], cbuf1[wave], ybuf[wave], v0, v0 + stride, lane, scale);
-        if (v0 + stride >= limit) break;
-        dequantize_tile128(a, tab, A, om, cbuf1[wave], cbuf0[wave], ybuf[wave], v0 + stride, v0 + 2 * stride,
-                           lane, scale);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Dispatch helpers.  Grids are sized to what is resident at once (CUs x
-// blocks per CU from the occupancy calculator), so every block of the
-// grid-stride loop gets the same share and there is no partial last wave.
 template <int D>
 constexpr int vecs_per_block() { return kWaves * (64 / lanes_per_vec(D)); }
-
-template <typename K>
-int resident_blocks(K kernel) {
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess || per_cu < 1)
-        per_cu = 1;
-    return per_cu;
-}
-
-// Fewer, longer-lived blocks measured faster than a full-occupancy grid: the
-// streaming loads are prefetched one vector ahead in every wave, and HBM
-// write throughput drops with many concurrent writers.
-constexpr int kDefaultBlocksPerCU = 3;
-
-inline int grid_for(int64_t n, int vpb, int per_cu) {
-    const int cap_env = blocks_per_cu_cap();
-    const int cap_cu = cap_env > 0 ? cap_env : kDefaultBlocksPerCU;
-    if (per_cu > cap_cu) per_cu = cap_cu;
-    const int64_t want = (n + vpb - 1) / vpb;
-    const int64_t cap = (int64_t)device_cu_count() * per_cu;
-    return (int)(want < cap ? (want > 0 ? want : 1) : cap);
-}
 
 template <int D, int G, bool F16, int BITS, int KIND>
 hipError_t run_q(const QuantArgs &a, hipStream_t s) {
@@ -1040,24 +793,12 @@ hipError_t run_dq(const DequantArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t run_q_mfma128(const QuantArgs &a, hipStream_t s) {
-    static const int per_cu = resident_blocks(k_quantize_mfma128);
-    hipLaunchKernelGGL(k_quantize_mfma128, dim3(grid_for(a.n, kWaves * kRowsPerWave, per_cu)), dim3(kBlock), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t run_dq_mfma128(const DequantArgs &a, hipStream_t s) {
-    static const int per_cu = resident_blocks(k_dequantize_mfma128);
-    hipLaunchKernelGGL(k_dequantize_mfma128, dim3(grid_for(a.n, kWaves * kRowsPerWave, per_cu)), dim3(kBlock), 0, s, a);
-    return hipGetLastError();
-}
-
 template <int D>
 hipError_t quant_d(bool f16, int bits, Kind kind, int layout, const QuantArgs &a, hipStream_t s) {
     constexpr int E = D / lanes_per_vec(D);
     switch (kind) {
     case kMse:
-        if (D == 128 && f16 && bits == 4 && hadamard_on_mfma()) return run_q_mfma128(a, s);
+        if (D == 128 && f16 && bits == 4 && hadamard_on_mfma()) return launch_quantize_kv128(a, s);
         // chunked layout: one 32-bit code word per lane-group (G = 32 / bits)
         if (layout == 1) {
             switch (bits) {
@@ -1094,7 +835,7 @@ hipError_t dequant_d(bool f16, int bits, Kind kind, int layout, const DequantArg
     constexpr int E = D / lanes_per_vec(D);
     switch (kind) {
     case kMse:
-        if (D == 128 && f16 && bits == 4 && hadamard_on_mfma()) return run_dq_mfma128(a, s);
+        if (D == 128 && f16 && bits == 4 && hadamard_on_mfma()) return launch_dequantize_kv128(a, s);
         if (layout == 1) {
             switch (bits) {
             case 1: return f16 ? run_dq<D, 32, true, 1, kMse>(a, s) : run_dq<D, 32, false, 1, kMse>(a, s);

@@ -1,0 +1,337 @@
+// rht_kv128.hip -- the d = 128, fp16, 4-bit encoder and decoder with the
+// H_32 factor of the transform on MFMA (KV-cache head vectors).
+//
+// Method: web page "Random-rotation quantization" (brain.bigb.es): rotate each
+// vector by Pi = H D / sqrt(d) ("Why rotation works"), quantize every rotated
+// coordinate with the N(0,1) Lloyd-Max codebook ("History", EDEN item), decode
+// with Pi^T ("intro", step 3).
+#include "rht_device.h"
+
+namespace rht {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Hadamard-as-GEMM variant for d = 128 (fp16 data, 4-bit codes).
+//
+// H_128 = H_4 (x) H_32 over the coordinate split e = 32 a + b (Sylvester
+// entries (-1)^popcount(e & e') factor over the two bit groups).  The H_32
+// factor runs on v_mfma_f32_32x32x16_f16 with the 32 vectors of a wave as the
+// N dimension; the H_4 factor is two butterfly stages in registers.  Lane l
+// serves vector j = l % 32 with half h = l / 32; in the K step (a', kk) it
+// supplies coordinates 32 a' + 16 h + 8 kk + t, t = 0..7 (16 bytes of fp16).
+// Output row i of a 32x32 tile is mapped to b = pi(i) so that the lane holds
+// b = 16 h + r in accumulator register r: the lane ends up with 16
+// consecutive coordinates per block a, i.e. whole 64-bit code words.
+// Products of fp16 values and +-1 are exact; accumulation is fp32.
+
+// b = pi(i) for the accumulator row i = 8 (r / 4) + 4 h + r % 4  ->  16 h + r.
+__device__ __forceinline__ uint32_t acc_row_to_b(uint32_t i) {
+    return 16u * ((i >> 2) & 1u) + 4u * (i >> 3) + (i & 3u);
+}
+
+__device__ __forceinline__ floatx16 mfma16(u32x4_t a, u32x4_t b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
+                                                  __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+}
+
+// Operand A for K step kk: A[i][k] = H_32[pi(i)][16 (k / 8) + 8 kk + k % 8], times
+// the sign s_{32 a' + that coordinate} when `dsign` is given.
+__device__ __forceinline__ u32x4_t hadamard_operand(uint32_t lane, int ap, int kk, const uint32_t *dsign) {
+    const uint32_t pb = acc_row_to_b(lane & 31u), h = lane >> 5;
+    uint32_t w[4];
+#pragma unroll
+    for (int t = 0; t < 8; t += 2) {
+        uint32_t half2 = 0;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const uint32_t b = 16u * h + 8u * kk + t + u;
+            uint32_t neg = __builtin_popcount(pb & b) & 1u;
+            if (dsign) {
+                const uint32_t e = 32u * ap + b;
+                neg ^= (dsign[e >> 5] >> (e & 31)) & 1u;
+            }
+            half2 |= (neg ? 0xBC00u : 0x3C00u) << (16 * u);
+        }
+        w[t / 2] = half2;
+    }
+    return u32x4_t{w[0], w[1], w[2], w[3]};
+}
+
+// Operand A for the decoder's K step m, whose K slots carry the fp16 hi and lo
+// parts of four coordinates: slot t of half h is coordinate 16 h + 4 m +
+// {0,1,0,1,2,3,2,3}[t] (hi parts in t = 0,1,4,5, lo parts in t = 2,3,6,7).
+__device__ __forceinline__ u32x4_t hadamard_operand_hilo(uint32_t lane, int m) {
+    const uint32_t pb = acc_row_to_b(lane & 31u), h = lane >> 5;
+    uint32_t w[4];
+#pragma unroll
+    for (int t = 0; t < 8; t += 2) {
+        uint32_t half2 = 0;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int tt = t + u;
+            const uint32_t b = 16u * h + 4u * m + (uint32_t)((tt & 1) + 2 * (tt >> 2));
+            half2 |= ((__builtin_popcount(pb & b) & 1u) ? 0xBC00u : 0x3C00u) << (16 * u);
+        }
+        w[t / 2] = half2;
+    }
+    return u32x4_t{w[0], w[1], w[2], w[3]};
+}
+
+// H_4 across the four accumulators, in place: c[a] <- sum_a' (-1)^popcount(a & a') c[a'].
+__device__ __forceinline__ void hadamard4(floatx16 (&c)[4]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const float u0 = c[0][r] + c[1][r], u1 = c[0][r] - c[1][r];
+        const float u2 = c[2][r] + c[3][r], u3 = c[2][r] - c[3][r];
+        c[0][r] = u0 + u2;
+        c[2][r] = u0 - u2;
+        c[1][r] = u1 + u3;
+        c[3][r] = u1 - u3;
+    }
+}
+
+// LDS staging for the d = 128 MFMA kernels.  A wave works on a tile of 32
+// rows.  Global traffic is coalesced: each load/store instruction of a wave
+// moves one contiguous KiB (four 256-byte fp16 rows, or sixteen 64-byte code
+// rows).  Inside LDS, the 16-byte chunk c of tile row r sits at chunk position
+// c ^ (r mod 16) (fp16 rows) or c ^ (r mod 4) (code rows), so the per-lane
+// reads and writes of the MFMA layout (one row per lane) hit distinct banks.
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kRowsPerWave = 32;
+constexpr int kTileBytes = kRowsPerWave * 256;   // fp16 rows of one wave
+constexpr int kCodeTileBytes = kRowsPerWave * 64;
+
+__device__ __forceinline__ uint32_t x_chunk(uint32_t r, uint32_t c) { return 16u * r + (c ^ (r & 15u)); }
+__device__ __forceinline__ uint32_t c_chunk(uint32_t r, uint32_t c) { return 4u * r + (c ^ (r & 3u)); }
+
+// Direct global -> LDS copy of the 32 fp16 rows starting at row0 (rows past
+// the end repeat the last row).  Instruction k fills LDS chunks 64k .. 64k+63.
+__device__ __forceinline__ void stage_rows(const uint16_t *x, int64_t row0, int64_t n, char *lds_tile,
+                                           uint32_t lane) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t r = 4u * k + (lane >> 4), pos = lane & 15u;
+        const int64_t row = row0 + r < n ? row0 + r : n - 1;
+        const uint4 *src = reinterpret_cast<const uint4 *>(x + row * 128) + (pos ^ (r & 15u));
+        __builtin_amdgcn_global_load_lds(src, (lds_void *)(lds_tile + 1024 * k), 16, 0, 0);
+    }
+}
+
+// One tile of the encoder: read the staged rows from `tile`, transform,
+// quantize, write codes and norms.  `next` is the other staging buffer; the
+// following tile's rows are copied into it while this one is processed.
+__device__ __forceinline__ void quantize_tile128(const QuantArgs &a, const uint2 *lut, const u32x4_t (&A)[4][2],
+                                                 const char *tile, char *next, char *ct, int64_t v0,
+                                                 int64_t v0_next, uint32_t lane) {
+    constexpr int D = 128;
+    const uint32_t j = lane & 31u, h = lane >> 5;
+    u32x4_t raw[4][2];
+#pragma unroll
+    for (int ap = 0; ap < 4; ++ap)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            raw[ap][kk] = *reinterpret_cast<const u32x4_t *>(tile + 16 * x_chunk(j, 4 * ap + 2 * h + kk));
+    stage_rows(static_cast<const uint16_t *>(a.x), v0_next, a.n, next, lane);
+    float ss = 0.0f, ss2 = 0.0f;
+    floatx16 c[4];
+#pragma unroll
+    for (int ap = 0; ap < 4; ++ap) {
+        c[ap] = floatx16{};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            c[ap] = mfma16(A[ap][kk], raw[ap][kk], c[ap]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (q & 1)
+                    ss2 = dot2(raw[ap][kk][q], raw[ap][kk][q], ss2);
+                else
+                    ss = dot2(raw[ap][kk][q], raw[ap][kk][q], ss);
+            }
+        }
+    }
+    ss += ss2;
+    ss += __shfl_xor(ss, 32);
+    const float nrm = sqrtf(ss);
+    const float inv16 = ss > 0.0f ? 16.0f / nrm : 0.0f;
+    hadamard4(c);
+#pragma unroll
+    for (int ap = 0; ap < 4; ++ap) {
+        uint32_t w0 = 0u, w1 = 0u;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) w0 |= nearest_code<D>(lut, c[ap][r] * inv16) << (4 * r);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) w1 |= nearest_code<D>(lut, c[ap][r + 8] * inv16) << (4 * r);
+        // code bytes 16 ap + 8 h .. +8 of row j: half of 16-byte chunk ap
+        *reinterpret_cast<uint2 *>(ct + 16 * c_chunk(j, ap) + 8 * h) = make_uint2(w0, w1);
+    }
+    const int64_t vec = v0 + j;
+    if (h == 0 && vec < a.n) a.scale[vec] = nrm;
+    // coalesced code stores: instruction k covers tile rows 16k .. 16k+15
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t r = 16u * k + (lane >> 2), cc = lane & 3u;
+        const uint4 val = *reinterpret_cast<const uint4 *>(ct + 16 * c_chunk(r, cc));
+        if (v0 + r < a.n) reinterpret_cast<uint4 *>(a.codes + (v0 + r) * 64)[cc] = val;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_quantize_mfma128(const QuantArgs a) {
+    constexpr int D = 128, VPB = kWaves * kRowsPerWave;
+    __shared__ uint2 lut[Lut<D>::kCells];
+    // two staging buffers as separate objects so the compiler can tell the
+    // copy into one from the reads of the other
+    __shared__ __attribute__((aligned(16))) char xbuf0[kWaves][kTileBytes];
+    __shared__ __attribute__((aligned(16))) char xbuf1[kWaves][kTileBytes];
+    __shared__ __attribute__((aligned(16))) char cbuf[kWaves][kCodeTileBytes];
+    build_lut<Lut<D>::kCells, Lut<D>::kOff>(lut, a.thr, 15);
+    __syncthreads();
+
+    const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+    u32x4_t A[4][2];
+#pragma unroll
+    for (int ap = 0; ap < 4; ++ap)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) A[ap][kk] = hadamard_operand(lane, ap, kk, a.dsign);
+
+    const int64_t stride = (int64_t)gridDim.x * VPB;
+    const int64_t first = (int64_t)blockIdx.x * VPB + wave * kRowsPerWave;
+    const int64_t limit = a.n + wave * kRowsPerWave;  // a block iteration runs while its first row < n
+    stage_rows(static_cast<const uint16_t *>(a.x), first, a.n, xbuf0[wave], lane);
+    for (int64_t v0 = first; v0 < limit; v0 += 2 * stride) {
+        quantize_tile128(a, lut, A, xbuf0[wave], xbuf1[wave], cbuf[wave], v0, v0 + stride, lane);
+        if (v0 + stride >= limit) break;
+        quantize_tile128(a, lut, A, xbuf1[wave], xbuf0[wave], cbuf[wave], v0 + stride, v0 + 2 * stride, lane);
+    }
+}
+
+// Direct global -> LDS copy of the 32 code rows at row0 (2 KiB; rows past the
+// end repeat the last row).
+__device__ __forceinline__ void stage_codes(const uint8_t *codes, int64_t row0, int64_t n, char *tile,
+                                            uint32_t lane) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t r = 16u * k + (lane >> 2), pos = lane & 3u;
+        const int64_t row = row0 + r < n ? row0 + r : n - 1;
+        const uint4 *src = reinterpret_cast<const uint4 *>(codes + row * 64) + (pos ^ (r & 3u));
+        __builtin_amdgcn_global_load_lds(src, (lds_void *)(tile + 1024 * k), 16, 0, 0);
+    }
+}
+
+// One tile of the decoder: codes from the staged `tile`, the next tile's codes
+// copied into `next` meanwhile, output transposed through `yt` into coalesced
+// stores.
+__device__ __forceinline__ void dequantize_tile128(const DequantArgs &a, const uint2 *tab, const u32x4_t (&A)[4],
+                                                   const uint32_t (&om)[4][8], const char *tile, char *next,
+                                                   char *yt, int64_t v0, int64_t v0_next, uint32_t lane,
+                                                   float &scale) {
+    constexpr int D = 128;
+    const uint32_t j = lane & 31u, h = lane >> 5;
+    uint2 cw[4];
+#pragma unroll
+    for (int ap = 0; ap < 4; ++ap)  // code bytes 16 ap + 8 h .. +8 of row j
+        cw[ap] = *reinterpret_cast<const uint2 *>(tile + 16 * c_chunk(j, ap) + 8 * h);
+    const float alpha = scale * (1.0f / D);
+    // the next tile's codes (LDS) and scales (registers) load during this one
+    stage_codes(a.codes, v0_next, a.n, next, lane);
+    const int64_t vnext = v0_next + j;
+    scale = a.scale[vnext < a.n ? vnext : a.n - 1];
+    floatx16 c[4];
+#pragma unroll
+    for (int ap = 0; ap < 4; ++ap) {
+        c[ap] = floatx16{};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            // code bytes 2m, 2m+1 of the chunk: coordinates 32 ap + 16 h + 4m .. +3
+            const uint32_t wd = m < 2 ? cw[ap].x : cw[ap].y;
+            const uint2 e0 = tab[(wd >> (16 * (m & 1))) & 0xFFu];
+            const uint2 e1 = tab[(wd >> (16 * (m & 1) + 8)) & 0xFFu];
+            c[ap] = mfma16(A[m], u32x4_t{e0.x, e0.y, e1.x, e1.y}, c[ap]);
+        }
+    }
+    hadamard4(c);
+#pragma unroll
+    for (int ap = 0; ap < 4; ++ap) {
+        uint32_t o[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const _Float16 lo = (_Float16)(c[ap][2 * p] * alpha);
+            const _Float16 hi = (_Float16)(c[ap][2 * p + 1] * alpha);
+            o[p] = ((uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16)) ^ om[ap][p];
+        }
+        // fp16 bytes 64 ap + 32 h .. +32 of row j: chunks 4 ap + 2 h, +1
+        *reinterpret_cast<uint4 *>(yt + 16 * x_chunk(j, 4 * ap + 2 * h)) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4 *>(yt + 16 * x_chunk(j, 4 * ap + 2 * h + 1)) = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+    // coalesced stores: instruction k covers tile rows 4k .. 4k+3
+    uint16_t *y = static_cast<uint16_t *>(a.y);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t r = 4u * k + (lane >> 4), cc = lane & 15u;
+        const uint4 val = *reinterpret_cast<const uint4 *>(yt + 16 * x_chunk(r, cc));
+        if (v0 + r < a.n) reinterpret_cast<uint4 *>(y + (v0 + r) * D)[cc] = val;
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_dequantize_mfma128(const DequantArgs a) {
+    constexpr int VPB = kWaves * kRowsPerWave;
+    // per code byte: (hi parts, lo parts) of its two levels as packed fp16
+    __shared__ uint2 tab[256];
+    __shared__ __attribute__((aligned(16))) char cbuf0[kWaves][kCodeTileBytes];
+    __shared__ __attribute__((aligned(16))) char cbuf1[kWaves][kCodeTileBytes];
+    __shared__ __attribute__((aligned(16))) char ybuf[kWaves][kTileBytes];
+    {
+        const uint32_t v = threadIdx.x;
+        const float c0 = a.lev[v & 15u], c1 = a.lev[v >> 4];
+        const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
+        const _Float16 l0 = (_Float16)(c0 - (float)h0), l1 = (_Float16)(c1 - (float)h1);
+        tab[v] = make_uint2((uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16),
+                            (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16));
+    }
+    __syncthreads();
+
+    const uint32_t lane = lane_id(), h = lane >> 5, wave = threadIdx.x >> 6;
+    u32x4_t A[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) A[m] = hadamard_operand_hilo(lane, m);
+    // D applied to the output: packed fp16 sign masks for coordinates 32 a + 16 h + r
+    uint32_t om[4][8];
+#pragma unroll
+    for (int ap = 0; ap < 4; ++ap)
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const uint32_t e = 32u * ap + 16u * h + 2u * p;
+            om[ap][p] = (((a.dsign[e >> 5] >> (e & 31)) & 1u) << 15) |
+                        (((a.dsign[(e + 1) >> 5] >> ((e + 1) & 31)) & 1u) << 31);
+        }
+
+    const int64_t stride = (int64_t)gridDim.x * VPB;
+    const int64_t first = (int64_t)blockIdx.x * VPB + wave * kRowsPerWave;
+    const int64_t limit = a.n + wave * kRowsPerWave;
+    stage_codes(a.codes, first, a.n, cbuf0[wave], lane);
+    const int64_t vfirst = first + (lane & 31u);
+    float scale = a.scale[vfirst < a.n ? vfirst : a.n - 1];
+    for (int64_t v0 = first; v0 < limit; v0 += 2 * stride) {
+        dequantize_tile128(a, tab, A, om, cbuf0[wave], cbuf1[wave], ybuf[wave], v0, v0 + stride, lane, scale);
+        if (v0 + stride >= limit) break;
+        dequantize_tile128(a, tab, A, om, cbuf1[wave], cbuf0[wave], ybuf[wave], v0 + stride, v0 + 2 * stride,
+                           lane, scale);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_kv128(const QuantArgs &a, hipStream_t s) {
+    static const int per_cu = resident_blocks(k_quantize_mfma128);
+    hipLaunchKernelGGL(k_quantize_mfma128, dim3(grid_for(a.n, kWaves * kRowsPerWave, per_cu)), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize_kv128(const DequantArgs &a, hipStream_t s) {
+    static const int per_cu = resident_blocks(k_dequantize_mfma128);
+    hipLaunchKernelGGL(k_dequantize_mfma128, dim3(grid_for(a.n, kWaves * kRowsPerWave, per_cu)), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace rht
