@@ -35,6 +35,11 @@
  *   [TQ-FWHT]        page "TurboQuant and per-layer outlier-aware K",
  *                    section "TurboQuant 2026": the rotation is the fast
  *                    Walsh-Hadamard transform.
+ *   [ATTN-ROT]       page "Attn-rot: TurboQuant lite in llama.cpp", opening
+ *                    section: the keys and values of the attention KV cache
+ *                    are rotated and quantized, attention then runs on them.
+ *   [RRQ practice]   "Practical use in llama.cpp": TurboQuant codebooks as
+ *                    KV-cache types for K and V.
  *
  * Readings taken where the pages are silent (each is one plain choice):
  *   - Pi = H D / sqrt(d): D = diag of seeded +-1 signs, H the Sylvester-ordered
@@ -49,6 +54,9 @@
  *   - residual scale: DRIVE's unbiased scale applied to the rotated-domain
  *     residual r, S_r = ||r||_2^2 / ||r||_1 (0 when ||r||_1 = 0).
  *   - outputs rounded to fp32 or fp16 with round-to-nearest-even.
+ *   - attention: out_i = sum_j softmax_j(scale * <q_i, k~_j>) v~_j over the
+ *     decoded keys k~ and values v~ (scale supplied by the caller, no mask);
+ *     keys and values may use different rotation seeds.
  */
 #include <math.h>
 #include <stdint.h>
@@ -553,5 +561,131 @@ int rho_score_dense(const float *q, int m, const uint8_t *codes, const float *no
     }
     free(z);
     free(s);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention over coded keys and values [ATTN-ROT], [RRQ practice],
+ * [RRQ decoders] (MSE decoder for the KV cache).  The plain definition:
+ * decode every key and value in fp64 (x~ = D H c ||x|| / d, no rounding),
+ * logits s_j = scale <q, k~_j>, p = softmax(s), out = sum_j p_j v~_j.
+ * q [heads][m][d] fp32, codes [heads][n][bits d / 8], norms [heads][n],
+ * out [heads][m][d] fp64.  n >= 1.                                          */
+static void decode_row_f64(const uint8_t *crow, double norm, int d, int bits, const double *lv,
+                           const int8_t *s, double *out)
+{
+    int i;
+    for (i = 0; i < d; ++i) out[i] = lv[get_field(crow, i, bits)] * (norm / d);
+    rho_fwht(out, d);
+    for (i = 0; i < d; ++i) out[i] *= s[i];
+}
+
+int rho_attention(const float *q, int m, const uint8_t *kc, const float *kn, const uint8_t *vc,
+                  const float *vn, int64_t heads, int64_t n, int d, int bits, uint64_t seed_k,
+                  uint64_t seed_v, double scale, double *out)
+{
+    double lv[16], th[15];
+    int8_t *sk, *sv;
+    double *kd, *vd, *logit;
+    int64_t b, j;
+    int i, t, row_bytes;
+    if (!valid_dim(d) || bits < 1 || bits > 4 || n < 1 || m < 0 || heads < 0) return -1;
+    if ((int64_t)bits * d % 8) return -1;
+    row_bytes = bits * d / 8;
+    rho_lloyd_max(bits, lv, th, NULL, NULL);
+    sk = (int8_t *)malloc((size_t)d);
+    sv = (int8_t *)malloc((size_t)d);
+    kd = (double *)malloc(sizeof(double) * (size_t)(n * d));
+    vd = (double *)malloc(sizeof(double) * (size_t)(n * d));
+    logit = (double *)malloc(sizeof(double) * (size_t)n);
+    rho_signs(seed_k, d, sk);
+    rho_signs(seed_v, d, sv);
+    for (b = 0; b < heads; ++b) {
+        for (j = 0; j < n; ++j) {
+            decode_row_f64(kc + (b * n + j) * row_bytes, kn[b * n + j], d, bits, lv, sk, kd + j * d);
+            decode_row_f64(vc + (b * n + j) * row_bytes, vn[b * n + j], d, bits, lv, sv, vd + j * d);
+        }
+        for (i = 0; i < m; ++i) {
+            const float *qi = q + (b * m + i) * d;
+            double *oi = out + (b * m + i) * d;
+            double mx = -INFINITY, sum = 0.0;
+            for (j = 0; j < n; ++j) {
+                double acc = 0.0;
+                for (t = 0; t < d; ++t) acc += (double)qi[t] * kd[j * d + t];
+                logit[j] = scale * acc;
+                if (logit[j] > mx) mx = logit[j];
+            }
+            for (t = 0; t < d; ++t) oi[t] = 0.0;
+            for (j = 0; j < n; ++j) {
+                double p = exp(logit[j] - mx);
+                sum += p;
+                for (t = 0; t < d; ++t) oi[t] += p * vd[j * d + t];
+            }
+            for (t = 0; t < d; ++t) oi[t] /= sum;
+        }
+    }
+    free(logit);
+    free(vd);
+    free(kd);
+    free(sv);
+    free(sk);
+    return 0;
+}
+
+/* The same attention computed in the rotated domains, as the decoders allow
+ * [RRQ decoders]: the logits come from the codes, s_j = scale (||k_j|| / d)
+ * <H D_k q, c[code_kj]>; the value sum stays rotated, z = sum_j p_j
+ * (||v_j|| / d) c[code_vj], and one inverse transform per query gives
+ * out = D_v H z (Pi_v^T is linear, so it moves out of the sum).             */
+int rho_attention_rotated(const float *q, int m, const uint8_t *kc, const float *kn,
+                          const uint8_t *vc, const float *vn, int64_t heads, int64_t n, int d,
+                          int bits, uint64_t seed_k, uint64_t seed_v, double scale, double *out)
+{
+    double lv[16], th[15];
+    int8_t *sk, *sv;
+    double *qt, *logit;
+    int64_t b, j;
+    int i, t, row_bytes;
+    if (!valid_dim(d) || bits < 1 || bits > 4 || n < 1 || m < 0 || heads < 0) return -1;
+    if ((int64_t)bits * d % 8) return -1;
+    row_bytes = bits * d / 8;
+    rho_lloyd_max(bits, lv, th, NULL, NULL);
+    sk = (int8_t *)malloc((size_t)d);
+    sv = (int8_t *)malloc((size_t)d);
+    qt = (double *)malloc(sizeof(double) * (size_t)d);
+    logit = (double *)malloc(sizeof(double) * (size_t)n);
+    rho_signs(seed_k, d, sk);
+    rho_signs(seed_v, d, sv);
+    for (b = 0; b < heads; ++b) {
+        for (i = 0; i < m; ++i) {
+            const float *qi = q + (b * m + i) * d;
+            double *z = out + (b * m + i) * d;
+            double mx = -INFINITY, sum = 0.0;
+            for (t = 0; t < d; ++t) qt[t] = sk[t] * (double)qi[t];
+            rho_fwht(qt, d);
+            for (j = 0; j < n; ++j) {
+                const uint8_t *crow = kc + (b * n + j) * row_bytes;
+                double acc = 0.0;
+                for (t = 0; t < d; ++t) acc += qt[t] * lv[get_field(crow, t, bits)];
+                logit[j] = scale * ((double)kn[b * n + j] / d) * acc;
+                if (logit[j] > mx) mx = logit[j];
+            }
+            for (t = 0; t < d; ++t) z[t] = 0.0;
+            for (j = 0; j < n; ++j) {
+                const uint8_t *crow = vc + (b * n + j) * row_bytes;
+                double p = exp(logit[j] - mx), w;
+                sum += p;
+                w = p * ((double)vn[b * n + j] / d);
+                for (t = 0; t < d; ++t) z[t] += w * lv[get_field(crow, t, bits)];
+            }
+            for (t = 0; t < d; ++t) z[t] /= sum;
+            rho_fwht(z, d);
+            for (t = 0; t < d; ++t) z[t] *= sv[t];
+        }
+    }
+    free(logit);
+    free(qt);
+    free(sv);
+    free(sk);
     return 0;
 }
