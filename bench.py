@@ -17,6 +17,7 @@ encoder and the same 324 B for the decoder.  `cpu_baseline` times the oracle
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -208,6 +209,37 @@ def other_workloads(torch, rht, dev, stream):
     return out
 
 
+def attention_workload(torch, rht, dev, stream, ck, nk, cv, nv, n_vec, d):
+    """Decode attention over the KV block just encoded: 32 layers x 8 KV heads
+    = 256 heads of 32768 tokens, 4 queries per KV head (grouped-query), scale
+    1/sqrt(d), logits and value sums in the rotated domains (rht_attention)."""
+    heads, m = 256, 4
+    n = n_vec // heads
+    g = torch.Generator(device=dev)
+    g.manual_seed(1010)
+    q = torch.randn((heads, m, d), generator=g, device=dev, dtype=torch.float32)
+    out = torch.empty((heads, m, d), dtype=torch.float32, device=dev)
+    need = rht.rht_attention_workspace_bytes(heads, m, n, d)
+    ws = torch.empty((need,), dtype=torch.uint8, device=dev)
+    sh = stream.cuda_stream
+    scale = 1.0 / math.sqrt(d)
+    times = time_launches(torch, stream, lambda i: rht.rht_attention(
+        q.data_ptr(), m, ck.data_ptr(), nk.data_ptr(), cv.data_ptr(), nv.data_ptr(), heads, n, d, 4,
+        42, 43, scale, out.data_ptr(), ws.data_ptr(), need, sh), 1)
+    st = stats(times)
+    ms = st["ms_median"]
+    # codes and norms of K and V, the queries and the outputs
+    alg = 2 * n_vec * (d // 2 + 4) + 2 * heads * m * d * 4
+    gbs = alg / (ms / 1e3) / 1e9
+    flops = 2.0 * 2 * heads * m * n * d  # logits and value sums, counted once
+    return dict(st, **{"workload": "decode attention over the KV block: 256 heads x 32768 tokens, "
+                                   "4-bit K and V, 4 queries per head, d=128",
+                       "algorithmic_bytes": alg, "GB_per_s": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS,
+                       "bound": "hbm", "tokens_per_s": heads * n / (ms / 1e3),
+                       "algorithmic_TFLOP_per_s": flops / (ms / 1e3) / 1e12,
+                       "workspace_bytes": need})
+
+
 def cpu_baseline(rows):
     import oracle
     import testdata
@@ -370,10 +402,13 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_other_workloads:
+        print("timing attention over the KV block", file=sys.stderr, flush=True)
+        attn = attention_workload(torch, rht, dev, stream, ck, nk, cv, nv, n, d)
         del xk, xv, ck, cv, nk, nv, yk, yv
         torch.cuda.empty_cache()
         print("timing the DRIVE, residual and scoring workloads", file=sys.stderr, flush=True)
         out["other_workloads"] = other_workloads(torch, rht, dev, stream)
+        out["other_workloads"]["attention"] = attn
     if not args.no_cpu_baseline:
         print("timing the CPU oracle on %d vectors" % args.cpu_rows, file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args.cpu_rows)

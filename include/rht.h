@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define RHT_ABI_VERSION 1
+#define RHT_ABI_VERSION 2
 
 typedef enum {
     RHT_OK = 0,
@@ -53,7 +53,8 @@ typedef enum {
     RHT_E_MODE = 5,    /* unknown mode, or a mode that does not allow these bits */
     RHT_E_ALIGN = 6,   /* a device pointer is not 16-byte aligned */
     RHT_E_COUNT = 7,   /* n < 0, or m outside [0, 64] */
-    RHT_E_DEVICE = 8   /* the HIP runtime reported an error (bad stream/pointer, launch) */
+    RHT_E_DEVICE = 8,  /* the HIP runtime reported an error (bad stream/pointer, launch) */
+    RHT_E_WORKSPACE = 9 /* workspace smaller than the call needs */
 } rht_status;
 
 typedef enum { RHT_F32 = 0, RHT_F16 = 1 } rht_dtype;
@@ -121,6 +122,35 @@ rht_status rht_residual_dequantize(const uint8_t *codes, const uint8_t *signs, c
  *   logits [m][n] fp32 written.  d in {64, 128, 256}; bits 1..4. */
 rht_status rht_score(const float *q, int32_t m, const uint8_t *codes, const float *norms, int64_t n,
                      int32_t d, int32_t bits, uint64_t seed, float *logits, void *stream);
+
+/* Attention over MSE-coded keys and values, computed in the rotated domains
+ * (page "Attn-rot: TurboQuant lite in llama.cpp", opening section: the keys
+ * and values of the KV cache are rotated and quantized; "Three decoders, one
+ * rotation": logits come from <Pi q, code>, and since Pi^T is linear the
+ * weighted sum of decoded values is one inverse rotation of the weighted sum
+ * of their codes).  For every head h and query i:
+ *   out[h][i] = sum_j softmax_j(scale * <q[h][i], k~[h][j]>) v~[h][j]
+ * where k~, v~ are the vectors rht_dequantize would decode (keys with seed_k,
+ * values with seed_v).  No mask; scale is applied as given (e.g. 1/sqrt(d)).
+ *   q          [heads][m][d] fp32, 1 <= m <= 16.
+ *   k_codes, v_codes [heads][n][bits*d/8] and k_norms, v_norms [heads][n]
+ *              fp32, as written by rht_quantize(..., RHT_SCALE_NORM, seed, ...).
+ *   out        [heads][m][d] fp32, written.
+ *   workspace  device scratch of at least rht_attention_workspace_bytes(heads,
+ *              m, n, d) bytes, owned by the caller; its contents on entry are
+ *              ignored and on return unspecified.  Calls that may run at the
+ *              same time must not share it.
+ *   d = 128 and bits = 4 only.  n >= 1 when heads > 0; heads = 0 is a no-op.
+ * Returns RHT_E_WORKSPACE (after the other checks) when workspace_bytes is
+ * too small. */
+rht_status rht_attention(const float *q, int32_t m, const uint8_t *k_codes, const float *k_norms,
+                         const uint8_t *v_codes, const float *v_norms, int64_t heads, int64_t n,
+                         int32_t d, int32_t bits, uint64_t seed_k, uint64_t seed_v, float scale,
+                         float *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Device workspace bytes rht_attention needs for these sizes; 0 when
+ * rht_attention would reject them or has nothing to do.  Host-only. */
+size_t rht_attention_workspace_bytes(int64_t heads, int32_t m, int64_t n, int32_t d);
 
 /* ---- host-side helpers: HOST pointers, synchronous, no GPU needed ---- */
 

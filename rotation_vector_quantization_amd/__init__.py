@@ -35,7 +35,7 @@ _LIB_PATH = os.path.join(_HERE, "librht.so")
 
 F32, F16 = 0, 1
 SCALE_NORM, SCALE_SIGN_BIASED, SCALE_SIGN_UNBIASED = 0, 1, 2
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _lib = None
 
@@ -65,13 +65,17 @@ def load():
     L.rht_residual_quantize.argtypes = [vp, i32, i64, i32, i32, u64, vp, vp, vp, vp, vp]
     L.rht_residual_dequantize.argtypes = [vp, vp, vp, vp, i64, i32, i32, u64, vp, i32, vp]
     L.rht_score.argtypes = [vp, i32, vp, vp, i64, i32, i32, u64, vp, vp]
+    L.rht_attention.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i32, i32, u64, u64, ctypes.c_float,
+                                vp, vp, ctypes.c_size_t, vp]
+    L.rht_attention_workspace_bytes.argtypes = [i64, i32, i64, i32]
+    L.rht_attention_workspace_bytes.restype = ctypes.c_size_t
     L.rht_codebook.argtypes = [i32, vp, vp]
     L.rht_signs.argtypes = [u64, i32, vp]
     L.rht_status_str.argtypes = [i32]
     L.rht_status_str.restype = ctypes.c_char_p
     L.rht_abi_version.restype = i32
     for f in ("rht_quantize", "rht_dequantize", "rht_residual_quantize", "rht_residual_dequantize",
-              "rht_score", "rht_codebook", "rht_signs"):
+              "rht_score", "rht_attention", "rht_codebook", "rht_signs"):
         getattr(L, f).restype = i32
     if L.rht_abi_version() != ABI_VERSION:
         raise ImportError("librht ABI %d, binding expects %d" % (L.rht_abi_version(), ABI_VERSION))
@@ -106,6 +110,16 @@ def rht_residual_dequantize(codes, signs, norms, res_scale, n, d, bits, seed, y,
 
 def rht_score(q, m, codes, norms, n, d, bits, seed, logits, stream=0):
     _ok(load().rht_score(q, m, codes, norms, n, d, bits, seed, logits, stream), "rht_score")
+
+
+def rht_attention(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, bits, seed_k, seed_v, scale,
+                  out, workspace, workspace_bytes, stream=0):
+    _ok(load().rht_attention(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, bits, seed_k, seed_v,
+                             scale, out, workspace, workspace_bytes, stream), "rht_attention")
+
+
+def rht_attention_workspace_bytes(heads, m, n, d) -> int:
+    return int(load().rht_attention_workspace_bytes(heads, m, n, d))
 
 
 def rht_codebook(bits: int):
@@ -222,3 +236,21 @@ def score(q, codes, norms, d: int, bits: int, seed: int):
     rht_score(q.data_ptr(), m, codes.data_ptr(), norms.data_ptr(), n, d, bits, seed,
               logits.data_ptr(), _stream(q.device))
     return logits
+
+
+def attention(q, k_codes, k_norms, v_codes, v_norms, bits: int, seed_k: int, seed_v: int, scale: float,
+              workspace=None):
+    """q [heads][m][d] fp32 over coded keys/values [heads][n][...] -> out fp32 [heads][m][d].
+    A workspace tensor of at least rht_attention_workspace_bytes bytes may be passed in."""
+    torch = _torch()
+    _check_gpu(q, k_codes, k_norms, v_codes, v_norms)
+    heads, m, d = q.shape
+    n = k_norms.shape[1]
+    out = torch.empty((heads, m, d), dtype=torch.float32, device=q.device)
+    need = rht_attention_workspace_bytes(heads, m, n, d)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    rht_attention(q.data_ptr(), m, k_codes.data_ptr(), k_norms.data_ptr(), v_codes.data_ptr(),
+                  v_norms.data_ptr(), heads, n, d, bits, seed_k, seed_v, scale, out.data_ptr(),
+                  workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q.device))
+    return out

@@ -113,6 +113,20 @@ int layout_choice() {
 
 rht_status launched(hipError_t e) { return e == hipSuccess ? RHT_OK : RHT_E_DEVICE; }
 
+// Key chunks per head for attention: enough (head, chunk) wavefronts to keep
+// every SIMD busy (about 4096), never more chunks than 32-key tiles.
+int64_t attention_chunks(int64_t heads, int64_t n) {
+    const int64_t tiles = (n + 31) / 32;
+    int64_t c = (4096 + heads - 1) / heads;
+    if (c > tiles) c = tiles;
+    if (c > 1024) c = 1024;
+    return c < 1 ? 1 : c;
+}
+
+bool attention_args_ok(int64_t heads, int32_t m, int64_t n) {
+    return heads >= 0 && m >= 1 && m <= kAttnMaxQueries && (heads == 0 || n >= 1);
+}
+
 std::atomic<int> g_cu[64];
 
 }  // namespace
@@ -164,6 +178,7 @@ const char *rht_status_str(rht_status s) {
     case RHT_E_ALIGN: return "device pointer not 16-byte aligned";
     case RHT_E_COUNT: return "negative count or m out of range";
     case RHT_E_DEVICE: return "HIP runtime error";
+    case RHT_E_WORKSPACE: return "workspace too small";
     }
     return "unknown status";
 }
@@ -312,6 +327,45 @@ rht_status rht_score(const float *q, int32_t m, const uint8_t *codes, const floa
     std::memcpy(a.lev, book(bits).lev, sizeof(a.lev));
     sign_words(seed, d, a.dsign);
     return launched(launch_score(d, bits, a, (hipStream_t)stream));
+}
+
+size_t rht_attention_workspace_bytes(int64_t heads, int32_t m, int64_t n, int32_t d) {
+    if (!attention_args_ok(heads, m, n) || d != 128 || heads == 0) return 0;
+    return (size_t)heads * (size_t)attention_chunks(heads, n) * (size_t)m * kAttnRecord * sizeof(float);
+}
+
+rht_status rht_attention(const float *q, int32_t m, const uint8_t *k_codes, const float *k_norms,
+                         const uint8_t *v_codes, const float *v_norms, int64_t heads, int64_t n,
+                         int32_t d, int32_t bits, uint64_t seed_k, uint64_t seed_v, float scale,
+                         float *out, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!attention_args_ok(heads, m, n)) return RHT_E_COUNT;
+    if (d != 128) return RHT_E_DIM;
+    if (bits != 4) return RHT_E_BITS;
+    if (heads == 0) return RHT_OK;
+    if (!q || !k_codes || !k_norms || !v_codes || !v_norms || !out || !workspace) return RHT_E_NULL;
+    if (!aligned(q) || !aligned(k_codes) || !aligned(k_norms) || !aligned(v_codes) || !aligned(v_norms) ||
+        !aligned(out) || !aligned(workspace))
+        return RHT_E_ALIGN;
+    if (workspace_bytes < rht_attention_workspace_bytes(heads, m, n, d)) return RHT_E_WORKSPACE;
+
+    AttnArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.kc = k_codes;
+    a.vc = v_codes;
+    a.kn = k_norms;
+    a.vn = v_norms;
+    a.ws = static_cast<float *>(workspace);
+    a.out = out;
+    a.heads = heads;
+    a.n = n;
+    a.m = m;
+    a.chunks = (int)attention_chunks(heads, n);
+    a.scale = scale;
+    std::memcpy(a.lev, book(bits).lev, sizeof(a.lev));
+    sign_words(seed_k, d, a.dsign_k);
+    sign_words(seed_v, d, a.dsign_v);
+    return launched(launch_attention(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

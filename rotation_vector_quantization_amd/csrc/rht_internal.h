@@ -55,6 +55,27 @@ struct ScoreArgs {
     uint32_t dsign[kMaxD / 32];
 };
 
+// Attention of m <= 16 queries over 4-bit coded keys and values, d = 128.
+// One partial record (rotated value sum z[128], running max M, running sum l,
+// two pad floats) per (head, chunk, query) in `ws`.
+constexpr int kAttnRecord = 132;
+constexpr int kAttnMaxQueries = 16;
+
+struct AttnArgs {
+    const float *q;      // [heads][m][128]
+    const uint8_t *kc;   // [heads][n][64]
+    const uint8_t *vc;
+    const float *kn;     // [heads][n]
+    const float *vn;
+    float *ws;           // [heads][chunks][m][kAttnRecord]
+    float *out;          // [heads][m][128]
+    int64_t heads, n;
+    int m, chunks;
+    float scale;
+    float lev[16];
+    uint32_t dsign_k[4], dsign_v[4];
+};
+
 // Launchers.  `layout` selects the coordinate-to-lane mapping of the MSE
 // kernels (0: each lane owns a contiguous run of the row; 1: the lanes of a
 // vector interleave in chunks of 32/bits coordinates, one code word each);
@@ -65,6 +86,7 @@ hipError_t launch_quantize(int d, bool f16, int bits, Kind kind, int layout, con
 hipError_t launch_dequantize(int d, bool f16out, int bits, Kind kind, int layout,
                              const DequantArgs &a, hipStream_t s);
 hipError_t launch_score(int d, int bits, const ScoreArgs &a, hipStream_t s);
+hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
 
 // The d = 128, fp16, 4-bit MSE encoder and decoder with the H_32 factor on
 // MFMA (launch_quantize / launch_dequantize pick them for that case).

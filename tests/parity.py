@@ -9,10 +9,13 @@
 * Reconstructions and scores are compared on identical code bytes (the oracle
   decodes the GPU's codes), per row and globally, relative L2 <= 1e-5 for fp32
   outputs and 2e-3 for fp16 outputs.
+* Attention outputs: the error model of attention_bound (fp16 hi/lo operands,
+  fp32 sums), per (head, query) row.
 """
 from __future__ import annotations
 
 import concurrent.futures
+import math
 import os
 
 import numpy as np
@@ -24,6 +27,26 @@ SCALE_RTOL = 1e-5
 RECON_F32 = 1e-5
 RECON_F16 = 2e-3
 SCORE_TOL = 1e-5
+# Attention error model.  The kernel forms every product from fp16 hi + lo
+# parts (x = hi + lo to 2^-22 relative) and sums them in fp32.  Per key j:
+#   products:   each logit s_j is a sum of d products t_jk.  Every product
+#               misses lo*lo and the rounding of the two lo parts, each at most
+#               2^-22 |t_jk|; the fp32 sums add a few 2^-24 of the sum's size.
+#               The query's and the 16 codebook levels' splits are fixed, but
+#               key j meets them through its own codes, so across keys these
+#               errors behave like independent ones: a logit is off by about
+#               ATTN_GAMMA_R * T_j, T_j = ||(t_jk)_k||_2, and the errors of
+#               different keys add in quadrature.  The value products carry
+#               the same relative error;
+#   final:      normalization, merging of chunks and the inverse transform,
+#               ATTN_GAMMA_F relative to the output.
+# A logit error ds_j moves the output by sum_j p_j ds_j (v_j - out).  Per (head, query):
+#   ||gpu - ref|| <= ATTN_SAFETY * [ ATTN_GAMMA_R sqrt(sum_j p_j^2 (T_j^2 ||v_j - ref||^2 + ||v_j||^2))
+#                    + ATTN_GAMMA_F ||ref|| ]
+# with ATTN_SAFETY a six-sigma margin on these rms estimates.
+ATTN_GAMMA_R = 2 * 2.0 ** -22 + 4 * 2.0 ** -24
+ATTN_GAMMA_F = 8 * 2.0 ** -24
+ATTN_SAFETY = 6.0
 
 
 def unpack(codes: np.ndarray, width: int, d: int) -> np.ndarray:
@@ -105,3 +128,32 @@ def check_rel(gpu: np.ndarray, ref: np.ndarray, rtol: float, what: str):
     assert err.max() <= rtol, "%s: max rel err %.3g > %.1g at %d (gpu %r ref %r)" % (
         what, err.max(), rtol, err.argmax(), gpu.flat[err.argmax()], ref.flat[err.argmax()])
     return float(err.max())
+
+
+def attention_bound(q, qt, kterm, kd, vd, ref, scale):
+    """Per (head, query) bound on ||gpu - ref|| from the error model above.
+    q [heads][m][d] queries; qt [heads][m][d] their rotations H D_k q; kterm
+    [heads][n][d] the factors (||k_j|| / d) c[code_jk] with which the rotated
+    query meets key j; kd, vd [heads][n][d] decoded keys and values; ref the
+    oracle output [heads][m][d]."""
+    out = np.zeros(ref.shape[:2])
+    for h in range(q.shape[0]):
+        s = scale * (q[h].astype(np.float64) @ kd[h].T)                          # [m][n]
+        p = np.exp(s - s.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        T = abs(scale) * np.sqrt((qt[h] ** 2) @ (kterm[h] ** 2).T)               # [m][n]
+        vnorm2 = (vd[h] ** 2).sum(1)                                             # [n]
+        spread2 = ((vd[h][None, :, :] - ref[h][:, None, :]) ** 2).sum(2)         # [m][n]
+        rand = np.sqrt((p ** 2 * (T ** 2 * spread2 + vnorm2[None, :])).sum(1))
+        out[h] = ATTN_SAFETY * (ATTN_GAMMA_R * rand + ATTN_GAMMA_F * np.linalg.norm(ref[h], axis=1))
+    return out
+
+
+def attention_terms(q, kc, kn, d, bits, seed_k, levels, signs_k, hadamard):
+    """Inputs of attention_bound: the rotated queries H D_k q and the factors
+    (||k_j|| / d) c[code_jk], from the oracle's codebook and signs and a dense
+    Hadamard matrix."""
+    qt = np.einsum("ij,hmj->hmi", hadamard, q.astype(np.float64) * signs_k[None, None, :])
+    code = unpack(kc.reshape(-1, kc.shape[-1]), bits, d).reshape(kc.shape[0], kc.shape[1], d)
+    kterm = levels[code] * (kn.astype(np.float64) / d)[..., None]
+    return qt, kterm

@@ -14,7 +14,7 @@ import rotation_vector_quantization_amd as rht
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rht.h")
 
-OK, E_NULL, E_DIM, E_BITS, E_DTYPE, E_MODE, E_ALIGN, E_COUNT, E_DEVICE = range(9)
+OK, E_NULL, E_DIM, E_BITS, E_DTYPE, E_MODE, E_ALIGN, E_COUNT, E_DEVICE, E_WORKSPACE = range(10)
 FAKE = 0x10000  # never dereferenced: validation fails (or n == 0) before any use
 
 
@@ -33,14 +33,14 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     for name in names:
         assert hasattr(lib, name), name
 
 
 def test_abi_version(lib):
-    assert rht.rht_abi_version() == 1
-    for s in range(9):
+    assert rht.rht_abi_version() == 2
+    for s in range(10):
         assert isinstance(rht.rht_status_str(s), str) and rht.rht_status_str(s)
 
 
@@ -110,3 +110,37 @@ def test_binding_rejects_cpu_tensors(lib):
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError):
         rht.quantize(torch.zeros(4, 128), 4, 1)
+
+
+def _att(lib, q=FAKE, m=4, kc=FAKE, kn=FAKE, vc=FAKE, vn=FAKE, heads=2, n=100, d=128, bits=4, out=FAKE,
+         ws=FAKE, wsb=1 << 40):
+    return lib.rht_attention(q, m, kc, kn, vc, vn, heads, n, d, bits, 1, 2, 0.1, out, ws, wsb, None)
+
+
+def test_attention_validation_order(lib):
+    assert _att(lib, heads=-1, d=64) == E_COUNT
+    for m in (0, 17, -1):
+        assert _att(lib, m=m, d=64) == E_COUNT
+    assert _att(lib, n=0, d=64) == E_COUNT
+    for d in (64, 256, 100):
+        assert _att(lib, d=d, bits=2) == E_DIM
+    for b in (1, 2, 3, 5):
+        assert _att(lib, bits=b) == E_BITS
+    assert _att(lib, heads=0, q=0, kc=0, kn=0, vc=0, vn=0, out=0, ws=0, n=0) == OK  # no-op
+    for kw in ("q", "kc", "kn", "vc", "vn", "out", "ws"):
+        assert _att(lib, **{kw: 0}) == E_NULL, kw
+    for kw in ("q", "kc", "kn", "vc", "vn", "out", "ws"):
+        assert _att(lib, **{kw: FAKE + 4}) == E_ALIGN, kw
+    need = rht.rht_attention_workspace_bytes(2, 4, 100, 128)
+    assert need > 0
+    assert _att(lib, wsb=need - 1) == E_WORKSPACE
+
+
+def test_attention_workspace_bytes(lib):
+    # one record of 132 floats per (head, chunk, query); chunks never exceed 32-key tiles
+    assert rht.rht_attention_workspace_bytes(1, 1, 1, 128) == 132 * 4
+    assert rht.rht_attention_workspace_bytes(2, 4, 100, 128) == 2 * 4 * 4 * 132 * 4
+    assert rht.rht_attention_workspace_bytes(256, 4, 32768, 128) == 256 * 16 * 4 * 132 * 4
+    assert rht.rht_attention_workspace_bytes(0, 4, 100, 128) == 0
+    assert rht.rht_attention_workspace_bytes(1, 17, 100, 128) == 0
+    assert rht.rht_attention_workspace_bytes(1, 4, 100, 64) == 0

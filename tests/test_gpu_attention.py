@@ -1,0 +1,156 @@
+"""GPU parity of attention over coded keys and values (rht_attention, through
+the C ABI) against the CPU oracle's plain definition: decode K and V in fp64,
+softmax(scale q.k), weighted sum of the decoded values.
+
+The coded inputs come from the oracle's encoder, or, at the full KV-block size,
+from a seeded byte generator (any byte string is a valid 4-bit code row); no
+input or expected value comes from the HIP path.  Tolerance: the error model
+in tests/parity.py (attention_bound), per (head, query) output row; the kernel
+splits every MFMA operand into fp16 hi + lo parts and accumulates in fp32, so
+its error is fp32-level, scaled by how strongly the softmax depends on the
+logits.  tests/test_attention_tolerance.py shows on the CPU that an emulation
+of this arithmetic stays well inside the bound and that losing a lo part
+leaves it.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import rotation_vector_quantization_amd as rht
+import scipy.linalg
+
+from parity import attention_bound, attention_terms, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+D, BITS = 128, 4
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    rht.load()
+    return torch.device("cuda:0")
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def coded(rng, heads, n, seed, row_scale=None):
+    x = rng.standard_normal((heads * n, D)).astype(np.float32)
+    if row_scale is not None:
+        x *= row_scale.reshape(-1, 1).astype(np.float32)
+    c, nr = oracle.quantize(x, BITS, seed)
+    return c.reshape(heads, n, -1), nr.reshape(heads, n)
+
+
+def run(q, kc, kn, vc, vn, sk, sv, scale, workspace=None):
+    return host(rht.attention(dev(q), dev(kc), dev(kn), dev(vc), dev(vn), BITS, sk, sv, scale,
+                              workspace=workspace))
+
+
+def decoded(codes, norms, seed):
+    heads, n, _ = codes.shape
+    out = oracle.dequantize(codes.reshape(heads * n, -1), norms.reshape(-1), D, BITS, seed, np.float32)
+    return out.reshape(heads, n, D).astype(np.float64)
+
+
+def check(got, want, what, q, kc, kn, vc, vn, sk, sv, scale):
+    heads, m, _ = want.shape
+    qt, kterm = attention_terms(q, kc, kn, D, BITS, sk, oracle.lloyd_max(BITS)[0],
+                                oracle.signs(sk, D).astype(np.float64), scipy.linalg.hadamard(D))
+    bound = attention_bound(q, qt, kterm, decoded(kc, kn, sk), decoded(vc, vn, sv), want, scale)
+    err = np.linalg.norm(got.astype(np.float64) - want, axis=2)
+    ref = np.linalg.norm(want, axis=2)
+    rel = np.where(ref > 0, err / np.maximum(ref, 1e-300), 0.0)
+    worst = np.unravel_index(np.argmax(err / np.maximum(bound, 1e-300)), err.shape)
+    say("%s: worst row rel L2 %.3g; worst error / bound %.3g" % (
+        what, rel.max(), (err / np.maximum(bound, 1e-300)).max()))
+    assert np.all(err <= bound), "%s: row %s error %.3g > bound %.3g (rel L2 %.3g)" % (
+        what, worst, err[worst], bound[worst], rel[worst])
+    assert np.all(got[ref == 0] == 0), "%s: zero rows not exactly zero" % what
+    assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("heads,m,n", [(1, 1, 1), (1, 4, 31), (3, 4, 32), (2, 16, 33), (3, 5, 100),
+                                       (2, 8, 1000), (1, 4, 4099), (5, 3, 257)])
+@pytest.mark.parametrize("scale", [1.0 / math.sqrt(D), 1.0])
+def test_attention_grid(heads, m, n, scale):
+    rng = np.random.default_rng(heads * 1000 + m * 10 + n)
+    kc, kn = coded(rng, heads, n, 51)
+    vc, vn = coded(rng, heads, n, 52)
+    q = (2 * rng.standard_normal((heads, m, D))).astype(np.float32)
+    say("attention grid heads=%d m=%d n=%d scale=%g" % (heads, m, n, scale))
+    want = oracle.attention(q, kc, kn, vc, vn, D, BITS, 51, 52, scale)
+    check(run(q, kc, kn, vc, vn, 51, 52, scale), want, "grid %d/%d/%d" % (heads, m, n),
+          q, kc, kn, vc, vn, 51, 52, scale)
+
+
+def test_attention_degenerate_queries_and_values():
+    rng = np.random.default_rng(3)
+    heads, m, n = 4, 6, 300
+    kc, kn = coded(rng, heads, n, 61)
+    vn_scale = np.ones(heads * n)
+    vn_scale[:n] = 0.0                                           # head 0: every value is zero
+    vn_scale[n:2 * n] = 10.0 ** rng.uniform(-20, 20, n)          # head 1: norms over 40 decades
+    vn_scale[2 * n + 37] = 0.0                                   # head 2: one zero value
+    vc, vn = coded(rng, heads, n, 62, vn_scale)
+    q = rng.standard_normal((heads, m, D)).astype(np.float32)
+    q[:, 0] = 0.0                                                # uniform weights
+    q[:, 1] *= 1e4                                               # hard attention
+    q[:, 2] *= 1e-30                                             # tiny query
+    say("attention degenerate cases")
+    want = oracle.attention(q, kc, kn, vc, vn, D, BITS, 61, 62, 1.0 / math.sqrt(D))
+    got = run(q, kc, kn, vc, vn, 61, 62, 1.0 / math.sqrt(D))
+    assert np.all(got[0] == 0.0)
+    check(got, want, "degenerate", q, kc, kn, vc, vn, 61, 62, 1.0 / math.sqrt(D))
+
+
+def test_attention_workspace_reused_by_a_smaller_call():
+    rng = np.random.default_rng(4)
+    big = (6, 8, 2000)
+    need = rht.rht_attention_workspace_bytes(*big, D)
+    ws = torch.empty((need,), dtype=torch.uint8, device="cuda:0")
+    for heads, m, n in (big, (2, 3, 77)):
+        kc, kn = coded(rng, heads, n, 71)
+        vc, vn = coded(rng, heads, n, 72)
+        q = rng.standard_normal((heads, m, D)).astype(np.float32)
+        say("attention with a shared workspace heads=%d m=%d n=%d" % (heads, m, n))
+        want = oracle.attention(q, kc, kn, vc, vn, D, BITS, 71, 72, 0.1)
+        check(run(q, kc, kn, vc, vn, 71, 72, 0.1, workspace=ws), want, "shared workspace",
+              q, kc, kn, vc, vn, 71, 72, 0.1)
+
+
+def test_attention_kv_block_full_size_sampled_heads():
+    # the benchmark's shape: 32 layers x 8 KV heads = 256 heads, 32768 tokens, 4 queries per head
+    heads, n, m = 256, 32768, 4
+    rng = np.random.default_rng(20250)
+    kc = rng.integers(0, 256, (heads, n, D // 2), dtype=np.uint8)
+    vc = rng.integers(0, 256, (heads, n, D // 2), dtype=np.uint8)
+    kn = np.exp(0.5 * rng.standard_normal((heads, n))).astype(np.float32) * math.sqrt(D)
+    vn = np.exp(0.5 * rng.standard_normal((heads, n))).astype(np.float32) * math.sqrt(D)
+    q = rng.standard_normal((heads, m, D)).astype(np.float32)
+    say("attention full size: %d heads x %d keys x %d queries" % (heads, n, m))
+    got = run(q, kc, kn, vc, vn, 42, 43, 1.0 / math.sqrt(D))
+    assert np.all(np.isfinite(got))
+    for h in (0, 77, 255):
+        want = oracle.attention(q[h:h + 1], kc[h:h + 1], kn[h:h + 1], vc[h:h + 1], vn[h:h + 1], D, BITS,
+                                42, 43, 1.0 / math.sqrt(D))
+        check(got[h:h + 1], want, "full size head %d" % h, q[h:h + 1], kc[h:h + 1], kn[h:h + 1],
+              vc[h:h + 1], vn[h:h + 1], 42, 43, 1.0 / math.sqrt(D))
