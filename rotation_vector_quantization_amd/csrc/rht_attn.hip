@@ -24,7 +24,9 @@
 //            a power of two into fp16 range.
 //   values:  z^T[coord][query] += sum_key Cv^T[coord][key] P[key][query],
 //            P = p_j ||v_j|| times a running power of two; the accumulator
-//            layout of the logits tiles is exactly the B layout P needs.
+//            layout of the logits tiles is exactly the B layout P needs; the
+//            value codes of a tile pass through LDS and an 8 x 8 nibble
+//            transpose so each lane holds eight keys' codes per coordinate.
 // Lane layout of the 16x16x32 instruction (lane l, g = l / 16): A holds
 // A[l % 16][8 g + t], B holds B[8 g + t][l % 16], C holds C[4 g + r][l % 16].
 #include "rht_device.h"
@@ -82,49 +84,71 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// Clamped fp32 load of element idx of a row of n (n >= 1).
-__device__ __forceinline__ float load_clamped(const float *p, int64_t idx, int64_t n) {
-    return p[idx < n ? idx : n - 1];
-}
-
 // Global loads of one 32-key tile for a lane: K code bytes 16g..16g+15 of keys
 // key0 + l%16 and key0 + 16 + l%16; the lane's two 16-byte pieces of the value
-// tile (chunks l and 64 + l of the 32 x 64-byte tile); the key and value norms
-// of the keys this lane's accumulator rows hold (4g + r and 16 + 4g + r).
+// tile (chunks l and 64 + l of the 32 x 64-byte tile); one norm (lanes 0-31:
+// key norm of key0 + l, lanes 32-63: value norm of key0 + l - 32).  Offsets are
+// 32-bit from per-head bases; FULL tiles need no clamping, the last partial
+// tile repeats key n-1 (its logits are masked).
 struct TileRegs {
     u32x4_t k0, k1, v0, v1;
-    float kn[8], vn[8];
+    float nrm;
 };
 
-__device__ __forceinline__ void load_tile(const AttnArgs &a, const uint8_t *kc, const uint8_t *vc,
-                                          const float *kn, const float *vn, int64_t key0, uint32_t lane,
-                                          TileRegs &t) {
+template <bool FULL>
+__device__ __forceinline__ void load_tile(const uint8_t *kc, const uint8_t *vc, const float *kn, const float *vn,
+                                          int64_t n, int64_t key0, uint32_t lane, TileRegs &t) {
     const uint32_t j = lane & 15u, g = lane >> 4;
-    const int64_t n = a.n;
-    auto row = [n](int64_t r) { return r < n ? r : n - 1; };
-    t.k0 = *reinterpret_cast<const u32x4_t *>(kc + row(key0 + j) * kACodeBytes + 16 * g);
-    t.k1 = *reinterpret_cast<const u32x4_t *>(kc + row(key0 + 16 + j) * kACodeBytes + 16 * g);
-    t.v0 = *reinterpret_cast<const u32x4_t *>(vc + row(key0 + lane / 4) * kACodeBytes + 16 * (lane % 4));
-    t.v1 = *reinterpret_cast<const u32x4_t *>(vc + row(key0 + 16 + lane / 4) * kACodeBytes + 16 * (lane % 4));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        t.kn[r] = load_clamped(kn, key0 + 4 * g + r, n);
-        t.kn[4 + r] = load_clamped(kn, key0 + 16 + 4 * g + r, n);
-        t.vn[r] = load_clamped(vn, key0 + 4 * g + r, n);
-        t.vn[4 + r] = load_clamped(vn, key0 + 16 + 4 * g + r, n);
+    uint32_t r0 = (uint32_t)key0 + j, r1 = r0 + 16, r2 = (uint32_t)key0 + lane / 4, r3 = r2 + 16;
+    uint32_t rn = (uint32_t)key0 + (lane & 31u);
+    if (!FULL) {
+        const uint32_t last = (uint32_t)(n - 1);
+        r0 = min(r0, last); r1 = min(r1, last); r2 = min(r2, last); r3 = min(r3, last); rn = min(rn, last);
     }
+    t.k0 = *reinterpret_cast<const u32x4_t *>(kc + r0 * kACodeBytes + 16 * g);
+    t.k1 = *reinterpret_cast<const u32x4_t *>(kc + r1 * kACodeBytes + 16 * g);
+    t.v0 = *reinterpret_cast<const u32x4_t *>(vc + r2 * kACodeBytes + 16 * (lane % 4));
+    t.v1 = *reinterpret_cast<const u32x4_t *>(vc + r3 * kACodeBytes + 16 * (lane % 4));
+    t.nrm = (lane < 32 ? kn : vn)[rn];
+}
+
+// Per code byte, the fp16 hi parts (tabh) and lo parts (tabl) of its two
+// levels, low nibble in the low half.  Separate word tables let every lookup
+// land directly in its MFMA operand register.
+// kTabCopies interleaved copies (entry i of copy r at word i * kTabCopies + r);
+// lane l reads copy l % kTabCopies, so only 64 / kTabCopies lanes of a wave
+// compete for the banks of one copy's words.
+#ifndef RHT_ATTN_TAB_COPIES
+#define RHT_ATTN_TAB_COPIES 32
+#endif
+constexpr int kTabCopies = RHT_ATTN_TAB_COPIES;
+
+struct LevelTables {
+    uint32_t h[256 * kTabCopies], l[256 * kTabCopies];
+};
+
+// The A operands for four code bytes: hi parts and lo parts, byte i in word i.
+// The reads go through volatile pointers so the compiler keeps them as single
+// ds_read_b32 into the operand registers instead of pairing the hi and lo
+// word of a byte into one two-register read that then needs moves.
+__device__ __forceinline__ void level_operands(const LevelTables &tb, uint32_t copy, uint32_t w, u32x4_t &ah,
+                                               u32x4_t &al) {
+    typedef __attribute__((address_space(3))) const volatile uint32_t lds_word;
+    const lds_word *h = (const lds_word *)tb.h + copy, *l = (const lds_word *)tb.l + copy;
+    const uint32_t b0 = (w & 0xFFu) * kTabCopies, b1 = ((w >> 8) & 0xFFu) * kTabCopies;
+    const uint32_t b2 = ((w >> 16) & 0xFFu) * kTabCopies, b3 = (w >> 24) * kTabCopies;
+    ah = u32x4_t{h[b0], h[b1], h[b2], h[b3]};
+    al = u32x4_t{l[b0], l[b1], l[b2], l[b3]};
 }
 
 // Logits of 16 keys (one 16-byte code piece per lane) against the queries.
-__device__ __forceinline__ floatx4 key_logits(const uint2 *tab, u32x4_t kc, const u32x4_t (&bh)[4],
-                                              const u32x4_t (&bl)[4]) {
+__device__ __forceinline__ floatx4 key_logits(const LevelTables &tb, uint32_t copy, u32x4_t kc,
+                                              const u32x4_t (&bh)[4], const u32x4_t (&bl)[4]) {
     floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        const uint32_t w = kc[ks];
-        const uint2 e0 = tab[w & 0xFFu], e1 = tab[(w >> 8) & 0xFFu];
-        const uint2 e2 = tab[(w >> 16) & 0xFFu], e3 = tab[w >> 24];
-        const u32x4_t ah = {e0.x, e1.x, e2.x, e3.x}, al = {e0.y, e1.y, e2.y, e3.y};
+        u32x4_t ah, al;
+        level_operands(tb, copy, kc[ks], ah, al);
         c = mfma1632(ah, bh[ks], c);
         c = mfma1632(ah, bl[ks], c);
         c = mfma1632(al, bh[ks], c);
@@ -132,52 +156,195 @@ __device__ __forceinline__ floatx4 key_logits(const uint2 *tab, u32x4_t kc, cons
     return c;
 }
 
-__global__ __launch_bounds__(kBlock) void k_attn_partial(const AttnArgs a) {
-    __shared__ uint2 tab[256];
-    __shared__ float qbuf[kWaves][16][kAD];
-    __shared__ __attribute__((aligned(16))) uint8_t vbuf[kWaves][32 * kVRow];
+// Transpose of an 8 x 8 matrix of nibbles: on entry nibble n of a[t] is
+// element (t, n), on return nibble t of a[n] is.  Swaps of 4x4 blocks
+// (16-bit halves), 2x2 blocks (bytes) and single nibbles.
+__device__ __forceinline__ void transpose_nibbles8(uint32_t (&a)[8]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint32_t lo = __builtin_amdgcn_perm(a[t + 4], a[t], 0x05040100u);
+        const uint32_t hi = __builtin_amdgcn_perm(a[t + 4], a[t], 0x07060302u);
+        a[t] = lo;
+        a[t + 4] = hi;
+    }
+#pragma unroll
+    for (int t = 0; t < 8; t += (t % 4 == 1) ? 3 : 1) {
+        const uint32_t lo = __builtin_amdgcn_perm(a[t + 2], a[t], 0x06020400u);
+        const uint32_t hi = __builtin_amdgcn_perm(a[t + 2], a[t], 0x07030501u);
+        a[t] = lo;
+        a[t + 2] = hi;
+    }
+#pragma unroll
+    for (int t = 0; t < 8; t += 2) {
+        const uint32_t x = a[t], y = a[t + 1];
+        a[t] = (x & 0x0F0F0F0Fu) | ((y << 4) & 0xF0F0F0F0u);
+        a[t + 1] = ((x >> 4) & 0x0F0F0F0Fu) | (y & 0xF0F0F0F0u);
+    }
+}
+
+// Per-wave running state of the online softmax.
+struct SoftmaxState {
+    float M, l;
+    int ev;              // value scale exponent: P = p ||v|| 2^(14 - ev)
+    floatx4 z[8];        // z^T tile n: row 4g + r <-> coordinate 32g + 8r + n, column = query
+};
+
+// Copy a tile's value codes (key r at vb + r * kVRow) and norms into LDS.
+// Done before the next tile's loads are issued: waiting for this tile's
+// registers then does not wait for the prefetch behind them.
+__device__ __forceinline__ void stage_tile(uint8_t *vb, float *nb, const TileRegs &t, uint32_t lane) {
+    *reinterpret_cast<u32x4_t *>(vb + (lane / 4) * kVRow + 16 * (lane % 4)) = t.v0;
+    *reinterpret_cast<u32x4_t *>(vb + (16 + lane / 4) * kVRow + 16 * (lane % 4)) = t.v1;
+    nb[lane] = t.nrm;
+}
+
+// One staged 32-key tile: logits on MFMA, online softmax, value sums on MFMA.
+// FULL: every key of the tile is < n.
+template <bool FULL>
+__device__ __forceinline__ void attend_tile(const LevelTables &tb, const uint8_t *vb, const float *nb,
+                                            u32x4_t k0, u32x4_t k1, const u32x4_t (&bh)[4], const u32x4_t (&bl)[4],
+                                            float fq, int64_t key0, int64_t n, uint32_t lane, SoftmaxState &st) {
+    const uint32_t j = lane & 15u, g = lane >> 4;
+
+    // logits: rows 4g + r of tile 0 are keys 4g + r, of tile 1 keys 16 + 4g + r
+    const floatx4 c0 = key_logits(tb, lane % kTabCopies, k0, bh, bl);
+    const floatx4 c1 = key_logits(tb, lane % kTabCopies, k1, bh, bl);
+    const float4 kn0 = *reinterpret_cast<const float4 *>(nb + 4 * g);
+    const float4 kn1 = *reinterpret_cast<const float4 *>(nb + 16 + 4 * g);
+    const float4 vn0 = *reinterpret_cast<const float4 *>(nb + 32 + 4 * g);
+    const float4 vn1 = *reinterpret_cast<const float4 *>(nb + 48 + 4 * g);
+    const float knr[8] = {kn0.x, kn0.y, kn0.z, kn0.w, kn1.x, kn1.y, kn1.z, kn1.w};
+    const float vnr[8] = {vn0.x, vn0.y, vn0.z, vn0.w, vn1.x, vn1.y, vn1.z, vn1.w};
+    float s[8], vmax = 0.0f, smax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const float cv = r < 4 ? c0[r] : c1[r - 4];
+        s[r] = cv * knr[r] * fq;
+        float vr = vnr[r];
+        if (!FULL) {
+            const bool live = key0 + (r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4)) < n;
+            s[r] = live ? s[r] : -INFINITY;
+            vr = live ? vr : 0.0f;
+        }
+        smax = fmaxf(smax, s[r]);
+        vmax = fmaxf(vmax, vr);
+    }
+    smax = fmaxf(smax, __shfl_xor(smax, 16));
+    smax = fmaxf(smax, __shfl_xor(smax, 32));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
+    const float Mn = fmaxf(st.M, smax);
+    const int evn = vmax > 0.0f ? max(st.ev, exponent_above(vmax)) : st.ev;
+    // rescale the running sums to the new max and value scale (skipped when
+    // neither moved for any query of the wave)
+    const float alpha = __builtin_amdgcn_exp2f(st.M - Mn);
+    const float rz = alpha * pow2i_down(st.ev - evn);
+    st.M = Mn;
+    st.ev = evn;
+    st.l *= alpha;
+    if (__any(rz != 1.0f)) {
+#pragma unroll
+        for (int nn = 0; nn < 8; ++nn) st.z[nn] *= rz;
+    }
+    const float vs = pow2i(14 - st.ev);
+    float P[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(s[r] - st.M);
+        st.l += pr;
+        P[r] = pr * vnr[r] * vs;
+    }
+    // B operand of the value product: k = 8g + t <-> key (t < 4 ? 4g + t : 16 + 4g + t - 4)
+    u32x4_t ph, pl;
     {
-        const uint32_t v = threadIdx.x;
-        tab[v] = split2(a.lev[v & 15u], a.lev[v >> 4]);
+        const uint2 s0 = split2(P[0], P[1]), s1 = split2(P[2], P[3]);
+        const uint2 s2 = split2(P[4], P[5]), s3 = split2(P[6], P[7]);
+        ph = u32x4_t{s0.x, s1.x, s2.x, s3.x};
+        pl = u32x4_t{s0.y, s1.y, s2.y, s3.y};
+    }
+    // A operand of tile n: row j <-> coordinate 8j + n, k = 8g + t <-> the key above.
+    // Code dword j of key t holds coordinates 8j .. 8j+7; transposed, byte w of
+    // word n holds coordinate 8j + n of keys 2w, 2w+1: one table entry each.
+    uint32_t a[8];
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+        const uint32_t key = tt < 4 ? 4 * g + tt : 16 + 4 * g + (tt - 4);
+        a[tt] = *reinterpret_cast<const uint32_t *>(vb + key * kVRow + 4 * j);
+    }
+    transpose_nibbles8(a);
+#pragma unroll
+    for (int nn = 0; nn < 8; ++nn) {
+        u32x4_t ah, al;
+        level_operands(tb, lane % kTabCopies, a[nn], ah, al);
+        st.z[nn] = mfma1632(ah, ph, st.z[nn]);
+        st.z[nn] = mfma1632(ah, pl, st.z[nn]);
+        st.z[nn] = mfma1632(al, ph, st.z[nn]);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_attn_partial(const AttnArgs a) {
+    __shared__ LevelTables tb;
+    __shared__ __attribute__((aligned(16))) uint8_t vbuf[kWaves][32 * kVRow];
+    __shared__ __attribute__((aligned(16))) float nbuf[kWaves][64];
+    for (uint32_t k = threadIdx.x; k < 256u * kTabCopies; k += kBlock) {
+        const uint32_t v = k / kTabCopies;
+        const uint2 e = split2(a.lev[v & 15u], a.lev[v >> 4]);
+        tb.h[k] = e.x;
+        tb.l[k] = e.y;
     }
     __syncthreads();
 
-    const uint32_t lane = lane_id(), wave = threadIdx.x >> 6, j = lane & 15u, g = lane >> 4;
+    const uint32_t lane = lane_id(), j = lane & 15u, g = lane >> 4;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t gw = (int64_t)blockIdx.x * kWaves + wave;
     if (gw >= a.heads * a.chunks) return;  // whole wave; no block barrier follows
     const int64_t head = gw / a.chunks;
     const int chunk = (int)(gw % a.chunks);
-    const int64_t tiles = (a.n + 31) / 32;
+    const int64_t n = a.n;
+    const int64_t tiles = (n + 31) / 32;
     const int64_t t_begin = tiles * chunk / a.chunks, t_end = tiles * (chunk + 1) / a.chunks;
 
-    // --- queries: q~ = H D_k q, scaled by 2^(14 - e) into fp16 range
+    // --- queries: q~ = H D_k q, scaled by 2^(14 - e) into fp16 range.  The
+    // B operand of the logits for lane (query j, group g), K step ks, word w is
+    // the coordinate pair 32g + 8ks + 2w (+1), held by lane 16g + 4ks + w after
+    // the transform; every lane fetches it for every query and keeps query j's.
     float qscale_mine = 1.0f;  // power of two applied to query j
-    for (int i = 0; i < 16; ++i) {
-        float v0 = 0.0f, v1 = 0.0f;
-        if (i < a.m) {
-            const float2 qv = reinterpret_cast<const float2 *>(a.q + (head * a.m + i) * kAD)[lane];
-            const uint32_t sb = a.dsign_k[lane >> 4] >> ((2 * lane) & 31);
-            v0 = (sb & 1u) ? -qv.x : qv.x;
-            v1 = (sb & 2u) ? -qv.y : qv.y;
-            fwht128_pairs(v0, v1, lane);
-        }
+    float qp[4][4][2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) qp[ks][w][0] = qp[ks][w][1] = 0.0f;
+    for (int i = 0; i < a.m; ++i) {
+        const float2 qv = reinterpret_cast<const float2 *>(a.q + (head * a.m + i) * kAD)[lane];
+        const uint32_t sb = a.dsign_k[lane >> 4] >> ((2 * lane) & 31);
+        float v0 = (sb & 1u) ? -qv.x : qv.x;
+        float v1 = (sb & 2u) ? -qv.y : qv.y;
+        fwht128_pairs(v0, v1, lane);
         const float mx = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
         const float sc = mx > 0.0f ? pow2i(min(14 - exponent_above(mx), 126)) : 1.0f;
-        if ((uint32_t)i == j) qscale_mine = sc;
-        qbuf[wave][i][2 * lane] = v0 * sc;
-        qbuf[wave][i][2 * lane + 1] = v1 * sc;
+        v0 *= sc;
+        v1 *= sc;
+        const bool mine = (uint32_t)i == j;
+        if (mine) qscale_mine = sc;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int src = 16 * (int)g + 4 * ks + w;
+                const float p0 = __shfl(v0, src), p1 = __shfl(v1, src);
+                qp[ks][w][0] = mine ? p0 : qp[ks][w][0];
+                qp[ks][w][1] = mine ? p1 : qp[ks][w][1];
+            }
     }
-    // B operand of the logits: B[k][query j] for K step ks, k = 8g + t <-> coordinate 32g + 8ks + t
     u32x4_t bh[4], bl[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         uint32_t h[4], l[4];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            const int c = 32 * g + 8 * ks + 2 * w;
-            const uint2 s = split2(qbuf[wave][j][c], qbuf[wave][j][c + 1]);
-            h[w] = s.x;
-            l[w] = s.y;
+            const uint2 sp = split2(qp[ks][w][0], qp[ks][w][1]);
+            h[w] = sp.x;
+            l[w] = sp.y;
         }
         bh[ks] = u32x4_t{h[0], h[1], h[2], h[3]};
         bl[ks] = u32x4_t{l[0], l[1], l[2], l[3]};
@@ -185,120 +352,60 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(const AttnArgs a) {
     // logits in base-2 units: s = C * ||k|| * fq
     const float fq = a.scale * 1.4426950408889634f / ((float)kAD * qscale_mine);
 
-    const uint8_t *kc = a.kc + head * a.n * kACodeBytes;
-    const uint8_t *vc = a.vc + head * a.n * kACodeBytes;
-    const float *kn = a.kn + head * a.n;
-    const float *vn = a.vn + head * a.n;
+    const uint8_t *kc = a.kc + head * n * kACodeBytes;
+    const uint8_t *vc = a.vc + head * n * kACodeBytes;
+    const float *kn = a.kn + head * n;
+    const float *vn = a.vn + head * n;
     uint8_t *vb = vbuf[wave];
+    float *nb = nbuf[wave];
 
-    float M = -INFINITY, l = 0.0f;
-    int ev = -100;  // value scale exponent: P = p ||v|| 2^(14 - ev)
-    floatx4 ze[4], zo[4];
+    SoftmaxState st;
+    st.M = -INFINITY;
+    st.l = 0.0f;
+    st.ev = -100;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        ze[p] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-        zo[p] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int nn = 0; nn < 8; ++nn) st.z[nn] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // full tiles with the next one's loads in flight (two register sets), then
+    // the partial last tile if n is not a multiple of 32
+    const int64_t t_full = min(t_end, n / 32);
+    TileRegs ra, rb;
+    int64_t tile = t_begin;
+    if (tile < t_full) load_tile<true>(kc, vc, kn, vn, n, tile * 32, lane, ra);
+    while (tile < t_full) {
+        stage_tile(vb, nb, ra, lane);
+        if (tile + 1 < t_full) load_tile<true>(kc, vc, kn, vn, n, (tile + 1) * 32, lane, rb);
+        attend_tile<true>(tb, vb, nb, ra.k0, ra.k1, bh, bl, fq, tile * 32, n, lane, st);
+        if (++tile >= t_full) break;
+        stage_tile(vb, nb, rb, lane);
+        if (tile + 1 < t_full) load_tile<true>(kc, vc, kn, vn, n, (tile + 1) * 32, lane, ra);
+        attend_tile<true>(tb, vb, nb, rb.k0, rb.k1, bh, bl, fq, tile * 32, n, lane, st);
+        ++tile;
+    }
+    if (t_full < t_end) {
+        load_tile<false>(kc, vc, kn, vn, n, t_full * 32, lane, ra);
+        stage_tile(vb, nb, ra, lane);
+        attend_tile<false>(tb, vb, nb, ra.k0, ra.k1, bh, bl, fq, t_full * 32, n, lane, st);
     }
 
-    TileRegs nxt;
-    if (t_begin < t_end) load_tile(a, kc, vc, kn, vn, t_begin * 32, lane, nxt);
-    for (int64_t tile = t_begin; tile < t_end; ++tile) {
-        const int64_t key0 = tile * 32;
-        const TileRegs cur = nxt;
-        // stage the value codes: key r at vb + r * kVRow
-        *reinterpret_cast<u32x4_t *>(vb + (lane / 4) * kVRow + 16 * (lane % 4)) = cur.v0;
-        *reinterpret_cast<u32x4_t *>(vb + (16 + lane / 4) * kVRow + 16 * (lane % 4)) = cur.v1;
-        if (tile + 1 < t_end) load_tile(a, kc, vc, kn, vn, key0 + 32, lane, nxt);
-
-        // logits: rows 4g + r of tile 0 are keys 4g + r, of tile 1 keys 16 + 4g + r
-        const floatx4 c0 = key_logits(tab, cur.k0, bh, bl);
-        const floatx4 c1 = key_logits(tab, cur.k1, bh, bl);
-        float s[8], vmax = 0.0f, smax = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int64_t key = key0 + (r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4));
-            const float cv = r < 4 ? c0[r] : c1[r - 4];
-            s[r] = key < a.n ? cv * cur.kn[r] * fq : -INFINITY;
-            smax = fmaxf(smax, s[r]);
-            if (key < a.n) vmax = fmaxf(vmax, cur.vn[r]);
-        }
-        smax = fmaxf(smax, __shfl_xor(smax, 16));
-        smax = fmaxf(smax, __shfl_xor(smax, 32));
-        vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
-        vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
-        const float Mn = fmaxf(M, smax);
-        const int evn = vmax > 0.0f ? max(ev, exponent_above(vmax)) : ev;
-        // rescale the running sums to the new max and value scale
-        const float alpha = __builtin_amdgcn_exp2f(M - Mn);
-        const float rz = alpha * pow2i_down(ev - evn);
-        M = Mn;
-        ev = evn;
-        l *= alpha;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            ze[p] *= rz;
-            zo[p] *= rz;
-        }
-        const float vs = pow2i(14 - ev);
-        float P[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const float pr = __builtin_amdgcn_exp2f(s[r] - M);
-            l += pr;
-            P[r] = pr * cur.vn[r] * vs;
-        }
-        // B operand of the value product: k = 8g + t <-> key (t < 4 ? 4g + t : 16 + 4g + t - 4)
-        u32x4_t ph, pl;
-        {
-            const uint2 s0 = split2(P[0], P[1]), s1 = split2(P[2], P[3]);
-            const uint2 s2 = split2(P[4], P[5]), s3 = split2(P[6], P[7]);
-            ph = u32x4_t{s0.x, s1.x, s2.x, s3.x};
-            pl = u32x4_t{s0.y, s1.y, s2.y, s3.y};
-        }
-        // A operand: row = coordinate 32p + 2 (l % 16) + e, k = 8g + t <-> the key above;
-        // code byte 16p + l % 16 of that key holds both coordinates of the pair.
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            uint2 e[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const uint32_t key = t < 4 ? 4 * g + t : 16 + 4 * g + (t - 4);
-                e[t] = tab[vb[key * kVRow + 16 * p + j]];
-            }
-            u32x4_t aeh, aol, ael, aoh;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                // low halves (even coordinate) and high halves (odd) of keys 2w, 2w+1
-                aeh[w] = __builtin_amdgcn_perm(e[2 * w + 1].x, e[2 * w].x, 0x05040100u);
-                aoh[w] = __builtin_amdgcn_perm(e[2 * w + 1].x, e[2 * w].x, 0x07060302u);
-                ael[w] = __builtin_amdgcn_perm(e[2 * w + 1].y, e[2 * w].y, 0x05040100u);
-                aol[w] = __builtin_amdgcn_perm(e[2 * w + 1].y, e[2 * w].y, 0x07060302u);
-            }
-            ze[p] = mfma1632(aeh, ph, ze[p]);
-            ze[p] = mfma1632(aeh, pl, ze[p]);
-            ze[p] = mfma1632(ael, ph, ze[p]);
-            zo[p] = mfma1632(aoh, ph, zo[p]);
-            zo[p] = mfma1632(aoh, pl, zo[p]);
-            zo[p] = mfma1632(aol, ph, zo[p]);
-        }
-    }
     // l: each lane group g summed its own keys
+    float l = st.l;
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    if ((int)j < a.m && t_begin < t_end) {
+    if ((int)j < a.m) {
         float *rec = a.ws + ((head * a.chunks + chunk) * a.m + j) * kAttnRecord;
-        // accumulator row 4g + r of pair p is coordinate 32p + 8g + 2r (+1 for the odd tile)
-        const float zs = pow2i(ev - 14) * (1.0f / (float)kAD);
+        // accumulator row 4g + r of tile n is coordinate 32g + 8r + n
+        const float zs = pow2i(st.ev - 14) * (1.0f / (float)kAD);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
+        for (int r = 0; r < 4; ++r) {
             float4 lo, hi;
-            lo.x = ze[p][0] * zs; lo.y = zo[p][0] * zs; lo.z = ze[p][1] * zs; lo.w = zo[p][1] * zs;
-            hi.x = ze[p][2] * zs; hi.y = zo[p][2] * zs; hi.z = ze[p][3] * zs; hi.w = zo[p][3] * zs;
-            reinterpret_cast<float4 *>(rec + 32 * p + 8 * g)[0] = lo;
-            reinterpret_cast<float4 *>(rec + 32 * p + 8 * g)[1] = hi;
+            lo.x = st.z[0][r] * zs; lo.y = st.z[1][r] * zs; lo.z = st.z[2][r] * zs; lo.w = st.z[3][r] * zs;
+            hi.x = st.z[4][r] * zs; hi.y = st.z[5][r] * zs; hi.z = st.z[6][r] * zs; hi.w = st.z[7][r] * zs;
+            reinterpret_cast<float4 *>(rec + 32 * g + 8 * r)[0] = lo;
+            reinterpret_cast<float4 *>(rec + 32 * g + 8 * r)[1] = hi;
         }
         if (g == 0) {
-            rec[kAD] = M;
+            rec[kAD] = st.M;
             rec[kAD + 1] = l;
         }
     }
