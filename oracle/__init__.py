@@ -58,6 +58,10 @@ def lib():
         L.rho_f64_to_f16.restype = ctypes.c_uint16
         L.rho_lloyd_max.argtypes = [i32, vp, vp, vp, vp]
         L.rho_quantize.argtypes = [vp, i32, i64, i32, i32, u64, vp, vp, vp]
+        L.rho_score_sign.argtypes = [vp, i32, vp, vp, i64, i32, u64, vp]
+        L.rho_score_sign_dense.argtypes = [vp, i32, vp, vp, i64, i32, u64, vp]
+        L.rho_score_residual.argtypes = [vp, i32, vp, vp, vp, vp, i64, i32, i32, u64, vp]
+        L.rho_score_residual_dense.argtypes = [vp, i32, vp, vp, vp, vp, i64, i32, i32, u64, vp]
         for f in (L.rho_attention, L.rho_attention_rotated):
             f.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i32, i32, u64, u64, ctypes.c_double, vp]
         L.rho_dequantize.argtypes = [vp, vp, i64, i32, i32, u64, vp, i32]
@@ -266,3 +270,32 @@ def attention_rotated(q, kc, kn, vc, vn, d, bits, seed_k, seed_v, scale):
     sum kept rotated, one inverse transform per query (fp64)."""
     return _attention(lib().rho_attention_rotated, "attention_rotated", q, kc, kn, vc, vn, d, bits,
                       seed_k, seed_v, scale)
+
+
+def score_sign(q, bits, scale, d: int, seed: int, dense: bool = False):
+    """<q, x^> for sign-coded keys (either DRIVE scale): fp32 logits[m][n] on
+    the codes, or with dense=True the fp64 plain definition."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    bits = np.ascontiguousarray(bits, dtype=np.uint8)
+    scale = np.ascontiguousarray(scale, dtype=np.float32)
+    m, n = q.shape[0], scale.shape[0]
+    out = np.zeros((m, n), np.float64 if dense else np.float32)
+    fn = lib().rho_score_sign_dense if dense else lib().rho_score_sign
+    _check(fn(_p(q), m, _p(bits), _p(scale), n, d, seed, _p(out)), "score_sign")
+    return out
+
+
+def score_residual(q, codes, signs, norms, res_scale, d: int, bits: int, seed: int, dense: bool = False):
+    """<q, x^> for residual-chain-coded keys: fp32 logits[m][n] on the codes,
+    or with dense=True the fp64 plain definition."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    signs = np.ascontiguousarray(signs, dtype=np.uint8)
+    norms = np.ascontiguousarray(norms, dtype=np.float32)
+    res_scale = np.ascontiguousarray(res_scale, dtype=np.float32)
+    m, n = q.shape[0], norms.shape[0]
+    out = np.zeros((m, n), np.float64 if dense else np.float32)
+    fn = lib().rho_score_residual_dense if dense else lib().rho_score_residual
+    _check(fn(_p(q), m, _p(codes), _p(signs), _p(norms), _p(res_scale), n, d, bits, seed, _p(out)),
+           "score_residual")
+    return out

@@ -689,3 +689,149 @@ int rho_attention_rotated(const float *q, int m, const uint8_t *kc, const float 
     free(sk);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Inner products with sign-coded and residual-coded keys [RRQ decoders]
+ * (inner-product decoder: <q, x> from <Pi q, sign(Pi x)> with a normalizing
+ * scalar), [RRQ bias] (the residual chain restores unbiased inner products).
+ * Both are <q, x^> for the vector x^ the matching decoder returns; since
+ * Pi^T = D H / sqrt(d) and H is symmetric, <q, D H z> = <H D q, z>, so the
+ * query is rotated once and the codes are used as they are:
+ *   sign codes:  x^ = S D H sigma / sqrt(d)  ->  (S / sqrt(d)) <H D q, sigma>
+ *   residual:    x^ = D H (||x|| c / d + S_r sigma / sqrt(d))
+ *                ->  (||x|| / d) <H D q, c> + (S_r / sqrt(d)) <H D q, sigma>
+ * sigma_i = +1 for a set bit, -1 otherwise.  Logits [m][n], rounded to fp32. */
+static double *rotate_queries(const float *q, int m, int d, const int8_t *s)
+{
+    double *qt = (double *)malloc(sizeof(double) * (size_t)d * (size_t)(m > 0 ? m : 1));
+    int i, j;
+    for (j = 0; j < m; ++j) {
+        for (i = 0; i < d; ++i) qt[(int64_t)j * d + i] = s[i] * (double)q[(int64_t)j * d + i];
+        rho_fwht(qt + (int64_t)j * d, d);
+    }
+    return qt;
+}
+
+int rho_score_sign(const float *q, int m, const uint8_t *bits, const float *scale, int64_t n, int d,
+                   uint64_t seed, float *logits)
+{
+    int8_t *s;
+    double *qt;
+    int64_t k;
+    int i, j;
+    double rd = sqrt((double)d);
+    if (!valid_dim(d) || d < 8 || n < 0 || m < 0) return -1;
+    s = (int8_t *)malloc((size_t)d);
+    rho_signs(seed, d, s);
+    qt = rotate_queries(q, m, d, s);
+    for (k = 0; k < n; ++k) {
+        const uint8_t *brow = bits + k * (d / 8);
+        for (j = 0; j < m; ++j) {
+            double acc = 0.0;
+            for (i = 0; i < d; ++i)
+                acc += qt[(int64_t)j * d + i] * (get_field(brow, i, 1) ? 1.0 : -1.0);
+            logits[(int64_t)j * n + k] = (float)((double)scale[k] / rd * acc);
+        }
+    }
+    free(qt);
+    free(s);
+    return 0;
+}
+
+int rho_score_residual(const float *q, int m, const uint8_t *codes, const uint8_t *signs,
+                       const float *norms, const float *res_scale, int64_t n, int d, int bits,
+                       uint64_t seed, float *logits)
+{
+    double lv[16], th[15];
+    int8_t *s;
+    double *qt;
+    int64_t k;
+    int i, j, b1 = bits - 1;
+    double rd = sqrt((double)d);
+    if (!valid_dim(d) || d < 8 || bits < 2 || bits > 5 || n < 0 || m < 0) return -1;
+    if ((int64_t)b1 * d % 8) return -1;
+    rho_lloyd_max(b1, lv, th, NULL, NULL);
+    s = (int8_t *)malloc((size_t)d);
+    rho_signs(seed, d, s);
+    qt = rotate_queries(q, m, d, s);
+    for (k = 0; k < n; ++k) {
+        const uint8_t *crow = codes + k * (b1 * d / 8);
+        const uint8_t *srow = signs + k * (d / 8);
+        for (j = 0; j < m; ++j) {
+            double ac = 0.0, as = 0.0;
+            for (i = 0; i < d; ++i) {
+                ac += qt[(int64_t)j * d + i] * lv[get_field(crow, i, b1)];
+                as += qt[(int64_t)j * d + i] * (get_field(srow, i, 1) ? 1.0 : -1.0);
+            }
+            logits[(int64_t)j * n + k] =
+                (float)((double)norms[k] / d * ac + (double)res_scale[k] / rd * as);
+        }
+    }
+    free(qt);
+    free(s);
+    return 0;
+}
+
+/* The plain definitions: decode every key in fp64 with its decoder, then
+ * logits = Q * x^T in fp64 (no rounding of x^ or of the result).            */
+int rho_score_sign_dense(const float *q, int m, const uint8_t *bits, const float *scale, int64_t n,
+                         int d, uint64_t seed, double *logits)
+{
+    int8_t *s;
+    double *z;
+    int64_t k;
+    int i, j;
+    double rd = sqrt((double)d);
+    if (!valid_dim(d) || d < 8 || n < 0 || m < 0) return -1;
+    s = (int8_t *)malloc((size_t)d);
+    z = (double *)malloc(sizeof(double) * (size_t)d);
+    rho_signs(seed, d, s);
+    for (k = 0; k < n; ++k) {
+        const uint8_t *brow = bits + k * (d / 8);
+        for (i = 0; i < d; ++i) z[i] = get_field(brow, i, 1) ? 1.0 : -1.0;
+        rho_fwht(z, d);
+        for (i = 0; i < d; ++i) z[i] *= (double)scale[k] * s[i] / rd;
+        for (j = 0; j < m; ++j) {
+            double acc = 0.0;
+            for (i = 0; i < d; ++i) acc += (double)q[(int64_t)j * d + i] * z[i];
+            logits[(int64_t)j * n + k] = acc;
+        }
+    }
+    free(z);
+    free(s);
+    return 0;
+}
+
+int rho_score_residual_dense(const float *q, int m, const uint8_t *codes, const uint8_t *signs,
+                             const float *norms, const float *res_scale, int64_t n, int d, int bits,
+                             uint64_t seed, double *logits)
+{
+    double lv[16], th[15];
+    int8_t *s;
+    double *z;
+    int64_t k;
+    int i, j, b1 = bits - 1;
+    double rd = sqrt((double)d);
+    if (!valid_dim(d) || d < 8 || bits < 2 || bits > 5 || n < 0 || m < 0) return -1;
+    if ((int64_t)b1 * d % 8) return -1;
+    rho_lloyd_max(b1, lv, th, NULL, NULL);
+    s = (int8_t *)malloc((size_t)d);
+    z = (double *)malloc(sizeof(double) * (size_t)d);
+    rho_signs(seed, d, s);
+    for (k = 0; k < n; ++k) {
+        const uint8_t *crow = codes + k * (b1 * d / 8);
+        const uint8_t *srow = signs + k * (d / 8);
+        double a = (double)norms[k] / d, sr = (double)res_scale[k] / rd;
+        for (i = 0; i < d; ++i) z[i] = lv[get_field(crow, i, b1)] * a + (get_field(srow, i, 1) ? sr : -sr);
+        rho_fwht(z, d);
+        for (i = 0; i < d; ++i) z[i] *= s[i];
+        for (j = 0; j < m; ++j) {
+            double acc = 0.0;
+            for (i = 0; i < d; ++i) acc += (double)q[(int64_t)j * d + i] * z[i];
+            logits[(int64_t)j * n + k] = acc;
+        }
+    }
+    free(z);
+    free(s);
+    return 0;
+}

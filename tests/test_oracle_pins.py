@@ -486,3 +486,66 @@ def test_attention_key_permutation_and_value_scaling():
     # swapping the key and value seeds changes the result
     other = oracle.attention_rotated(q, kc, kn, vc, vn, d, bits, 42, 41, 0.3)
     assert np.abs(other - base).max() > 1e-3 * np.abs(base).max()
+
+
+# ------------------------------------------------- sign and residual scoring
+@pytest.mark.parametrize("d", [8, 64, 256])
+@pytest.mark.parametrize("unbiased", [False, True])
+def test_sign_score_equals_definition_and_decoder(d, unbiased):
+    rng = np.random.default_rng(d + unbiased)
+    x = rng.standard_normal((50, d)).astype(np.float32)
+    q = rng.standard_normal((7, d)).astype(np.float32)
+    b, S = oracle.sign_quantize(x, unbiased, 17)
+    rot = oracle.score_sign(q, b, S, d, 17).astype(np.float64)
+    dense = oracle.score_sign(q, b, S, d, 17, dense=True)
+    np.testing.assert_allclose(rot, dense, rtol=2e-7, atol=2e-7 * np.abs(dense).max())
+    # the dense definition against the (separately pinned) mean decoder
+    xh = oracle.sign_dequantize(b, S, d, 17).astype(np.float64)
+    np.testing.assert_allclose(dense, q.astype(np.float64) @ xh.T, rtol=1e-6, atol=1e-6 * np.abs(dense).max())
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("d", [16, 128])
+def test_residual_score_equals_definition_and_decoder(bits, d):
+    rng = np.random.default_rng(bits * d)
+    x = rng.standard_normal((40, d)).astype(np.float32)
+    q = rng.standard_normal((5, d)).astype(np.float32)
+    c, g, nr, rs = oracle.residual_quantize(x, bits, 23)
+    rot = oracle.score_residual(q, c, g, nr, rs, d, bits, 23).astype(np.float64)
+    dense = oracle.score_residual(q, c, g, nr, rs, d, bits, 23, dense=True)
+    np.testing.assert_allclose(rot, dense, rtol=2e-7, atol=2e-7 * np.abs(dense).max())
+    xh = oracle.residual_dequantize(c, g, nr, rs, d, bits, 23).astype(np.float64)
+    np.testing.assert_allclose(dense, q.astype(np.float64) @ xh.T, rtol=1e-6, atol=1e-6 * np.abs(dense).max())
+
+
+def test_inner_product_bias_harness():
+    # Monte Carlo over rotation seeds ("Bias vs unbiasedness"; "Three decoders"):
+    # DRIVE's unbiased scale gives mean <q, x^> = <q, x>; the biased scale and
+    # the MSE codes shrink it, the MSE codes by about 1 - D_b (centroid rule);
+    # the residual chain (reading: same rotation, S_r = ||r||^2 / ||r||_1)
+    # shrinks less than its own stage-1 code.
+    rng = np.random.default_rng(1)
+    d, seeds = 64, range(1500)
+    x = rng.standard_normal((1, d)).astype(np.float32)
+    q = (x + 0.5 * rng.standard_normal((1, d))).astype(np.float32)
+    true = float(x[0].astype(np.float64) @ q[0].astype(np.float64))
+    est = {k: [] for k in ("unb", "bia", "mse1", "mse2", "res2", "res3")}
+    for s in seeds:
+        b, S = oracle.sign_quantize(x, True, s)
+        est["unb"].append(oracle.score_sign(q, b, S, d, s)[0, 0])
+        b, S = oracle.sign_quantize(x, False, s)
+        est["bia"].append(oracle.score_sign(q, b, S, d, s)[0, 0])
+        for bb in (1, 2):
+            c, nr = oracle.quantize(x, bb, s)
+            est["mse%d" % bb].append(oracle.score(q, c, nr, d, bb, s)[0, 0])
+        for bb in (2, 3):
+            c, g, nr, rs = oracle.residual_quantize(x, bb, s)
+            est["res%d" % bb].append(oracle.score_residual(q, c, g, nr, rs, d, bb, s)[0, 0])
+    r = {k: np.mean(v) / true for k, v in est.items()}
+    se = {k: np.std(v) / np.sqrt(len(v)) / true for k, v in est.items()}
+    assert abs(r["unb"] - 1) < 5 * se["unb"], (r["unb"], se["unb"])
+    assert r["bia"] < 0.75
+    for bb in (1, 2):
+        assert abs(r["mse%d" % bb] - (1 - oracle.lloyd_max(bb)[2])) < 0.02 + 5 * se["mse%d" % bb]
+    assert r["mse1"] < r["res2"] < 1 - 5 * se["res2"]
+    assert r["mse2"] < r["res3"] < 1 - 5 * se["res3"]
