@@ -206,6 +206,30 @@ def other_workloads(torch, rht, dev, stream):
                                "keys_per_s": nk / (sms / 1e3), "TFLOP_per_s": tfs,
                                "frac_of_fp32_mfma_peak": tfs / 157.3, "GB_per_s": sbytes / (sms / 1e3) / 1e9,
                                "bound": "mfma fp32 (157.3 TFLOP/s)"})
+    del cs, ns, ls
+
+    # the same keys as 1-bit sign codes (unbiased scale) and as a 2+1-bit residual chain
+    bsg, ssg = rht.quantize(keys, 1, wk.rot_seed, mode=rht.SCALE_SIGN_UNBIASED)
+    rc, rg, rn, rr = rht.residual_quantize(keys, 3, wk.rot_seed)
+    sets_b = [(bsg.clone(), ssg.clone()) for _ in range(sets)]
+    sets_r = [(rc.clone(), rg.clone(), rn.clone(), rr.clone()) for _ in range(sets)]
+    ls = [torch.empty((m, nk), dtype=torch.float32, device=dev) for _ in range(sets)]
+    for name, fn, key_bytes in (
+            ("score_sign", lambda i: rht.rht_score_sign(q.data_ptr(), m, sets_b[i][0].data_ptr(),
+                                                        sets_b[i][1].data_ptr(), nk, d5, wk.rot_seed,
+                                                        ls[i].data_ptr(), sh), d5 // 8 + 4),
+            ("score_residual", lambda i: rht.rht_residual_score(
+                q.data_ptr(), m, sets_r[i][0].data_ptr(), sets_r[i][1].data_ptr(), sets_r[i][2].data_ptr(),
+                sets_r[i][3].data_ptr(), nk, d5, 3, wk.rot_seed, ls[i].data_ptr(), sh), 3 * d5 // 8 + 8)):
+        st = stats(time_launches(torch, stream, fn, sets))
+        ms = st["ms_median"]
+        tfs = flops / (ms / 1e3) / 1e12
+        out[name] = dict(st, **{"workload": "131072 keys d=128 %s, 64 fp32 queries, fp32 logits" % (
+                                    "1-bit sign codes + S" if name == "score_sign" else "2-bit codes + sign plane + 2 scales"),
+                                "keys_per_s": nk / (ms / 1e3), "TFLOP_per_s": tfs,
+                                "frac_of_fp32_mfma_peak": tfs / 157.3,
+                                "GB_per_s": (nk * key_bytes + m * d5 * 4 + m * nk * 4) / (ms / 1e3) / 1e9,
+                                "bound": "mfma fp32 (157.3 TFLOP/s)"})
     return out
 
 

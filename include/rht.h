@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define RHT_ABI_VERSION 2
+#define RHT_ABI_VERSION 3
 
 typedef enum {
     RHT_OK = 0,
@@ -122,6 +122,29 @@ rht_status rht_residual_dequantize(const uint8_t *codes, const uint8_t *signs, c
  *   logits [m][n] fp32 written.  d in {64, 128, 256}; bits 1..4. */
 rht_status rht_score(const float *q, int32_t m, const uint8_t *codes, const float *norms, int64_t n,
                      int32_t d, int32_t bits, uint64_t seed, float *logits, void *stream);
+
+/* Inner products with sign-coded keys ("Three decoders, one rotation",
+ * inner-product decoder: <q, x> from <Pi q, sign(Pi x)> with a normalizing
+ * scalar).  For bits and S written by rht_quantize(..., RHT_SCALE_SIGN_BIASED
+ * or RHT_SCALE_SIGN_UNBIASED, seed, ...) with bits = 1, the logits are the
+ * inner products with the mean decoder's vectors, x^ = S D H sigma / sqrt(d):
+ *   logits[j][k] = (S_k / sqrt(d)) * sum_i (H D q_j)_i sigma_{k,i},  sigma = +-1.
+ * With the unbiased scale their mean over rotation seeds is <q_j, x_k>.
+ *   q [m][d] fp32, 0 <= m <= 64; bits [n][d/8]; scale [n] fp32;
+ *   logits [m][n] fp32 written.  d in {64, 128, 256}. */
+rht_status rht_score_sign(const float *q, int32_t m, const uint8_t *bits, const float *scale, int64_t n,
+                          int32_t d, uint64_t seed, float *logits, void *stream);
+
+/* Inner products with residual-chain-coded keys ("History", TurboQuant item;
+ * "Bias vs unbiasedness": b-1 bit MSE code plus a 1-bit code of the residual):
+ *   logits[j][k] = (||x_k|| / d) sum_i (H D q_j)_i c[code_{k,i}]
+ *                + (S_r,k / sqrt(d)) sum_i (H D q_j)_i sigma_{k,i}
+ * = <q_j, x^_k> for the vectors rht_residual_dequantize returns.  Arguments
+ * as written by rht_residual_quantize (total bits 2..4); q [m][d] fp32,
+ * 0 <= m <= 64; logits [m][n] fp32 written; d in {64, 128, 256}. */
+rht_status rht_residual_score(const float *q, int32_t m, const uint8_t *codes, const uint8_t *signs,
+                              const float *norms, const float *res_scale, int64_t n, int32_t d, int32_t bits,
+                              uint64_t seed, float *logits, void *stream);
 
 /* Attention over MSE-coded keys and values, computed in the rotated domains
  * (page "Attn-rot: TurboQuant lite in llama.cpp", opening section: the keys

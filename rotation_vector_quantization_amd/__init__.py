@@ -35,7 +35,7 @@ _LIB_PATH = os.path.join(_HERE, "librht.so")
 
 F32, F16 = 0, 1
 SCALE_NORM, SCALE_SIGN_BIASED, SCALE_SIGN_UNBIASED = 0, 1, 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _lib = None
 
@@ -65,6 +65,8 @@ def load():
     L.rht_residual_quantize.argtypes = [vp, i32, i64, i32, i32, u64, vp, vp, vp, vp, vp]
     L.rht_residual_dequantize.argtypes = [vp, vp, vp, vp, i64, i32, i32, u64, vp, i32, vp]
     L.rht_score.argtypes = [vp, i32, vp, vp, i64, i32, i32, u64, vp, vp]
+    L.rht_score_sign.argtypes = [vp, i32, vp, vp, i64, i32, u64, vp, vp]
+    L.rht_residual_score.argtypes = [vp, i32, vp, vp, vp, vp, i64, i32, i32, u64, vp, vp]
     L.rht_attention.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i32, i32, u64, u64, ctypes.c_float,
                                 vp, vp, ctypes.c_size_t, vp]
     L.rht_attention_workspace_bytes.argtypes = [i64, i32, i64, i32]
@@ -75,7 +77,8 @@ def load():
     L.rht_status_str.restype = ctypes.c_char_p
     L.rht_abi_version.restype = i32
     for f in ("rht_quantize", "rht_dequantize", "rht_residual_quantize", "rht_residual_dequantize",
-              "rht_score", "rht_attention", "rht_codebook", "rht_signs"):
+              "rht_score", "rht_score_sign", "rht_residual_score", "rht_attention", "rht_codebook",
+              "rht_signs"):
         getattr(L, f).restype = i32
     if L.rht_abi_version() != ABI_VERSION:
         raise ImportError("librht ABI %d, binding expects %d" % (L.rht_abi_version(), ABI_VERSION))
@@ -110,6 +113,15 @@ def rht_residual_dequantize(codes, signs, norms, res_scale, n, d, bits, seed, y,
 
 def rht_score(q, m, codes, norms, n, d, bits, seed, logits, stream=0):
     _ok(load().rht_score(q, m, codes, norms, n, d, bits, seed, logits, stream), "rht_score")
+
+
+def rht_score_sign(q, m, bits, scale, n, d, seed, logits, stream=0):
+    _ok(load().rht_score_sign(q, m, bits, scale, n, d, seed, logits, stream), "rht_score_sign")
+
+
+def rht_residual_score(q, m, codes, signs, norms, res_scale, n, d, bits, seed, logits, stream=0):
+    _ok(load().rht_residual_score(q, m, codes, signs, norms, res_scale, n, d, bits, seed, logits, stream),
+        "rht_residual_score")
 
 
 def rht_attention(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, bits, seed_k, seed_v, scale,
@@ -235,6 +247,28 @@ def score(q, codes, norms, d: int, bits: int, seed: int):
     logits = torch.empty((m, n), dtype=torch.float32, device=q.device)
     rht_score(q.data_ptr(), m, codes.data_ptr(), norms.data_ptr(), n, d, bits, seed,
               logits.data_ptr(), _stream(q.device))
+    return logits
+
+
+def score_sign(q, bits, scale, d: int, seed: int):
+    """q [m][d] fp32 (m <= 64) against sign-coded keys -> logits fp32 [m][n]."""
+    torch = _torch()
+    _check_gpu(q, bits, scale)
+    m, n = q.shape[0], scale.shape[0]
+    logits = torch.empty((m, n), dtype=torch.float32, device=q.device)
+    rht_score_sign(q.data_ptr(), m, bits.data_ptr(), scale.data_ptr(), n, d, seed, logits.data_ptr(),
+                   _stream(q.device))
+    return logits
+
+
+def residual_score(q, codes, signs, norms, res_scale, d: int, bits: int, seed: int):
+    """q [m][d] fp32 (m <= 64) against residual-chain-coded keys -> logits fp32 [m][n]."""
+    torch = _torch()
+    _check_gpu(q, codes, signs, norms, res_scale)
+    m, n = q.shape[0], norms.shape[0]
+    logits = torch.empty((m, n), dtype=torch.float32, device=q.device)
+    rht_residual_score(q.data_ptr(), m, codes.data_ptr(), signs.data_ptr(), norms.data_ptr(),
+                       res_scale.data_ptr(), n, d, bits, seed, logits.data_ptr(), _stream(q.device))
     return logits
 
 

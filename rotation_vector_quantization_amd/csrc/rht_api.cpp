@@ -324,9 +324,60 @@ rht_status rht_score(const float *q, int32_t m, const uint8_t *codes, const floa
     a.norms = norms;
     a.logits = logits;
     a.n = n;
+    a.key_mult = 1.0f / (float)d;
     std::memcpy(a.lev, book(bits).lev, sizeof(a.lev));
     sign_words(seed, d, a.dsign);
-    return launched(launch_score(d, bits, a, (hipStream_t)stream));
+    return launched(launch_score(d, bits, false, a, (hipStream_t)stream));
+}
+
+rht_status rht_score_sign(const float *q, int32_t m, const uint8_t *bits, const float *scale, int64_t n,
+                          int32_t d, uint64_t seed, float *logits, void *stream) {
+    if (n < 0 || m < 0 || m > 64) return RHT_E_COUNT;
+    if (d != 64 && d != 128 && d != 256) return RHT_E_DIM;
+    if (n == 0 || m == 0) return RHT_OK;
+    if (!q || !bits || !scale || !logits) return RHT_E_NULL;
+    if (!aligned(q) || !aligned(bits) || !aligned(scale) || !aligned(logits)) return RHT_E_ALIGN;
+
+    ScoreArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.m = m;
+    a.codes = bits;
+    a.norms = scale;
+    a.logits = logits;
+    a.n = n;
+    a.key_mult = 1.0f / std::sqrt((float)d);
+    a.lev[0] = -1.0f;  // bit 0: the rotated coordinate was negative
+    a.lev[1] = 1.0f;
+    sign_words(seed, d, a.dsign);
+    return launched(launch_score(d, 1, false, a, (hipStream_t)stream));
+}
+
+rht_status rht_residual_score(const float *q, int32_t m, const uint8_t *codes, const uint8_t *signs,
+                              const float *norms, const float *res_scale, int64_t n, int32_t d, int32_t bits,
+                              uint64_t seed, float *logits, void *stream) {
+    if (n < 0 || m < 0 || m > 64) return RHT_E_COUNT;
+    if (d != 64 && d != 128 && d != 256) return RHT_E_DIM;
+    if (bits < 2 || bits > 4) return RHT_E_BITS;
+    if (n == 0 || m == 0) return RHT_OK;
+    if (!q || !codes || !signs || !norms || !res_scale || !logits) return RHT_E_NULL;
+    if (!aligned(q) || !aligned(codes) || !aligned(signs) || !aligned(norms) || !aligned(res_scale) ||
+        !aligned(logits))
+        return RHT_E_ALIGN;
+
+    ScoreArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.m = m;
+    a.codes = codes;
+    a.norms = norms;
+    a.signs = signs;
+    a.res_scale = res_scale;
+    a.logits = logits;
+    a.n = n;
+    std::memcpy(a.lev, book(bits - 1).lev, sizeof(a.lev));
+    sign_words(seed, d, a.dsign);
+    return launched(launch_score(d, bits - 1, true, a, (hipStream_t)stream));
 }
 
 size_t rht_attention_workspace_bytes(int64_t heads, int32_t m, int64_t n, int32_t d) {

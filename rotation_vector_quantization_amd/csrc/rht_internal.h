@@ -46,12 +46,15 @@ struct DequantArgs {
 
 struct ScoreArgs {
     const float *q;
-    const uint8_t *codes;
-    const float *norms;
+    const uint8_t *codes;    // MSE codes, sign bits, or the residual chain's stage-1 codes
+    const float *norms;      // ||x|| (MSE, residual) or S (sign codes)
+    const uint8_t *signs;    // residual sign plane
+    const float *res_scale;  // S_r
     float *logits;
     int64_t n;
     int m;
-    float lev[16];
+    float key_mult;          // per-key factor = norms[k] * key_mult (1/d, or 1/sqrt(d) for sign codes)
+    float lev[16];           // levels (sign codes: -1, +1)
     uint32_t dsign[kMaxD / 32];
 };
 
@@ -85,7 +88,9 @@ hipError_t launch_quantize(int d, bool f16, int bits, Kind kind, int layout, con
                            hipStream_t s);
 hipError_t launch_dequantize(int d, bool f16out, int bits, Kind kind, int layout,
                              const DequantArgs &a, hipStream_t s);
-hipError_t launch_score(int d, int bits, const ScoreArgs &a, hipStream_t s);
+// bits = code width of a.codes; residual: scores the chain of stage-1 codes
+// plus the sign plane.
+hipError_t launch_score(int d, int bits, bool residual, const ScoreArgs &a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
 
 // The d = 128, fp16, 4-bit MSE encoder and decoder with the H_32 factor on

@@ -713,10 +713,13 @@ __global__ __launch_bounds__(kBlock) void k_dequantize(const DequantArgs a) {
 
 // ---------------------------------------------------------------------------
 // Scoring on the codes in the rotated domain: logits = Qt * C^T scaled per key,
-// Qt = (H D Q^T)^T formed once per block into LDS, C[k][i] = c[code_{k,i}].
+// Qt = (H D Q^T)^T formed once per block into LDS, C[k][i] = c[code_{k,i}]
+// (MSE codes: Lloyd-Max levels, factor ||k|| / d; sign codes: +-1, factor
+// S / sqrt(d)).  RES: the residual chain, C[k][i] = (||k|| / d) c[code_{k,i}]
+// + (S_r / sqrt(d)) sigma_{k,i}, no further factor.
 // The contraction runs on v_mfma_f32_32x32x2_f32: per wave a 64-query x
 // 32-key tile (two 32x32 accumulators sharing the key operand).
-template <int D, int BITS>
+template <int D, int BITS, bool RES>
 __global__ __launch_bounds__(kBlock) void k_score(const ScoreArgs a) {
     constexpr int LPV = lanes_per_vec(D), E = D / LPV, VPW = 64 / LPV, VPB = kWaves * VPW;
     constexpr int QS = 96;  // LDS row stride of the transposed queries (bank spread)
@@ -750,25 +753,39 @@ __global__ __launch_bounds__(kBlock) void k_score(const ScoreArgs a) {
          tile += (int64_t)gridDim.x * kWaves) {
         const int64_t key = tile * 32 + col;
         const bool valid = key < a.n;
+        const int64_t row = valid ? key : a.n - 1;
         uint32_t w[ROWW];
-        load_words<ROWW>(reinterpret_cast<const uint32_t *>(a.codes) + (valid ? key : a.n - 1) * ROWW, w);
+        load_words<ROWW>(reinterpret_cast<const uint32_t *>(a.codes) + row * ROWW, w);
+        // residual chain: B element (||x|| / d) c[code] + (S_r / sqrt(d)) sigma, so the
+        // accumulator is the logit itself
+        uint32_t sw[RES ? D / 32 : 1];
+        float na = 0.0f, nb = 0.0f;
+        if constexpr (RES) {
+            load_words<D / 32>(reinterpret_cast<const uint32_t *>(a.signs) + row * (D / 32), sw);
+            na = a.norms[row] * (1.0f / D);
+            nb = a.res_scale[row] * (1.0f / __builtin_sqrtf((float)D));
+        }
         floatx16 acc0 = {}, acc1 = {};
 #pragma unroll
         for (int s = 0; s < D / 2; ++s) {
             const uint32_t c0 = get_code<BITS, ROWW>(w, 2 * s), c1 = get_code<BITS, ROWW>(w, 2 * s + 1);
-            const float b = slev[par ? c1 : c0];
             const int i = 2 * s + par;
+            float b = slev[par ? c1 : c0];
+            if constexpr (RES) {
+                const float sg = ((sw[i >> 5] >> (i & 31)) & 1u) ? nb : -nb;
+                b = fmaf(na, b, sg);
+            }
             const float a0 = qt[i * QS + col], a1 = qt[i * QS + 32 + col];
             acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b, acc0, 0, 0, 0);
             acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b, acc1, 0, 0, 0);
         }
         if (valid) {
-            const float sc = a.norms[key] * (1.0f / D);
+            const float sc = RES ? 1.0f : a.norms[key] * a.key_mult;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = 8 * (r / 4) + 4 * par + (r % 4);
-                if (row < a.m) a.logits[(int64_t)row * a.n + key] = acc0[r] * sc;
-                if (row + 32 < a.m) a.logits[(int64_t)(row + 32) * a.n + key] = acc1[r] * sc;
+                const int qrow = 8 * (r / 4) + 4 * par + (r % 4);
+                if (qrow < a.m) a.logits[(int64_t)qrow * a.n + key] = acc0[r] * sc;
+                if (qrow + 32 < a.m) a.logits[(int64_t)(qrow + 32) * a.n + key] = acc1[r] * sc;
             }
         }
     }
@@ -864,24 +881,32 @@ hipError_t dequant_d(bool f16, int bits, Kind kind, int layout, const DequantArg
     return hipErrorInvalidValue;
 }
 
-template <int D, int BITS>
+template <int D, int BITS, bool RES>
 hipError_t run_score(const ScoreArgs &a, hipStream_t s) {
     const int64_t tiles = (a.n + 31) / 32;
     int64_t blocks = (tiles + kWaves - 1) / kWaves;
     const int64_t cap = (int64_t)device_cu_count() * 2;
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL((k_score<D, BITS>), dim3((int)blocks), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((k_score<D, BITS, RES>), dim3((int)blocks), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t score_d(int bits, const ScoreArgs &a, hipStream_t s) {
+hipError_t score_d(int bits, bool residual, const ScoreArgs &a, hipStream_t s) {
+    if (residual) {
+        switch (bits) {
+        case 1: return run_score<D, 1, true>(a, s);
+        case 2: return run_score<D, 2, true>(a, s);
+        case 3: return run_score<D, 3, true>(a, s);
+        }
+        return hipErrorInvalidValue;
+    }
     switch (bits) {
-    case 1: return run_score<D, 1>(a, s);
-    case 2: return run_score<D, 2>(a, s);
-    case 3: return run_score<D, 3>(a, s);
-    case 4: return run_score<D, 4>(a, s);
+    case 1: return run_score<D, 1, false>(a, s);
+    case 2: return run_score<D, 2, false>(a, s);
+    case 3: return run_score<D, 3, false>(a, s);
+    case 4: return run_score<D, 4, false>(a, s);
     }
     return hipErrorInvalidValue;
 }
@@ -918,11 +943,11 @@ hipError_t launch_dequantize(int d, bool f16out, int bits, Kind kind, int layout
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_score(int d, int bits, const ScoreArgs &a, hipStream_t s) {
+hipError_t launch_score(int d, int bits, bool residual, const ScoreArgs &a, hipStream_t s) {
     switch (d) {
-    case 64: return score_d<64>(bits, a, s);
-    case 128: return score_d<128>(bits, a, s);
-    case 256: return score_d<256>(bits, a, s);
+    case 64: return score_d<64>(bits, residual, a, s);
+    case 128: return score_d<128>(bits, residual, a, s);
+    case 256: return score_d<256>(bits, residual, a, s);
     }
     return hipErrorInvalidValue;
 }

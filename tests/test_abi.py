@@ -33,13 +33,13 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for name in names:
         assert hasattr(lib, name), name
 
 
 def test_abi_version(lib):
-    assert rht.rht_abi_version() == 2
+    assert rht.rht_abi_version() == 3
     for s in range(10):
         assert isinstance(rht.rht_status_str(s), str) and rht.rht_status_str(s)
 
@@ -144,3 +144,21 @@ def test_attention_workspace_bytes(lib):
     assert rht.rht_attention_workspace_bytes(0, 4, 100, 128) == 0
     assert rht.rht_attention_workspace_bytes(1, 17, 100, 128) == 0
     assert rht.rht_attention_workspace_bytes(1, 4, 100, 64) == 0
+
+
+def test_sign_and_residual_score_validation(lib):
+    S = lib.rht_score_sign
+    assert S(FAKE, 65, FAKE, FAKE, 10, 128, 1, FAKE, None) == E_COUNT
+    assert S(FAKE, 4, FAKE, FAKE, -1, 128, 1, FAKE, None) == E_COUNT
+    assert S(FAKE, 4, FAKE, FAKE, 10, 32, 1, FAKE, None) == E_DIM
+    assert S(0, 0, 0, 0, 10, 128, 1, 0, None) == OK
+    assert S(FAKE, 4, 0, FAKE, 10, 128, 1, FAKE, None) == E_NULL
+    assert S(FAKE, 4, FAKE + 4, FAKE, 10, 128, 1, FAKE, None) == E_ALIGN
+    R = lib.rht_residual_score
+    assert R(FAKE, 65, FAKE, FAKE, FAKE, FAKE, 10, 128, 3, 1, FAKE, None) == E_COUNT
+    assert R(FAKE, 4, FAKE, FAKE, FAKE, FAKE, 10, 512, 3, 1, FAKE, None) == E_DIM
+    for b in (1, 5):
+        assert R(FAKE, 4, FAKE, FAKE, FAKE, FAKE, 10, 128, b, 1, FAKE, None) == E_BITS
+    assert R(FAKE, 4, FAKE, FAKE, FAKE, FAKE, 0, 128, 3, 1, FAKE, None) == OK
+    assert R(FAKE, 4, FAKE, 0, FAKE, FAKE, 10, 128, 3, 1, FAKE, None) == E_NULL
+    assert R(FAKE, 4, FAKE, FAKE, FAKE, FAKE + 8, 10, 128, 3, 1, FAKE, None) == E_ALIGN
