@@ -58,6 +58,7 @@ def lib():
         L.rho_f64_to_f16.restype = ctypes.c_uint16
         L.rho_lloyd_max.argtypes = [i32, vp, vp, vp, vp]
         L.rho_quantize.argtypes = [vp, i32, i64, i32, i32, u64, vp, vp, vp]
+        L.rho_quantize_eden.argtypes = [vp, i32, i64, i32, i32, u64, vp, vp]
         L.rho_score_sign.argtypes = [vp, i32, vp, vp, i64, i32, u64, vp]
         L.rho_score_sign_dense.argtypes = [vp, i32, vp, vp, i64, i32, u64, vp]
         L.rho_score_residual.argtypes = [vp, i32, vp, vp, vp, vp, i64, i32, i32, u64, vp]
@@ -154,6 +155,17 @@ def quantize(x: np.ndarray, bits: int, seed: int, want_y: bool = False):
     _check(lib().rho_quantize(_p(x), _dtype_code(x), n, d, bits, seed, _p(codes), _p(norms), _p(y)),
            "quantize")
     return (codes, norms, y) if want_y else (codes, norms)
+
+
+def quantize_eden(x: np.ndarray, bits: int, seed: int):
+    """MSE codes with the EDEN-style unbiased scale S = d ||x||^2 / <c, H D x>:
+    (codes u8[n][bits*d/8], S f32[n]); decode with dequantize()."""
+    x = np.ascontiguousarray(x)
+    n, d = x.shape
+    codes = np.zeros((n, bits * d // 8), np.uint8)
+    S = np.zeros(n, np.float32)
+    _check(lib().rho_quantize_eden(_p(x), _dtype_code(x), n, d, bits, seed, _p(codes), _p(S)), "quantize_eden")
+    return codes, S
 
 
 def dequantize(codes: np.ndarray, norms: np.ndarray, d: int, bits: int, seed: int,

@@ -305,6 +305,49 @@ int rho_quantize(const void *x, int dtype, int64_t n, int d, int bits, uint64_t 
     return 0;
 }
 
+/* EDEN-style unbiased scale for the MSE codes [RRQ EDEN], [RRQ bias]
+ * (reading: DRIVE's unbiased scale carried over to the Lloyd-Max code): the
+ * codes are the MSE encoder's; the stored scalar is the S that makes the
+ * decoder x^ = D H (c S / d) satisfy <x^, x> = ||x||^2,
+ *   S = d ||x||^2 / <c[code], H D x>   (0 when that inner product is 0).
+ * The MSE decoder (rho_dequantize) decodes it unchanged.                     */
+int rho_quantize_eden(const void *x, int dtype, int64_t n, int d, int bits, uint64_t seed,
+                      uint8_t *codes, float *scale)
+{
+    double lv[16], th[15];
+    int8_t *s;
+    double *h;
+    int64_t r;
+    int i, k, K, row_bytes;
+    if (!valid_dim(d) || bits < 1 || bits > 4 || n < 0) return -1;
+    if ((int64_t)bits * d % 8) return -1;
+    K = 1 << bits;
+    row_bytes = bits * d / 8;
+    rho_lloyd_max(bits, lv, th, NULL, NULL);
+    s = (int8_t *)malloc((size_t)d);
+    h = (double *)malloc(sizeof(double) * (size_t)d);
+    rho_signs(seed, d, s);
+    for (r = 0; r < n; ++r) {
+        double ss, nrm, ch = 0.0;
+        uint8_t *crow = codes + r * row_bytes;
+        rotate_row(x, dtype, r, d, s, h, &ss);
+        nrm = sqrt(ss);
+        memset(crow, 0, (size_t)row_bytes);
+        for (i = 0; i < d; ++i) {
+            double y = nrm > 0.0 ? h[i] / nrm : 0.0;
+            unsigned code = 0;
+            for (k = 0; k < K - 1; ++k)
+                if (y >= th[k]) ++code;
+            put_field(crow, i, bits, code);
+            ch += lv[code] * h[i];
+        }
+        scale[r] = (float)(ch != 0.0 ? d * ss / ch : 0.0);
+    }
+    free(h);
+    free(s);
+    return 0;
+}
+
 /* MSE decoder [RRQ decoders], [RRQ intro] step 3: x~ = Pi^T (c * ||x|| / sqrt(d))
  * = D H (c * ||x|| / d), from the stored bytes only.                         */
 int rho_dequantize(const uint8_t *codes, const float *norms, int64_t n, int d, int bits,

@@ -549,3 +549,50 @@ def test_inner_product_bias_harness():
         assert abs(r["mse%d" % bb] - (1 - oracle.lloyd_max(bb)[2])) < 0.02 + 5 * se["mse%d" % bb]
     assert r["mse1"] < r["res2"] < 1 - 5 * se["res2"]
     assert r["mse2"] < r["res3"] < 1 - 5 * se["res3"]
+
+
+# ---------------------------------------------------------------- EDEN scale
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("d", [16, 128])
+def test_eden_scale_closed_form(bits, d):
+    rng = np.random.default_rng(bits + d)
+    x = rng.standard_normal((30, d)).astype(np.float32)
+    x[0] = 0.0
+    c, S = oracle.quantize_eden(x, bits, 61)
+    c_mse, nr = oracle.quantize(x, bits, 61)
+    np.testing.assert_array_equal(c, c_mse)                      # same codes as the MSE encoder
+    assert S[0] == 0.0
+    # <x^, x> = ||x||^2 for the decoded vector (decoder output rounded to fp32)
+    xh = oracle.dequantize(c, S, d, bits, 61).astype(np.float64)
+    x64 = x.astype(np.float64)
+    np.testing.assert_allclose((xh * x64).sum(1)[1:], (x64 ** 2).sum(1)[1:], rtol=2e-6)
+    # and S relates to the MSE scale through the per-vector shrink <x~, x> / ||x||^2
+    xt = oracle.dequantize(c_mse, nr, d, bits, 61).astype(np.float64)
+    shrink = (xt * x64).sum(1)[1:] / (x64 ** 2).sum(1)[1:]
+    np.testing.assert_allclose(S[1:] * shrink, nr[1:], rtol=2e-6)
+
+
+def test_eden_one_bit_is_drive_unbiased():
+    rng = np.random.default_rng(77)
+    d = 64
+    x = rng.standard_normal((20, d)).astype(np.float32)
+    c, S = oracle.quantize_eden(x, 1, 5)
+    b, Sd = oracle.sign_quantize(x, True, 5)
+    np.testing.assert_array_equal(c, b)
+    np.testing.assert_allclose(oracle.dequantize(c, S, d, 1, 5), oracle.sign_dequantize(b, Sd, d, 5),
+                               rtol=1e-5, atol=1e-6)
+
+
+def test_eden_inner_products_unbiased_over_seeds():
+    rng = np.random.default_rng(1)
+    d, seeds = 64, range(1500)
+    x = rng.standard_normal((1, d)).astype(np.float32)
+    q = (x + 0.5 * rng.standard_normal((1, d))).astype(np.float32)
+    true = float(x[0].astype(np.float64) @ q[0].astype(np.float64))
+    for bits in (2, 3):
+        v = []
+        for s in seeds:
+            c, S = oracle.quantize_eden(x, bits, s)
+            v.append(oracle.score(q, c, S, d, bits, s)[0, 0])
+        r, se = np.mean(v) / true, np.std(v) / np.sqrt(len(v)) / true
+        assert abs(r - 1) < 5 * se + 2e-3, (bits, r, se)
