@@ -70,14 +70,21 @@ typedef enum {
        MSE-optimal).  bits must be 1. */
     RHT_SCALE_SIGN_BIASED = 1,
     /* Same bits, S = ||x||_2^2 / ||Pi x||_1 (unbiased; 0 when ||Pi x||_1 = 0). */
-    RHT_SCALE_SIGN_UNBIASED = 2
+    RHT_SCALE_SIGN_UNBIASED = 2,
+    /* EDEN-style unbiased scale for the MSE code ("History", EDEN item; "Bias
+       vs unbiasedness"): the codes of RHT_SCALE_NORM, scalar S = d ||x||^2 /
+       <c[code], H D x> (0 when that is 0), so the decoder's x^ = D H (c S / d)
+       has <x^, x> = ||x||^2.  bits 1..4; at 1 bit it equals the unbiased sign
+       code.  Decodes, scores and attends exactly like RHT_SCALE_NORM codes
+       with S in place of ||x||. */
+    RHT_SCALE_EDEN = 3
 } rht_mode;
 
 /* Encode n vectors.
  *   x      [n][d] elements of type xt (fp32 or fp16), read only.
  *   codes  [n][bits*d/8] bytes, written.
- *   scale  [n] fp32, written: ||x||_2 (RHT_SCALE_NORM) or S (sign modes).
- *   bits   1..4 for RHT_SCALE_NORM; exactly 1 for the sign modes.
+ *   scale  [n] fp32, written: ||x||_2 (RHT_SCALE_NORM) or S (sign modes, RHT_SCALE_EDEN).
+ *   bits   1..4 for RHT_SCALE_NORM and RHT_SCALE_EDEN; exactly 1 for the sign modes.
  * Passage: "intro" steps 1-2; "History" (EDEN normalization and Lloyd-Max
  * codebook; DRIVE signs and scale). */
 rht_status rht_quantize(const void *x, rht_dtype xt, int64_t n, int32_t d, int32_t bits,

@@ -23,7 +23,7 @@ import os
 import numpy as np
 
 __all__ = [
-    "RhtError", "F32", "F16", "SCALE_NORM", "SCALE_SIGN_BIASED", "SCALE_SIGN_UNBIASED",
+    "RhtError", "F32", "F16", "SCALE_NORM", "SCALE_SIGN_BIASED", "SCALE_SIGN_UNBIASED", "SCALE_EDEN",
     "library_path", "load", "rht_quantize", "rht_dequantize", "rht_residual_quantize",
     "rht_residual_dequantize", "rht_score", "rht_codebook", "rht_signs", "rht_status_str",
     "rht_abi_version", "quantize", "dequantize", "residual_quantize", "residual_dequantize",
@@ -34,7 +34,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "librht.so")
 
 F32, F16 = 0, 1
-SCALE_NORM, SCALE_SIGN_BIASED, SCALE_SIGN_UNBIASED = 0, 1, 2
+SCALE_NORM, SCALE_SIGN_BIASED, SCALE_SIGN_UNBIASED, SCALE_EDEN = 0, 1, 2, 3
 ABI_VERSION = 3
 
 _lib = None

@@ -207,9 +207,10 @@ rht_status rht_quantize(const void *x, rht_dtype xt, int64_t n, int32_t d, int32
     if (n < 0) return RHT_E_COUNT;
     if (!pow2_dim(d)) return RHT_E_DIM;
     if (bits < 1 || bits > 4) return RHT_E_BITS;
-    if (mode != RHT_SCALE_NORM && mode != RHT_SCALE_SIGN_BIASED && mode != RHT_SCALE_SIGN_UNBIASED)
+    if (mode != RHT_SCALE_NORM && mode != RHT_SCALE_SIGN_BIASED && mode != RHT_SCALE_SIGN_UNBIASED &&
+        mode != RHT_SCALE_EDEN)
         return RHT_E_MODE;
-    if (mode != RHT_SCALE_NORM && bits != 1) return RHT_E_MODE;
+    if ((mode == RHT_SCALE_SIGN_BIASED || mode == RHT_SCALE_SIGN_UNBIASED) && bits != 1) return RHT_E_MODE;
     if (xt != RHT_F32 && xt != RHT_F16) return RHT_E_DTYPE;
     if (n == 0) return RHT_OK;
     if (!x || !codes || !scale) return RHT_E_NULL;
@@ -225,7 +226,9 @@ rht_status rht_quantize(const void *x, rht_dtype xt, int64_t n, int32_t d, int32
     std::memcpy(a.lev, b.lev, sizeof(a.lev));
     std::memcpy(a.thr, b.thr, sizeof(a.thr));
     sign_words(seed, d, a.dsign);
-    const Kind kind = mode == RHT_SCALE_NORM ? kMse : (mode == RHT_SCALE_SIGN_BIASED ? kDriveBiased : kDriveUnbiased);
+    const Kind kind = mode == RHT_SCALE_NORM ? kMse
+                      : mode == RHT_SCALE_EDEN ? kEden
+                      : mode == RHT_SCALE_SIGN_BIASED ? kDriveBiased : kDriveUnbiased;
     return launched(launch_quantize(d, xt == RHT_F16, bits, kind, layout_choice(), a, (hipStream_t)stream));
 }
 
@@ -235,9 +238,10 @@ rht_status rht_dequantize(const uint8_t *codes, const float *scale, int64_t n, i
     if (n < 0) return RHT_E_COUNT;
     if (!pow2_dim(d)) return RHT_E_DIM;
     if (bits < 1 || bits > 4) return RHT_E_BITS;
-    if (mode != RHT_SCALE_NORM && mode != RHT_SCALE_SIGN_BIASED && mode != RHT_SCALE_SIGN_UNBIASED)
+    if (mode != RHT_SCALE_NORM && mode != RHT_SCALE_SIGN_BIASED && mode != RHT_SCALE_SIGN_UNBIASED &&
+        mode != RHT_SCALE_EDEN)
         return RHT_E_MODE;
-    if (mode != RHT_SCALE_NORM && bits != 1) return RHT_E_MODE;
+    if ((mode == RHT_SCALE_SIGN_BIASED || mode == RHT_SCALE_SIGN_UNBIASED) && bits != 1) return RHT_E_MODE;
     if (yt != RHT_F32 && yt != RHT_F16) return RHT_E_DTYPE;
     if (n == 0) return RHT_OK;
     if (!codes || !scale || !y) return RHT_E_NULL;
@@ -251,7 +255,9 @@ rht_status rht_dequantize(const uint8_t *codes, const float *scale, int64_t n, i
     a.n = n;
     std::memcpy(a.lev, book(bits).lev, sizeof(a.lev));
     sign_words(seed, d, a.dsign);
-    const Kind kind = mode == RHT_SCALE_NORM ? kMse : (mode == RHT_SCALE_SIGN_BIASED ? kDriveBiased : kDriveUnbiased);
+    // an EDEN scale decodes exactly like ||x||: x^ = D H (c * scale / d)
+    const Kind kind = (mode == RHT_SCALE_NORM || mode == RHT_SCALE_EDEN) ? kMse
+                      : mode == RHT_SCALE_SIGN_BIASED ? kDriveBiased : kDriveUnbiased;
     return launched(launch_dequantize(d, yt == RHT_F16, bits, kind, layout_choice(), a, (hipStream_t)stream));
 }
 

@@ -16,6 +16,7 @@ enum Kind : int {
     kDriveBiased,    // 1-bit signs + ||Pi x||_1 / d
     kDriveUnbiased,  // 1-bit signs + ||x||^2 / ||Pi x||_1
     kResidual,       // (b-1)-bit codes + residual signs + ||x|| + S_r
+    kEden,           // b-bit Lloyd-Max codes + S = d ||x||^2 / <c, H D x>
 };
 
 // Kernel arguments are passed by value (well under the 4 KiB kernarg limit).
@@ -25,7 +26,7 @@ struct QuantArgs {
     const void *x;
     uint8_t *codes;      // MSE / stage-1 codes, or the DRIVE sign bits
     uint8_t *signs;      // residual sign plane
-    float *scale;        // ||x|| (MSE, residual) or S (DRIVE)
+    float *scale;        // ||x|| (MSE, residual) or S (DRIVE, EDEN)
     float *res_scale;    // S_r (residual)
     int64_t n;
     float lev[16];       // fp32 Lloyd-Max levels of the code width

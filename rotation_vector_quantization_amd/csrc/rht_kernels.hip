@@ -389,10 +389,10 @@ __global__ __launch_bounds__(kBlock) void k_quantize(const QuantArgs a) {
     static_assert(KIND != kResidual || G % 32 == 0, "residual sign words need 32-coordinate groups");
     constexpr int ROWW = D * CB / 32;  // code words per row
 
-    constexpr bool RES = KIND == kResidual;
-    __shared__ uint2 lut[DRIVE || RES ? 1 : Lut<D>::kCells];
-    __shared__ u32x4_t lutl[RES ? Lut<D>::kCells : 1];
-    if constexpr (RES) {
+    constexpr bool RES = KIND == kResidual, EDEN = KIND == kEden;
+    __shared__ uint2 lut[DRIVE || RES || EDEN ? 1 : Lut<D>::kCells];
+    __shared__ u32x4_t lutl[RES || EDEN ? Lut<D>::kCells : 1];
+    if constexpr (RES || EDEN) {
         build_lut_lev<Lut<D>::kCells, Lut<D>::kOff>(lutl, a.thr, a.lev, (1 << CB) - 1);
         __syncthreads();
     } else if constexpr (!DRIVE) {
@@ -469,7 +469,7 @@ __global__ __launch_bounds__(kBlock) void k_quantize(const QuantArgs a) {
             const float inv16 = ss > 0.0f ? fq * (16.0f / nrm) : 0.0f;
             uint32_t w[NG][WPG];
             uint32_t sw[NG][RES ? G / 32 : 1];
-            float r2 = 0.0f, r1 = 0.0f;
+            float r2 = 0.0f, r1 = 0.0f, ch = 0.0f;
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
 #pragma unroll
@@ -495,13 +495,27 @@ __global__ __launch_bounds__(kBlock) void k_quantize(const QuantArgs a) {
                         // a zero vector has residual 0 everywhere, whose sign bit is +1
                         sw[gi][i] = ss > 0.0f ? ~neg : 0xFFFFFFFFu;
                     }
+                } else if constexpr (EDEN) {
+                    // <16 c[code], y16> = 256 <c, H D x> / ||x||
+#pragma unroll
+                    for (int t = 0; t < G; ++t) {
+                        const float y16 = v[gi * G + t] * inv16;
+                        float l16;
+                        put_code<CB, WPG>(w[gi], t, nearest_code_lev<D>(lutl, y16, l16));
+                        ch = fmaf(l16, y16, ch);
+                    }
                 } else {
 #pragma unroll
                     for (int t = 0; t < G; ++t)
                         put_code<CB, WPG>(w[gi], t, nearest_code<D>(lut, v[gi * G + t] * inv16));
                 }
             }
-            float sr = 0.0f;
+            float sr = 0.0f, se = 0.0f;
+            if constexpr (EDEN) {
+                // S = d ||x||^2 / <c, H D x> = d ||x|| * 256 / <16 c, y16>
+                ch = vec_sum<LPV>(ch);
+                se = ch > 0.0f ? (float)D * nrm * (256.0f / ch) : 0.0f;
+            }
             if constexpr (RES) {
                 r2 = vec_sum<LPV>(r2);
                 r1 = vec_sum<LPV>(r1);
@@ -519,7 +533,7 @@ __global__ __launch_bounds__(kBlock) void k_quantize(const QuantArgs a) {
                         store_words<G / 32>(sd + (gi * LPV + q) * (G / 32), sw[gi]);
                     if (q == 0) a.res_scale[vec] = sr;
                 }
-                if (q == 0) a.scale[vec] = nrm;
+                if (q == 0) a.scale[vec] = EDEN ? se : nrm;
             }
         }
     }
@@ -841,6 +855,14 @@ hipError_t quant_d(bool f16, int bits, Kind kind, int layout, const QuantArgs &a
         case 2: return f16 ? run_q<D, E, true, 2, kResidual>(a, s) : run_q<D, E, false, 2, kResidual>(a, s);
         case 3: return f16 ? run_q<D, E, true, 3, kResidual>(a, s) : run_q<D, E, false, 3, kResidual>(a, s);
         case 4: return f16 ? run_q<D, E, true, 4, kResidual>(a, s) : run_q<D, E, false, 4, kResidual>(a, s);
+        }
+        break;
+    case kEden:
+        switch (bits) {
+        case 1: return f16 ? run_q<D, E, true, 1, kEden>(a, s) : run_q<D, E, false, 1, kEden>(a, s);
+        case 2: return f16 ? run_q<D, E, true, 2, kEden>(a, s) : run_q<D, E, false, 2, kEden>(a, s);
+        case 3: return f16 ? run_q<D, E, true, 3, kEden>(a, s) : run_q<D, E, false, 3, kEden>(a, s);
+        case 4: return f16 ? run_q<D, E, true, 4, kEden>(a, s) : run_q<D, E, false, 4, kEden>(a, s);
         }
         break;
     }

@@ -73,7 +73,9 @@ def test_quantize_validation_order(lib):
         assert _q(lib, d=d) == E_DIM
     for b in (0, 5, -1):
         assert _q(lib, bits=b) == E_BITS
-    assert _q(lib, mode=3) == E_MODE
+    assert _q(lib, mode=4) == E_MODE
+    assert _q(lib, mode=-1) == E_MODE
+    assert _q(lib, mode=3, bits=4, x=0) == E_NULL               # EDEN accepts bits 1..4
     assert _q(lib, mode=1, bits=2) == E_MODE
     assert _q(lib, mode=2, bits=4) == E_MODE
     assert _q(lib, xt=2) == E_DTYPE
@@ -89,6 +91,8 @@ def test_other_entry_points_validate(lib):
     L = lib
     assert L.rht_dequantize(FAKE, FAKE, 1, 128, 4, 0, 1, FAKE, 5, None) == E_DTYPE
     assert L.rht_dequantize(FAKE, FAKE, 1, 128, 2, 1, 1, FAKE, 0, None) == E_MODE
+    assert L.rht_dequantize(FAKE, FAKE, 1, 128, 2, 4, 1, FAKE, 0, None) == E_MODE
+    assert L.rht_dequantize(0, FAKE, 1, 128, 3, 3, 1, FAKE, 0, None) == E_NULL
     assert L.rht_dequantize(0, FAKE, 1, 128, 4, 0, 1, FAKE, 0, None) == E_NULL
     assert L.rht_dequantize(FAKE, FAKE, 0, 128, 4, 0, 1, 0, 0, None) == OK
     assert L.rht_residual_quantize(FAKE, 0, 1, 128, 1, 1, FAKE, FAKE, FAKE, FAKE, None) == E_BITS

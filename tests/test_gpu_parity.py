@@ -100,6 +100,30 @@ def test_mse_roundtrip_grid(d, bits, xdt):
         check_recon(y, ref, tol, "dequant %s" % odt)
 
 
+# ------------------------------------------------------------------ EDEN scale
+@pytest.mark.parametrize("xdt", ["f32", "f16"])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("d", [32, 128, 256, 1024, 4096])
+def test_eden_grid(d, bits, xdt):
+    n = 555 if d <= 1024 else 131
+    seed = 3000 + d + bits
+    say("eden grid d=%d bits=%d x=%s n=%d" % (d, bits, xdt, n))
+    x = small_input(n, d, np_dtype(xdt), seed)
+    codes, S = gpu_quantize(x, bits, seed, rht.SCALE_EDEN)
+    ocodes, oS = oracle.quantize_eden(x, bits, seed)
+    _, th, _, _ = oracle.lloyd_max(bits)
+    gc, oc = unpack(codes, bits, d), unpack(ocodes, bits, d)
+    check_codes(gc, oc, lambda rows: oracle.quantize(x[rows], bits, seed, want_y=True)[2], th, "eden codes")
+    # S sums over every code of its row: compare it on rows whose codes all agree
+    same = (gc == oc).all(1)
+    check_rel(S[same], oS[same], SCALE_RTOL, "eden S")
+    assert S[0] == 0
+    for odt, tol in (("f32", RECON_F32), ("f16", RECON_F16)):
+        y = host(rht.dequantize(dev(codes), dev(S), d, bits, seed, rht.SCALE_EDEN, dtype=tdtype(odt)))
+        ref = oracle.dequantize(codes, S, d, bits, seed, np_dtype(odt))
+        check_recon(y, ref, tol, "eden decode %s" % odt)
+
+
 # ------------------------------------------------------------------ DRIVE
 @pytest.mark.parametrize("mode", [rht.SCALE_SIGN_BIASED, rht.SCALE_SIGN_UNBIASED])
 @pytest.mark.parametrize("xdt", ["f32", "f16"])
