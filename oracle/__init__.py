@@ -59,6 +59,9 @@ def lib():
         L.rho_lloyd_max.argtypes = [i32, vp, vp, vp, vp]
         L.rho_quantize.argtypes = [vp, i32, i64, i32, i32, u64, vp, vp, vp]
         L.rho_quantize_eden.argtypes = [vp, i32, i64, i32, i32, u64, vp, vp]
+        L.rho_lloyd_max_beta.argtypes = [i32, i32, vp, vp, vp, vp]
+        L.rho_quantize_cb.argtypes = [vp, i32, i64, i32, i32, u64, vp, vp, vp, vp, vp]
+        L.rho_dequantize_cb.argtypes = [vp, vp, i64, i32, i32, u64, vp, vp, i32]
         L.rho_score_sign.argtypes = [vp, i32, vp, vp, i64, i32, u64, vp]
         L.rho_score_sign_dense.argtypes = [vp, i32, vp, vp, i64, i32, u64, vp]
         L.rho_score_residual.argtypes = [vp, i32, vp, vp, vp, vp, i64, i32, i32, u64, vp]
@@ -143,6 +146,43 @@ def lloyd_max(bits: int):
     it = np.zeros(1, np.int32)
     _check(lib().rho_lloyd_max(bits, _p(lv), _p(th), _p(mse), _p(it)), "lloyd_max")
     return lv, th[: K - 1], float(mse[0]), int(it[0])
+
+
+def lloyd_max_beta(bits: int, d: int):
+    """(levels, thresholds, mse, iterations) of the Lloyd-Max codebook for the
+    exact marginal of sqrt(d) * (a coordinate of a uniformly rotated unit vector)."""
+    K = 1 << bits
+    lv = np.zeros(K, np.float64)
+    th = np.zeros(max(K - 1, 1), np.float64)
+    mse = np.zeros(1, np.float64)
+    it = np.zeros(1, np.int32)
+    _check(lib().rho_lloyd_max_beta(bits, d, _p(lv), _p(th), _p(mse), _p(it)), "lloyd_max_beta")
+    return lv, th[: K - 1], float(mse[0]), int(it[0])
+
+
+def quantize_cb(x: np.ndarray, bits: int, seed: int, levels, thresholds, want_y: bool = False):
+    """MSE encoder with the given codebook: (codes, norms[, y])."""
+    x = np.ascontiguousarray(x)
+    n, d = x.shape
+    lv = np.ascontiguousarray(levels, dtype=np.float64)
+    th = np.ascontiguousarray(thresholds, dtype=np.float64)
+    codes = np.zeros((n, bits * d // 8), np.uint8)
+    norms = np.zeros(n, np.float32)
+    y = np.zeros((n, d), np.float64) if want_y else None
+    _check(lib().rho_quantize_cb(_p(x), _dtype_code(x), n, d, bits, seed, _p(lv), _p(th), _p(codes), _p(norms),
+                                 _p(y)), "quantize_cb")
+    return (codes, norms, y) if want_y else (codes, norms)
+
+
+def dequantize_cb(codes, norms, d: int, bits: int, seed: int, levels, out_dtype=np.float32):
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    norms = np.ascontiguousarray(norms, dtype=np.float32)
+    lv = np.ascontiguousarray(levels, dtype=np.float64)
+    n = norms.shape[0]
+    oc = F16 if np.dtype(out_dtype) == np.float16 else F32
+    out = np.zeros((n, d), _np_out_dtype(oc))
+    _check(lib().rho_dequantize_cb(_p(codes), _p(norms), n, d, bits, seed, _p(lv), _p(out), oc), "dequantize_cb")
+    return out
 
 
 def quantize(x: np.ndarray, bits: int, seed: int, want_y: bool = False):

@@ -226,6 +226,88 @@ int rho_lloyd_max(int bits, double *levels, double *thresholds, double *mse, int
 }
 
 /* ------------------------------------------------------------------------ */
+/* Lloyd-Max codebook for the exact finite-d marginal [RRQ why]: a coordinate
+ * t of a uniformly rotated unit vector in R^d has density proportional to
+ * (1 - t^2)^((d-3)/2) on [-1, 1] (a Beta law), so y = sqrt(d) t (variance 1)
+ * has density proportional to (1 - y^2/d)^((d-3)/2) on [-sqrt(d), sqrt(d)].
+ * With y = sqrt(d) sin(theta) a cell [a, b) has mass proportional to the
+ * integral of cos(theta)^(d-2) over [asin(a/sqrt d), asin(b/sqrt d)) and first
+ * moment sqrt(d) * integral of sin(theta) cos(theta)^(d-2); both integrands
+ * are smooth, so composite Simpson's rule gives them to rounding.  Lloyd's
+ * fixed point as for N(0,1), started from the N(0,1) codebook.  d >= 2.     */
+static double beta_cell_integral(double ta, double tb, int d, int moment)
+{
+    /* |y| > 12 carries less than exp(-72) of the mass (the tails are lighter
+     * than the normal law's): clip there so the points sit where the mass is */
+    const int N = 4000; /* Simpson intervals per cell (even) */
+    const double tmax = asin(fmin(1.0, 12.0 / sqrt((double)d)));
+    double h, acc = 0.0;
+    int i;
+    ta = fmax(ta, -tmax);
+    tb = fmin(tb, tmax);
+    if (tb <= ta) return 0.0;
+    h = (tb - ta) / N;
+    for (i = 0; i <= N; ++i) {
+        double th = ta + h * i;
+        double f = pow(cos(th), (double)(d - 2)) * (moment ? sin(th) : 1.0);
+        acc += f * (i == 0 || i == N ? 1.0 : (i % 2 ? 4.0 : 2.0));
+    }
+    return acc * h / 3.0;
+}
+
+int rho_lloyd_max_beta(int bits, int d, double *levels, double *thresholds, double *mse, int *iters_out)
+{
+    double c[16], t[17], rd = sqrt((double)d), total;
+    int K, k, it;
+    if (bits < 1 || bits > 4 || d < 2) return -1;
+    K = 1 << bits;
+    rho_lloyd_max(bits, c, t + 1, NULL, NULL);
+    /* start inside the support [-sqrt(d), sqrt(d)] */
+    if (c[K - 1] >= 0.9 * rd)
+        for (k = 0; k < K; ++k) c[k] *= 0.9 * rd / c[K - 1];
+    total = beta_cell_integral(-RHO_PI / 2, RHO_PI / 2, d, 0);
+    for (it = 0; it < 100000; ++it) {
+        double delta = 0.0;
+        t[0] = -RHO_PI / 2;
+        t[K] = RHO_PI / 2;
+        for (k = 1; k < K; ++k) {
+            double m = 0.5 * (c[k - 1] + c[k]);
+            if (m < -rd) m = -rd;
+            if (m > rd) m = rd;
+            t[k] = asin(m / rd);
+        }
+        for (k = 0; k < K; ++k) {
+            double z = beta_cell_integral(t[k], t[k + 1], d, 0);
+            double m1 = rd * beta_cell_integral(t[k], t[k + 1], d, 1);
+            double nc = z > 0.0 ? m1 / z : c[k];
+            if (fabs(nc - c[k]) > delta) delta = fabs(nc - c[k]);
+            c[k] = nc;
+        }
+        if (delta < 1e-14) break;
+    }
+    /* symmetrize; the middle threshold is exactly 0 */
+    for (k = 0; k < K / 2; ++k) {
+        double a = 0.5 * (c[K - 1 - k] - c[k]);
+        c[k] = -a;
+        c[K - 1 - k] = a;
+    }
+    for (k = 0; k < K; ++k) levels[k] = c[k];
+    for (k = 1; k < K; ++k) thresholds[k - 1] = k == K / 2 ? 0.0 : 0.5 * (c[k - 1] + c[k]);
+    if (mse) {
+        /* E[(Y - c(Y))^2] = E[Y^2] - sum_k P_k c_k^2 = 1 - sum_k P_k c_k^2 (centroid rule) */
+        double acc = 0.0;
+        for (k = 0; k < K; ++k) {
+            double lo = k == 0 ? -RHO_PI / 2 : asin(fmax(-1.0, fmin(1.0, thresholds[k - 1] / rd)));
+            double hi = k == K - 1 ? RHO_PI / 2 : asin(fmax(-1.0, fmin(1.0, thresholds[k] / rd)));
+            acc += beta_cell_integral(lo, hi, d, 0) / total * c[k] * c[k];
+        }
+        *mse = 1.0 - acc;
+    }
+    if (iters_out) *iters_out = it;
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* bit packing: LSB-first bitstream, field i at bits [w*i, w*i + w)          */
 static void put_field(uint8_t *row, int i, int w, unsigned v)
 {
@@ -369,6 +451,71 @@ int rho_dequantize(const uint8_t *codes, const float *norms, int64_t n, int d, i
         const uint8_t *crow = codes + r * row_bytes;
         double scale = (double)norms[r] / d;
         for (i = 0; i < d; ++i) z[i] = lv[get_field(crow, i, bits)] * scale;
+        rho_fwht(z, d);
+        for (i = 0; i < d; ++i) store_elem(out, out_dtype, r * d + i, s[i] * z[i]);
+    }
+    free(z);
+    free(s);
+    return 0;
+}
+
+/* The MSE encoder and decoder with a codebook given by the caller (levels
+ * ascending, thresholds[k] between levels k and k+1): used for the exact
+ * finite-d codebook; identical to rho_quantize / rho_dequantize otherwise.   */
+int rho_quantize_cb(const void *x, int dtype, int64_t n, int d, int bits, uint64_t seed,
+                    const double *levels, const double *thresholds, uint8_t *codes, float *norms,
+                    double *y_out)
+{
+    int8_t *s;
+    double *h;
+    int64_t r;
+    int i, k, K, row_bytes;
+    (void)levels;
+    if (!valid_dim(d) || bits < 1 || bits > 4 || n < 0) return -1;
+    if ((int64_t)bits * d % 8) return -1;
+    K = 1 << bits;
+    row_bytes = bits * d / 8;
+    s = (int8_t *)malloc((size_t)d);
+    h = (double *)malloc(sizeof(double) * (size_t)d);
+    rho_signs(seed, d, s);
+    for (r = 0; r < n; ++r) {
+        double ss, nrm;
+        uint8_t *crow = codes + r * row_bytes;
+        rotate_row(x, dtype, r, d, s, h, &ss);
+        nrm = sqrt(ss);
+        memset(crow, 0, (size_t)row_bytes);
+        for (i = 0; i < d; ++i) {
+            double y = nrm > 0.0 ? h[i] / nrm : 0.0;
+            unsigned code = 0;
+            for (k = 0; k < K - 1; ++k)
+                if (y >= thresholds[k]) ++code;
+            put_field(crow, i, bits, code);
+            if (y_out) y_out[r * d + i] = y;
+        }
+        norms[r] = (float)nrm;
+    }
+    free(h);
+    free(s);
+    return 0;
+}
+
+int rho_dequantize_cb(const uint8_t *codes, const float *norms, int64_t n, int d, int bits, uint64_t seed,
+                      const double *levels, void *out, int out_dtype)
+{
+    int8_t *s;
+    double *z;
+    int64_t r;
+    int i, row_bytes;
+    if (!valid_dim(d) || bits < 1 || bits > 4 || n < 0) return -1;
+    if ((int64_t)bits * d % 8) return -1;
+    row_bytes = bits * d / 8;
+    s = (int8_t *)malloc((size_t)d);
+    z = (double *)malloc(sizeof(double) * (size_t)d);
+    rho_signs(seed, d, s);
+    for (r = 0; r < n; ++r) {
+        const uint8_t *crow = codes + r * row_bytes;
+        double scale = (double)norms[r] / d;
+        for (i = 0; i < d; ++i) z[i] = levels[get_field(crow, i, bits)] * scale;
         rho_fwht(z, d);
         for (i = 0; i < d; ++i) store_elem(out, out_dtype, r * d + i, s[i] * z[i]);
     }

@@ -596,3 +596,66 @@ def test_eden_inner_products_unbiased_over_seeds():
             v.append(oracle.score(q, c, S, d, bits, s)[0, 0])
         r, se = np.mean(v) / true, np.std(v) / np.sqrt(len(v)) / true
         assert abs(r - 1) < 5 * se + 2e-3, (bits, r, se)
+
+
+# ------------------------------------------------- exact finite-d codebooks
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_beta_codebook_d3_is_the_uniform_quantizer(bits):
+    # d = 3: a coordinate of a random unit vector is uniform on [-1, 1]
+    K = 1 << bits
+    lv, th, mse, _ = oracle.lloyd_max_beta(bits, 3)
+    r3 = math.sqrt(3.0)
+    np.testing.assert_allclose(lv, r3 * (-1 + (2 * np.arange(K) + 1) / K), atol=1e-10)
+    np.testing.assert_allclose(th, r3 * (-1 + 2 * np.arange(1, K) / K), atol=1e-10)
+    assert abs(mse - 1.0 / K ** 2) < 1e-10
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("d", [8, 64, 1024])
+def test_beta_codebook_fixed_point_by_scipy(bits, d):
+    # centroid and midpoint conditions under scipy's Beta law: (1 + y/sqrt d)/2 ~ Beta((d-1)/2, (d-1)/2);
+    # the density is log-concave, so the Lloyd-Max fixed point is unique
+    lv, th, mse, _ = oracle.lloyd_max_beta(bits, d)
+    a, sd = (d - 1) / 2.0, math.sqrt(d)
+    law = scipy.stats.beta(a, a)
+    pdf = lambda y: law.pdf((1 + y / sd) / 2) / (2 * sd)
+    edges = np.concatenate([[-sd], th, [sd]])
+    np.testing.assert_allclose(th, (lv[1:] + lv[:-1]) / 2, atol=1e-12)
+    err = 0.0
+    for k in range(len(lv)):
+        p = law.cdf((1 + edges[k + 1] / sd) / 2) - law.cdf((1 + edges[k] / sd) / 2)
+        m1 = scipy.integrate.quad(lambda y: y * pdf(y), edges[k], edges[k + 1], epsabs=1e-14, epsrel=1e-13)[0]
+        assert abs(m1 / p - lv[k]) < 1e-8, (k, m1 / p, lv[k])
+        err += scipy.integrate.quad(lambda y: (y - lv[k]) ** 2 * pdf(y), edges[k], edges[k + 1],
+                                    epsabs=1e-14, epsrel=1e-12)[0]
+    assert abs(err - mse) < 1e-8
+
+
+@pytest.mark.parametrize("d", [2, 5, 16, 128, 4096])
+def test_beta_codebook_one_bit_closed_form(d):
+    # 1 bit: the level is E|Y| = sqrt(d) E|t| = sqrt(d) Gamma(d/2) / (sqrt(pi) Gamma((d+1)/2))
+    lv = oracle.lloyd_max_beta(1, d)[0]
+    want = math.sqrt(d) * math.exp(math.lgamma(d / 2) - math.lgamma((d + 1) / 2)) / math.sqrt(math.pi)
+    np.testing.assert_allclose(lv, [-want, want], rtol=1e-11)
+
+
+def test_beta_codebook_tends_to_the_normal_one():
+    for bits in (1, 2, 3, 4):
+        g = oracle.lloyd_max(bits)[0]
+        b = oracle.lloyd_max_beta(bits, 1 << 16)[0]
+        assert np.abs(b - g).max() < 2e-4
+    # lighter tails at small d pull the outermost 3- and 4-bit levels in
+    for bits in (3, 4):
+        assert oracle.lloyd_max_beta(bits, 16)[0][-1] < oracle.lloyd_max(bits)[0][-1]
+
+
+def test_given_codebook_codec_matches_the_normal_codec():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((40, 64)).astype(np.float32)
+    for bits in (1, 3, 4):
+        lv, th, _, _ = oracle.lloyd_max(bits)
+        c, n = oracle.quantize(x, bits, 9)
+        cc, nn = oracle.quantize_cb(x, bits, 9, lv, th)
+        np.testing.assert_array_equal(c, cc)
+        np.testing.assert_array_equal(n, nn)
+        np.testing.assert_array_equal(oracle.dequantize(c, n, 64, bits, 9), oracle.dequantize_cb(c, n, 64, bits, 9, lv))
