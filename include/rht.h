@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define RHT_ABI_VERSION 3
+#define RHT_ABI_VERSION 4
 
 typedef enum {
     RHT_OK = 0,
@@ -77,7 +77,12 @@ typedef enum {
        has <x^, x> = ||x||^2.  bits 1..4; at 1 bit it equals the unbiased sign
        code.  Decodes, scores and attends exactly like RHT_SCALE_NORM codes
        with S in place of ||x||. */
-    RHT_SCALE_EDEN = 3
+    RHT_SCALE_EDEN = 3,
+    /* RHT_SCALE_NORM with the exact finite-d codebook ("Why rotation works":
+       a rotated coordinate follows a Beta law, not N(0,1)): the Lloyd-Max
+       quantizer of y = sqrt(d) t, (1 + t)/2 ~ Beta((d-1)/2, (d-1)/2), see
+       rht_codebook_beta.  bits 1..4; decode with the same mode. */
+    RHT_SCALE_NORM_BETA = 4
 } rht_mode;
 
 /* Encode n vectors.
@@ -188,6 +193,13 @@ size_t rht_attention_workspace_bytes(int64_t heads, int32_t m, int64_t n, int32_
  * levels[2^bits] ascending, thresholds[2^bits - 1] = midpoints of neighbouring
  * levels, the middle one exactly 0.  bits 1..4.  Either pointer may be NULL. */
 rht_status rht_codebook(int32_t bits, float *levels, float *thresholds);
+
+/* The fp32 exact finite-d codebook RHT_SCALE_NORM_BETA uses for (bits, d):
+ * the Lloyd-Max quantizer of sqrt(d) times a coordinate of a uniformly
+ * rotated unit vector ("Why rotation works": a Beta marginal), levels[2^bits]
+ * ascending, thresholds[2^bits - 1] midpoints, the middle one 0.  bits 1..4,
+ * d a power of two in [32, 4096].  Either pointer may be NULL. */
+rht_status rht_codebook_beta(int32_t bits, int32_t d, float *levels, float *thresholds);
 
 /* The diagonal D of the rotation for (seed, d): signs[i] = -1 when the top bit
  * of the i-th SplitMix64 output started from state `seed` is set, else +1.

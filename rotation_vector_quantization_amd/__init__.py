@@ -24,6 +24,7 @@ import numpy as np
 
 __all__ = [
     "RhtError", "F32", "F16", "SCALE_NORM", "SCALE_SIGN_BIASED", "SCALE_SIGN_UNBIASED", "SCALE_EDEN",
+    "SCALE_NORM_BETA",
     "library_path", "load", "rht_quantize", "rht_dequantize", "rht_residual_quantize",
     "rht_residual_dequantize", "rht_score", "rht_codebook", "rht_signs", "rht_status_str",
     "rht_abi_version", "quantize", "dequantize", "residual_quantize", "residual_dequantize",
@@ -34,8 +35,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "librht.so")
 
 F32, F16 = 0, 1
-SCALE_NORM, SCALE_SIGN_BIASED, SCALE_SIGN_UNBIASED, SCALE_EDEN = 0, 1, 2, 3
-ABI_VERSION = 3
+SCALE_NORM, SCALE_SIGN_BIASED, SCALE_SIGN_UNBIASED, SCALE_EDEN, SCALE_NORM_BETA = 0, 1, 2, 3, 4
+ABI_VERSION = 4
 
 _lib = None
 
@@ -72,13 +73,14 @@ def load():
     L.rht_attention_workspace_bytes.argtypes = [i64, i32, i64, i32]
     L.rht_attention_workspace_bytes.restype = ctypes.c_size_t
     L.rht_codebook.argtypes = [i32, vp, vp]
+    L.rht_codebook_beta.argtypes = [i32, i32, vp, vp]
     L.rht_signs.argtypes = [u64, i32, vp]
     L.rht_status_str.argtypes = [i32]
     L.rht_status_str.restype = ctypes.c_char_p
     L.rht_abi_version.restype = i32
     for f in ("rht_quantize", "rht_dequantize", "rht_residual_quantize", "rht_residual_dequantize",
               "rht_score", "rht_score_sign", "rht_residual_score", "rht_attention", "rht_codebook",
-              "rht_signs"):
+              "rht_codebook_beta", "rht_signs"):
         getattr(L, f).restype = i32
     if L.rht_abi_version() != ABI_VERSION:
         raise ImportError("librht ABI %d, binding expects %d" % (L.rht_abi_version(), ABI_VERSION))
@@ -141,6 +143,16 @@ def rht_codebook(bits: int):
     th = np.zeros(max(K - 1, 1), np.float32)
     _ok(load().rht_codebook(bits, lv.ctypes.data_as(ctypes.c_void_p), th.ctypes.data_as(ctypes.c_void_p)),
         "rht_codebook")
+    return lv, th[: K - 1]
+
+
+def rht_codebook_beta(bits: int, d: int):
+    """The exact finite-d codebook: (levels[2^bits], thresholds[2^bits - 1]) float32."""
+    K = 1 << bits
+    lv = np.zeros(K, np.float32)
+    th = np.zeros(max(K - 1, 1), np.float32)
+    _ok(load().rht_codebook_beta(bits, d, lv.ctypes.data_as(ctypes.c_void_p), th.ctypes.data_as(ctypes.c_void_p)),
+        "rht_codebook_beta")
     return lv, th[: K - 1]
 
 

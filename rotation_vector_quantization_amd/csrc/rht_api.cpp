@@ -56,25 +56,132 @@ void solve_half(int bits, double *p) {
     }
 }
 
+void fill_book(FloatBook &fb, int bits, const double *p);
+
 void build_books() {
     for (int bits = 1; bits <= 4; ++bits) {
         const int h = 1 << (bits - 1), K = 2 * h;
         double p[8];
         solve_half(bits, p);
-        FloatBook &fb = g_books[bits];
-        std::memset(&fb, 0, sizeof(fb));
-        for (int j = 0; j < h; ++j) {
-            fb.lev[h + j] = (float)p[j];
-            fb.lev[h - 1 - j] = (float)-p[j];
-        }
-        fb.thr[h - 1] = 0.0f;
-        for (int j = 1; j < h; ++j) {
-            const float t = (float)(0.5 * (p[j - 1] + p[j]));
-            fb.thr[h - 1 + j] = t;
-            fb.thr[h - 1 - j] = -t;
-        }
+        fill_book(g_books[bits], bits, p);
+        (void)h;
         (void)K;
     }
+}
+
+// Exact finite-d codebook ("Why rotation works": a coordinate t of a
+// uniformly rotated unit vector follows a Beta law, (1 + t)/2 ~
+// Beta((d-1)/2, (d-1)/2); the codebook is the Lloyd-Max quantizer of
+// y = sqrt(d) t).  Solved on the positive half-line like the N(0,1) one, with
+// cell masses from the regularized incomplete beta function and cell first
+// moments in closed form:
+//   integral of y f(y) over [y1, y2) = sqrt(d) / ((d-1) B(1/2, (d-1)/2))
+//       * ((1 - t1^2)^((d-1)/2) - (1 - t2^2)^((d-1)/2)),  t = y / sqrt(d).
+
+// Continued fraction of I_x(a, b) (Abramowitz and Stegun 26.5.8), evaluated
+// with the modified Lentz method; accurate for x < (a + 1) / (a + b + 2).
+double beta_cf(double a, double b, double x) {
+    const double tiny = 1e-300;
+    double c = 1.0, dd = 1.0 - (a + b) * x / (a + 1.0);
+    if (std::fabs(dd) < tiny) dd = tiny;
+    dd = 1.0 / dd;
+    double f = dd;
+    for (int m = 1; m < 10000; ++m) {
+        // even step: m (b - m) x / ((a + 2m - 1)(a + 2m))
+        double num = m * (b - m) * x / ((a + 2.0 * m - 1.0) * (a + 2.0 * m));
+        dd = 1.0 + num * dd;
+        c = 1.0 + num / c;
+        if (std::fabs(dd) < tiny) dd = tiny;
+        if (std::fabs(c) < tiny) c = tiny;
+        dd = 1.0 / dd;
+        f *= dd * c;
+        // odd step: -(a + m)(a + b + m) x / ((a + 2m)(a + 2m + 1))
+        num = -(a + m) * (a + b + m) * x / ((a + 2.0 * m) * (a + 2.0 * m + 1.0));
+        dd = 1.0 + num * dd;
+        c = 1.0 + num / c;
+        if (std::fabs(dd) < tiny) dd = tiny;
+        if (std::fabs(c) < tiny) c = tiny;
+        dd = 1.0 / dd;
+        const double step = dd * c;
+        f *= step;
+        if (std::fabs(step - 1.0) < 1e-16) break;
+    }
+    return f;
+}
+
+// Regularized incomplete beta I_x(a, a) for 0 <= x <= 1/2 (symmetric law).
+double inc_beta_sym(double a, double x) {
+    if (x <= 0.0) return 0.0;
+    const double lnpre = a * std::log(x) + a * std::log1p(-x) - std::log(a) -
+                         (2.0 * std::lgamma(a) - std::lgamma(2.0 * a));
+    return std::exp(lnpre) * beta_cf(a, a, x);
+}
+
+// P(Y >= y) for y >= 0 under the finite-d law.
+double beta_upper_tail(double y, int d) {
+    const double rd = std::sqrt((double)d);
+    if (y >= rd) return 0.0;
+    return inc_beta_sym(0.5 * (d - 1), 0.5 * (1.0 - y / rd));
+}
+
+// First-moment kernel (1 - t^2)^((d-1)/2) at y (0 beyond the support).
+double beta_moment_kernel(double y, int d) {
+    const double t = y / std::sqrt((double)d);
+    return t >= 1.0 ? 0.0 : std::exp(0.5 * (d - 1) * std::log1p(-t * t));
+}
+
+void solve_half_beta(int bits, int d, double *p) {
+    const int h = 1 << (bits - 1);
+    const double rd = std::sqrt((double)d);
+    // sqrt(d) / ((d-1) B(1/2, (d-1)/2))
+    const double mk = rd / (d - 1.0) *
+                      std::exp(std::lgamma(0.5 * d) - std::lgamma(0.5) - std::lgamma(0.5 * (d - 1)));
+    for (int j = 0; j < h; ++j) p[j] = std::fmin((j + 0.5) * 2.5 / h, 0.9 * rd);
+    for (int it = 0; it < 200000; ++it) {
+        double edges[9];
+        edges[0] = 0.0;
+        for (int j = 1; j < h; ++j) edges[j] = 0.5 * (p[j - 1] + p[j]);
+        edges[h] = rd;
+        double change = 0.0;
+        for (int j = 0; j < h; ++j) {
+            const double mass = beta_upper_tail(edges[j], d) - beta_upper_tail(edges[j + 1], d);
+            const double c = mk * (beta_moment_kernel(edges[j], d) - beta_moment_kernel(edges[j + 1], d)) / mass;
+            change = std::fmax(change, std::fabs(c - p[j]));
+            p[j] = c;
+        }
+        if (change < 1e-14) break;
+    }
+}
+
+void fill_book(FloatBook &fb, int bits, const double *p) {
+    const int h = 1 << (bits - 1);
+    std::memset(&fb, 0, sizeof(fb));
+    for (int j = 0; j < h; ++j) {
+        fb.lev[h + j] = (float)p[j];
+        fb.lev[h - 1 - j] = (float)-p[j];
+    }
+    fb.thr[h - 1] = 0.0f;
+    for (int j = 1; j < h; ++j) {
+        const float t = (float)(0.5 * (p[j - 1] + p[j]));
+        fb.thr[h - 1 + j] = t;
+        fb.thr[h - 1 - j] = -t;
+    }
+}
+
+constexpr int kLogMinD = 5, kLogMaxD = 12;
+FloatBook g_beta[5][kLogMaxD + 1];
+std::once_flag g_beta_once[5][kLogMaxD + 1];
+
+// The finite-d codebook for a supported (bits, d); computed once.
+const FloatBook &beta_book(int bits, int d) {
+    int lg = 0;
+    while ((1 << lg) < d) ++lg;
+    std::call_once(g_beta_once[bits][lg], [bits, d, lg] {
+        double p[8];
+        solve_half_beta(bits, d, p);
+        fill_book(g_beta[bits][lg], bits, p);
+    });
+    return g_beta[bits][lg];
 }
 
 const FloatBook &book(int bits) {
@@ -192,6 +299,15 @@ rht_status rht_codebook(int32_t bits, float *levels, float *thresholds) {
     return RHT_OK;
 }
 
+rht_status rht_codebook_beta(int32_t bits, int32_t d, float *levels, float *thresholds) {
+    if (bits < 1 || bits > 4) return RHT_E_BITS;
+    if (!pow2_dim(d)) return RHT_E_DIM;
+    const FloatBook &b = beta_book(bits, d);
+    if (levels) std::memcpy(levels, b.lev, sizeof(float) * (1u << bits));
+    if (thresholds) std::memcpy(thresholds, b.thr, sizeof(float) * ((1u << bits) - 1));
+    return RHT_OK;
+}
+
 rht_status rht_signs(uint64_t seed, int32_t d, int8_t *signs) {
     if (!signs) return RHT_E_NULL;
     if (d < 1 || d > (1 << 20)) return RHT_E_DIM;
@@ -208,7 +324,7 @@ rht_status rht_quantize(const void *x, rht_dtype xt, int64_t n, int32_t d, int32
     if (!pow2_dim(d)) return RHT_E_DIM;
     if (bits < 1 || bits > 4) return RHT_E_BITS;
     if (mode != RHT_SCALE_NORM && mode != RHT_SCALE_SIGN_BIASED && mode != RHT_SCALE_SIGN_UNBIASED &&
-        mode != RHT_SCALE_EDEN)
+        mode != RHT_SCALE_EDEN && mode != RHT_SCALE_NORM_BETA)
         return RHT_E_MODE;
     if ((mode == RHT_SCALE_SIGN_BIASED || mode == RHT_SCALE_SIGN_UNBIASED) && bits != 1) return RHT_E_MODE;
     if (xt != RHT_F32 && xt != RHT_F16) return RHT_E_DTYPE;
@@ -222,11 +338,11 @@ rht_status rht_quantize(const void *x, rht_dtype xt, int64_t n, int32_t d, int32
     a.codes = codes;
     a.scale = scale;
     a.n = n;
-    const FloatBook &b = book(bits);
+    const FloatBook &b = mode == RHT_SCALE_NORM_BETA ? beta_book(bits, d) : book(bits);
     std::memcpy(a.lev, b.lev, sizeof(a.lev));
     std::memcpy(a.thr, b.thr, sizeof(a.thr));
     sign_words(seed, d, a.dsign);
-    const Kind kind = mode == RHT_SCALE_NORM ? kMse
+    const Kind kind = (mode == RHT_SCALE_NORM || mode == RHT_SCALE_NORM_BETA) ? kMse
                       : mode == RHT_SCALE_EDEN ? kEden
                       : mode == RHT_SCALE_SIGN_BIASED ? kDriveBiased : kDriveUnbiased;
     return launched(launch_quantize(d, xt == RHT_F16, bits, kind, layout_choice(), a, (hipStream_t)stream));
@@ -239,7 +355,7 @@ rht_status rht_dequantize(const uint8_t *codes, const float *scale, int64_t n, i
     if (!pow2_dim(d)) return RHT_E_DIM;
     if (bits < 1 || bits > 4) return RHT_E_BITS;
     if (mode != RHT_SCALE_NORM && mode != RHT_SCALE_SIGN_BIASED && mode != RHT_SCALE_SIGN_UNBIASED &&
-        mode != RHT_SCALE_EDEN)
+        mode != RHT_SCALE_EDEN && mode != RHT_SCALE_NORM_BETA)
         return RHT_E_MODE;
     if ((mode == RHT_SCALE_SIGN_BIASED || mode == RHT_SCALE_SIGN_UNBIASED) && bits != 1) return RHT_E_MODE;
     if (yt != RHT_F32 && yt != RHT_F16) return RHT_E_DTYPE;
@@ -253,10 +369,10 @@ rht_status rht_dequantize(const uint8_t *codes, const float *scale, int64_t n, i
     a.scale = scale;
     a.y = y;
     a.n = n;
-    std::memcpy(a.lev, book(bits).lev, sizeof(a.lev));
+    std::memcpy(a.lev, (mode == RHT_SCALE_NORM_BETA ? beta_book(bits, d) : book(bits)).lev, sizeof(a.lev));
     sign_words(seed, d, a.dsign);
     // an EDEN scale decodes exactly like ||x||: x^ = D H (c * scale / d)
-    const Kind kind = (mode == RHT_SCALE_NORM || mode == RHT_SCALE_EDEN) ? kMse
+    const Kind kind = (mode == RHT_SCALE_NORM || mode == RHT_SCALE_EDEN || mode == RHT_SCALE_NORM_BETA) ? kMse
                       : mode == RHT_SCALE_SIGN_BIASED ? kDriveBiased : kDriveUnbiased;
     return launched(launch_dequantize(d, yt == RHT_F16, bits, kind, layout_choice(), a, (hipStream_t)stream));
 }

@@ -33,13 +33,13 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for name in names:
         assert hasattr(lib, name), name
 
 
 def test_abi_version(lib):
-    assert rht.rht_abi_version() == 3
+    assert rht.rht_abi_version() == 4
     for s in range(10):
         assert isinstance(rht.rht_status_str(s), str) and rht.rht_status_str(s)
 
@@ -73,7 +73,8 @@ def test_quantize_validation_order(lib):
         assert _q(lib, d=d) == E_DIM
     for b in (0, 5, -1):
         assert _q(lib, bits=b) == E_BITS
-    assert _q(lib, mode=4) == E_MODE
+    assert _q(lib, mode=5) == E_MODE
+    assert _q(lib, mode=4, bits=3, x=0) == E_NULL               # finite-d codebook, bits 1..4
     assert _q(lib, mode=-1) == E_MODE
     assert _q(lib, mode=3, bits=4, x=0) == E_NULL               # EDEN accepts bits 1..4
     assert _q(lib, mode=1, bits=2) == E_MODE
@@ -91,7 +92,7 @@ def test_other_entry_points_validate(lib):
     L = lib
     assert L.rht_dequantize(FAKE, FAKE, 1, 128, 4, 0, 1, FAKE, 5, None) == E_DTYPE
     assert L.rht_dequantize(FAKE, FAKE, 1, 128, 2, 1, 1, FAKE, 0, None) == E_MODE
-    assert L.rht_dequantize(FAKE, FAKE, 1, 128, 2, 4, 1, FAKE, 0, None) == E_MODE
+    assert L.rht_dequantize(FAKE, FAKE, 1, 128, 2, 5, 1, FAKE, 0, None) == E_MODE
     assert L.rht_dequantize(0, FAKE, 1, 128, 3, 3, 1, FAKE, 0, None) == E_NULL
     assert L.rht_dequantize(0, FAKE, 1, 128, 4, 0, 1, FAKE, 0, None) == E_NULL
     assert L.rht_dequantize(FAKE, FAKE, 0, 128, 4, 0, 1, 0, 0, None) == OK
@@ -166,3 +167,22 @@ def test_sign_and_residual_score_validation(lib):
     assert R(FAKE, 4, FAKE, FAKE, FAKE, FAKE, 0, 128, 3, 1, FAKE, None) == OK
     assert R(FAKE, 4, FAKE, 0, FAKE, FAKE, 10, 128, 3, 1, FAKE, None) == E_NULL
     assert R(FAKE, 4, FAKE, FAKE, FAKE, FAKE + 8, 10, 128, 3, 1, FAKE, None) == E_ALIGN
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("d", [32, 128, 1024, 4096])
+def test_beta_codebook_matches_oracle(lib, bits, d):
+    lv, th = rht.rht_codebook_beta(bits, d)
+    olv, oth, _, _ = oracle.lloyd_max_beta(bits, d)
+    # the library's solver (incomplete beta, closed-form moments) vs the oracle's (Simpson), in fp32
+    assert np.all(np.abs(lv - olv.astype(np.float32)) <= np.spacing(np.abs(olv).astype(np.float32)))
+    oth32 = oth.astype(np.float32)
+    assert np.all(np.abs(th - oth32) <= np.spacing(np.maximum(np.abs(oth32), np.float32(1e-30))))
+    assert th[len(th) // 2] == 0.0
+
+
+def test_beta_codebook_validation(lib):
+    f = lambda b, d: lib.rht_codebook_beta(b, d, None, None)
+    assert f(0, 128) == E_BITS and f(5, 128) == E_BITS
+    assert f(4, 100) == E_DIM and f(4, 16) == E_DIM and f(4, 8192) == E_DIM
+    assert f(4, 128) == OK

@@ -124,6 +124,28 @@ def test_eden_grid(d, bits, xdt):
         check_recon(y, ref, tol, "eden decode %s" % odt)
 
 
+# ------------------------------------------------------------------ finite-d codebook
+@pytest.mark.parametrize("xdt", ["f32", "f16"])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("d", [32, 128, 1024])
+def test_beta_codebook_grid(d, bits, xdt):
+    # d = 128, fp16, 4 bits runs the MFMA KV-block kernels with this codebook
+    n = 555
+    seed = 4000 + d + bits
+    say("finite-d codebook grid d=%d bits=%d x=%s" % (d, bits, xdt))
+    x = small_input(n, d, np_dtype(xdt), seed)
+    lv, th, _, _ = oracle.lloyd_max_beta(bits, d)
+    codes, norms = gpu_quantize(x, bits, seed, rht.SCALE_NORM_BETA)
+    ocodes, onorms = oracle.quantize_cb(x, bits, seed, lv, th)
+    check_codes(unpack(codes, bits, d), unpack(ocodes, bits, d),
+                lambda rows: oracle.quantize_cb(x[rows], bits, seed, lv, th, want_y=True)[2], th, "beta codes")
+    check_rel(norms, onorms, NORM_RTOL, "norms")
+    for odt, tol in (("f32", RECON_F32), ("f16", RECON_F16)):
+        y = host(rht.dequantize(dev(codes), dev(norms), d, bits, seed, rht.SCALE_NORM_BETA, dtype=tdtype(odt)))
+        ref = oracle.dequantize_cb(codes, norms, d, bits, seed, lv, np_dtype(odt))
+        check_recon(y, ref, tol, "beta decode %s" % odt)
+
+
 # ------------------------------------------------------------------ DRIVE
 @pytest.mark.parametrize("mode", [rht.SCALE_SIGN_BIASED, rht.SCALE_SIGN_UNBIASED])
 @pytest.mark.parametrize("xdt", ["f32", "f16"])
