@@ -220,11 +220,12 @@ int layout_choice() {
 
 rht_status launched(hipError_t e) { return e == hipSuccess ? RHT_OK : RHT_E_DEVICE; }
 
-// Key chunks per head for attention: enough (head, chunk) wavefronts to keep
-// every SIMD busy (about 4096), never more chunks than 32-key tiles.
+// Key chunks per head for attention: enough (head, chunk) wavefronts to fill
+// the chip once (256 CUs x 12 resident waves), never more chunks than 32-key
+// tiles.  A fixed count keeps the workspace size independent of the device.
 int64_t attention_chunks(int64_t heads, int64_t n) {
     const int64_t tiles = (n + 31) / 32;
-    int64_t c = (4096 + heads - 1) / heads;
+    int64_t c = (3072 + heads - 1) / heads;
     if (c > tiles) c = tiles;
     if (c > 1024) c = 1024;
     return c < 1 ? 1 : c;

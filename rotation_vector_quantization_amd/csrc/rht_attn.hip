@@ -37,6 +37,13 @@ namespace {
 constexpr int kAD = 128;           // coordinates per vector
 constexpr int kACodeBytes = 64;    // 4-bit codes per row
 constexpr int kVRow = 80;          // LDS row stride of a staged value tile (bank spread)
+// Blocks of RHT_ATTN_WAVES wavefronts share one copy of the level tables; one
+// block fills a CU up to the register limit (3 waves per SIMD).
+#ifndef RHT_ATTN_WAVES
+#define RHT_ATTN_WAVES 12
+#endif
+constexpr int kAWaves = RHT_ATTN_WAVES;
+constexpr int kABlock = 64 * kAWaves;
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
@@ -144,16 +151,17 @@ __device__ __forceinline__ void level_operands(const LevelTables &tb, uint32_t c
 // Logits of 16 keys (one 16-byte code piece per lane) against the queries.
 __device__ __forceinline__ floatx4 key_logits(const LevelTables &tb, uint32_t copy, u32x4_t kc,
                                               const u32x4_t (&bh)[4], const u32x4_t (&bl)[4]) {
-    floatx4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+    // two independent accumulation chains (even and odd K steps)
+    floatx4 c[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         u32x4_t ah, al;
         level_operands(tb, copy, kc[ks], ah, al);
-        c = mfma1632(ah, bh[ks], c);
-        c = mfma1632(ah, bl[ks], c);
-        c = mfma1632(al, bh[ks], c);
+        c[ks & 1] = mfma1632(ah, bh[ks], c[ks & 1]);
+        c[ks & 1] = mfma1632(ah, bl[ks], c[ks & 1]);
+        c[ks & 1] = mfma1632(al, bh[ks], c[ks & 1]);
     }
-    return c;
+    return c[0] + c[1];
 }
 
 // Transpose of an 8 x 8 matrix of nibbles: on entry nibble n of a[t] is
@@ -282,11 +290,11 @@ __device__ __forceinline__ void attend_tile(const LevelTables &tb, const uint8_t
     }
 }
 
-__global__ __launch_bounds__(kBlock) void k_attn_partial(const AttnArgs a) {
+__global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
     __shared__ LevelTables tb;
-    __shared__ __attribute__((aligned(16))) uint8_t vbuf[kWaves][32 * kVRow];
-    __shared__ __attribute__((aligned(16))) float nbuf[kWaves][64];
-    for (uint32_t k = threadIdx.x; k < 256u * kTabCopies; k += kBlock) {
+    __shared__ __attribute__((aligned(16))) uint8_t vbuf[kAWaves][32 * kVRow];
+    __shared__ __attribute__((aligned(16))) float nbuf[kAWaves][64];
+    for (uint32_t k = threadIdx.x; k < 256u * kTabCopies; k += kABlock) {
         const uint32_t v = k / kTabCopies;
         const uint2 e = split2(a.lev[v & 15u], a.lev[v >> 4]);
         tb.h[k] = e.x;
@@ -296,7 +304,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_partial(const AttnArgs a) {
 
     const uint32_t lane = lane_id(), j = lane & 15u, g = lane >> 4;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t gw = (int64_t)blockIdx.x * kWaves + wave;
+    const int64_t gw = (int64_t)blockIdx.x * kAWaves + wave;
     if (gw >= a.heads * a.chunks) return;  // whole wave; no block barrier follows
     const int64_t head = gw / a.chunks;
     const int chunk = (int)(gw % a.chunks);
@@ -447,7 +455,7 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(const AttnArgs a) {
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
     const int64_t waves = a.heads * a.chunks;
-    hipLaunchKernelGGL(k_attn_partial, dim3((unsigned)((waves + kWaves - 1) / kWaves)), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(k_attn_partial, dim3((unsigned)((waves + kAWaves - 1) / kAWaves)), dim3(kABlock), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t rows = a.heads * a.m;

@@ -145,7 +145,7 @@ def test_attention_workspace_bytes(lib):
     # one record of 132 floats per (head, chunk, query); chunks never exceed 32-key tiles
     assert rht.rht_attention_workspace_bytes(1, 1, 1, 128) == 132 * 4
     assert rht.rht_attention_workspace_bytes(2, 4, 100, 128) == 2 * 4 * 4 * 132 * 4
-    assert rht.rht_attention_workspace_bytes(256, 4, 32768, 128) == 256 * 16 * 4 * 132 * 4
+    assert rht.rht_attention_workspace_bytes(256, 4, 32768, 128) == 256 * 12 * 4 * 132 * 4
     assert rht.rht_attention_workspace_bytes(0, 4, 100, 128) == 0
     assert rht.rht_attention_workspace_bytes(1, 17, 100, 128) == 0
     assert rht.rht_attention_workspace_bytes(1, 4, 100, 64) == 0
