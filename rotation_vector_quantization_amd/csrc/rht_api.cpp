@@ -168,7 +168,7 @@ void fill_book(FloatBook &fb, int bits, const double *p) {
     }
 }
 
-constexpr int kLogMinD = 5, kLogMaxD = 12;
+constexpr int kLogMaxD = 12;
 FloatBook g_beta[5][kLogMaxD + 1];
 std::once_flag g_beta_once[5][kLogMaxD + 1];
 

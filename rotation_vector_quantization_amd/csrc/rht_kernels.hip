@@ -539,6 +539,177 @@ __global__ __launch_bounds__(kBlock) void k_quantize(const QuantArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Residual-chain encoder for d = 256, fp16 input, with the H_32 factor of the
+// transform on MFMA.  H_256 = H_8 (x) H_32 over the split e = 32 a + b (a is
+// the high index, Sylvester order).  A wave works on tiles of 16 vectors; for
+// each input block a' one v_mfma_f32_16x16x32_f16 per half computes
+// H_32 (D x)_{a'} with the 16 vectors as columns (K = 32 = the whole block):
+// lane l (vector j = l % 16, g = l / 16) supplies the fp16 coordinates
+// 32 a' + 8 g .. +8 of vector j (signs D applied by XOR), and the A rows are
+// permuted so that accumulator register r of half mh holds output coordinate
+// b = 8 g + 4 mh + r.  The H_8 factor is three add/sub stages across the eight
+// blocks in registers; lane (j, g) ends with coordinates 32 a + 8 g .. +8 of
+// vector j for every a: CB whole bytes of codes and one byte of signs per
+// block, staged through LDS into coalesced row stores.
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kR256Rows = 16;  // vectors per wave tile
+
+__device__ __forceinline__ floatx4 mfma16x16x32(u32x4_t a, u32x4_t b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c,
+                                                  0, 0, 0);
+}
+
+// Rows of a wave tile (16 x 256 fp16), lane (j, g): the 16-byte piece of row j
+// holding coordinates 32 a + 8 g .. +8, for every block a.  Rows past the end
+// repeat the last row.
+__device__ __forceinline__ void load_res256(const uint16_t *x, int64_t row0, int64_t n, uint32_t j, uint32_t g,
+                                            u32x4_t (&raw)[8]) {
+    const int64_t row = row0 + j < n ? row0 + j : n - 1;
+    const u32x4_t *p = reinterpret_cast<const u32x4_t *>(x + row * 256) + g;
+#pragma unroll
+    for (int a = 0; a < 8; ++a) raw[a] = p[4 * a];
+}
+
+template <int CB>
+__global__ __launch_bounds__(kBlock) void k_residual_quantize_mfma256(const QuantArgs a) {
+    constexpr int D = 256, VPB = kWaves * kR256Rows;
+    constexpr int CROW = D * CB / 8, SROW = D / 8;  // code and sign bytes per row
+    __shared__ u32x4_t lutl[Lut<D>::kCells];
+    __shared__ __attribute__((aligned(16))) uint8_t ctile[kWaves][kR256Rows * CROW];
+    __shared__ __attribute__((aligned(16))) uint8_t stile[kWaves][kR256Rows * SROW];
+    build_lut_lev<Lut<D>::kCells, Lut<D>::kOff>(lutl, a.thr, a.lev, (1 << CB) - 1);
+    __syncthreads();
+
+    const uint32_t lane = lane_id(), j = lane & 15u, g = lane >> 4;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // A operands: row rho = l % 16 of half mh is output coordinate b = 8 (rho / 4) + 4 mh + rho % 4,
+    // K index k = 8 g + t
+    u32x4_t A[2];
+#pragma unroll
+    for (int mh = 0; mh < 2; ++mh) {
+        const uint32_t b = 8u * (j >> 2) + 4u * mh + (j & 3u);
+        uint32_t w[4];
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+            const uint32_t k0 = 8u * g + t, k1 = k0 + 1;
+            w[t / 2] = ((__builtin_popcount(b & k0) & 1u) ? 0xBC00u : 0x3C00u) |
+                       (((__builtin_popcount(b & k1) & 1u) ? 0xBC00u : 0x3C00u) << 16);
+        }
+        A[mh] = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
+    // D as XOR masks on the fp16 sign bits of this lane's coordinates 32 a + 8 g + t
+    u32x4_t smask[8];
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+        const uint32_t bits8 = (a.dsign[blk] >> (8 * g)) & 0xFFu;
+        uint32_t w[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            w[p] = (((bits8 >> (2 * p)) & 1u) << 15) | (((bits8 >> (2 * p + 1)) & 1u) << 31);
+        smask[blk] = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
+    const float sqrt_d = 16.0f;
+    const uint16_t *x = static_cast<const uint16_t *>(a.x);
+    uint8_t *ct = ctile[wave];
+    uint8_t *st = stile[wave];
+
+    const int64_t stride = (int64_t)gridDim.x * VPB;
+    const int64_t first = (int64_t)blockIdx.x * VPB + wave * kR256Rows;
+    // the next tile's rows are in flight while this tile is rotated and quantized
+    u32x4_t raw[8], nxt[8];
+    if (first < a.n) load_res256(x, first, a.n, j, g, nxt);
+    for (int64_t v0 = first; v0 < a.n; v0 += stride) {
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) raw[blk] = nxt[blk];
+        if (v0 + stride < a.n) load_res256(x, v0 + stride, a.n, j, g, nxt);
+        // ||x||^2 of vector j from the fp16 data (this lane: 64 of its coordinates)
+        float ss = 0.0f, ss2 = 0.0f;
+        floatx4 c[8][2];
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                if (p & 1)
+                    ss2 = dot2(raw[blk][p], raw[blk][p], ss2);
+                else
+                    ss = dot2(raw[blk][p], raw[blk][p], ss);
+            }
+            const u32x4_t bsigned = raw[blk] ^ smask[blk];
+            c[blk][0] = mfma16x16x32(A[0], bsigned, floatx4{0.0f, 0.0f, 0.0f, 0.0f});
+            c[blk][1] = mfma16x16x32(A[1], bsigned, floatx4{0.0f, 0.0f, 0.0f, 0.0f});
+        }
+        ss += ss2;
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        // H_8 across the blocks
+#pragma unroll
+        for (int hs = 1; hs < 8; hs <<= 1)
+#pragma unroll
+            for (int blk = 0; blk < 8; ++blk)
+                if (!(blk & hs)) {
+#pragma unroll
+                    for (int mh = 0; mh < 2; ++mh) {
+                        const floatx4 u = c[blk][mh], v = c[blk + hs][mh];
+                        c[blk][mh] = u + v;
+                        c[blk + hs][mh] = u - v;
+                    }
+                }
+
+        const float nrm = sqrtf(ss);
+        const float inv16 = ss > 0.0f ? 16.0f / nrm : 0.0f;
+        float r2 = 0.0f, r1 = 0.0f;
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+            // coordinates 32 blk + 8 g + 4 mh + r, in order t = 4 mh + r
+            uint32_t code = 0u, neg = 0u;
+#pragma unroll
+            for (int t = 7; t >= 0; --t) {
+                const float y16 = c[blk][t >> 2][t & 3] * inv16;
+                float l16;
+                const uint32_t cd = nearest_code_lev<D>(lutl, y16, l16);
+                code |= cd << (CB * t);
+                const float rho = y16 - l16;
+                r2 = fmaf(rho, rho, r2);
+                r1 += fabsf(rho);
+                neg = (neg << 1) | (__builtin_bit_cast(uint32_t, rho) >> 31);
+            }
+            // a zero vector has residual 0 everywhere, whose sign bit is +1
+            const uint32_t sbits = ss > 0.0f ? (~neg & 0xFFu) : 0xFFu;
+            uint8_t *cp = ct + j * CROW + CB * (4 * blk + g);
+#pragma unroll
+            for (int by = 0; by < CB; ++by) cp[by] = (uint8_t)(code >> (8 * by));
+            st[j * SROW + 4 * blk + g] = (uint8_t)sbits;
+        }
+        r2 += __shfl_xor(r2, 16);
+        r2 += __shfl_xor(r2, 32);
+        r1 += __shfl_xor(r1, 16);
+        r1 += __shfl_xor(r1, 32);
+        const float sr = r1 > 0.0f ? (nrm * (1.0f / 16.0f)) * (r2 / (sqrt_d * r1)) : 0.0f;
+        if (g == 0 && v0 + j < a.n) {
+            a.scale[v0 + j] = nrm;
+            a.res_scale[v0 + j] = sr;
+        }
+        // coalesced copy-out of the code and sign tiles (16-byte pieces)
+        constexpr int CPIECES = kR256Rows * CROW / 16, SPIECES = kR256Rows * SROW / 16;
+#pragma unroll
+        for (int k = 0; k < (CPIECES + 63) / 64; ++k) {
+            const uint32_t pc = 64u * k + lane;
+            if (pc < (uint32_t)CPIECES) {
+                const uint32_t r = pc / (CROW / 16);
+                const u32x4_t val = reinterpret_cast<const u32x4_t *>(ct)[pc];
+                if (v0 + r < a.n) reinterpret_cast<u32x4_t *>(a.codes + v0 * CROW)[pc] = val;
+            }
+        }
+        if (lane < (uint32_t)SPIECES) {
+            const uint32_t r = lane / (SROW / 16);
+            const u32x4_t val = reinterpret_cast<const u32x4_t *>(st)[lane];
+            if (v0 + r < a.n) reinterpret_cast<u32x4_t *>(a.signs + v0 * SROW)[lane] = val;
+        }
+    }
+}
+
 // Codes (and residual signs) and scales lane q needs for vector `vec`.
 template <int D, int G, int BITS, int KIND>
 __device__ __forceinline__ void fetch_codes(const DequantArgs &a, int64_t vec, uint32_t q,
@@ -576,7 +747,6 @@ __global__ __launch_bounds__(kBlock) void k_dequantize(const DequantArgs a) {
     constexpr bool DRIVE = (KIND == kDriveBiased || KIND == kDriveUnbiased);
     constexpr int CB = KIND == kResidual ? BITS - 1 : (DRIVE ? 1 : BITS);
     constexpr int WPG = G * CB / 32;
-    constexpr int ROWW = D * CB / 32;
     static_assert(G * CB % 32 == 0, "a group's codes fill whole words");
 
     // 4-bit codes are decoded a byte (two codes) at a time from a 256-entry
@@ -824,6 +994,23 @@ hipError_t run_dq(const DequantArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int CB>
+hipError_t run_res256_cb(const QuantArgs &a, hipStream_t s) {
+    static const int per_cu = resident_blocks(k_residual_quantize_mfma256<CB>);
+    hipLaunchKernelGGL(k_residual_quantize_mfma256<CB>, dim3(grid_for(a.n, kWaves * kR256Rows, per_cu)), dim3(kBlock),
+                       0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t run_res256(int cb, const QuantArgs &a, hipStream_t s) {
+    switch (cb) {
+    case 1: return run_res256_cb<1>(a, s);
+    case 2: return run_res256_cb<2>(a, s);
+    case 3: return run_res256_cb<3>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int D>
 hipError_t quant_d(bool f16, int bits, Kind kind, int layout, const QuantArgs &a, hipStream_t s) {
     constexpr int E = D / lanes_per_vec(D);
@@ -851,6 +1038,7 @@ hipError_t quant_d(bool f16, int bits, Kind kind, int layout, const QuantArgs &a
         return f16 ? run_q<D, E, true, 1, kDriveUnbiased>(a, s)
                    : run_q<D, E, false, 1, kDriveUnbiased>(a, s);
     case kResidual:
+        if (D == 256 && f16 && hadamard_on_mfma()) return run_res256(bits - 1, a, s);
         switch (bits) {
         case 2: return f16 ? run_q<D, E, true, 2, kResidual>(a, s) : run_q<D, E, false, 2, kResidual>(a, s);
         case 3: return f16 ? run_q<D, E, true, 3, kResidual>(a, s) : run_q<D, E, false, 3, kResidual>(a, s);
@@ -898,6 +1086,8 @@ hipError_t dequant_d(bool f16, int bits, Kind kind, int layout, const DequantArg
         case 3: return f16 ? run_dq<D, E, true, 3, kResidual>(a, s) : run_dq<D, E, false, 3, kResidual>(a, s);
         case 4: return f16 ? run_dq<D, E, true, 4, kResidual>(a, s) : run_dq<D, E, false, 4, kResidual>(a, s);
         }
+        break;
+    case kEden:  // EDEN codes decode as MSE codes (the caller passes kMse)
         break;
     }
     return hipErrorInvalidValue;
