@@ -284,7 +284,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=25)
-    ap.add_argument("--cpu-rows", type=int, default=1 << 20)
+    ap.add_argument("--cpu-rows", type=int, default=3 << 20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip timing the DRIVE, residual and scoring workloads")
