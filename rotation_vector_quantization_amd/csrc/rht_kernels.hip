@@ -710,6 +710,272 @@ __global__ __launch_bounds__(kBlock) void k_residual_quantize_mfma256(const Quan
     }
 }
 
+// ---------------------------------------------------------------------------
+// Residual-chain decoder for d = 256 with fp16 output, H_32 on MFMA.
+// x^ = D H z with z = (||x|| / d) c[code] + (S_r / sqrt(d)) sigma splits by
+// linearity into two products per block a, with the 16 vectors of a wave tile
+// as the columns of v_mfma_f32_16x16x32_f16: P = H_32 c (each level enters as
+// its fp16 hi and lo parts in neighbouring K slots, so the fp32 level is
+// exact) and Q = H_32 sigma (+-1, exact).  Lane (j, g) combines
+// (||x_j|| / d) P + (S_r,j / sqrt(d)) Q for output coordinates 32 a + 8 g .. +8,
+// runs H_8 across the blocks in registers and applies D as an XOR on the fp16
+// sign bits.  Lookup tables turn a group of four codes into the {hi, hi, lo, lo}
+// operand words and a sign byte into eight +-1 halves.
+//
+// Memory: a tile's code rows, sign rows, norms and residual scales reach LDS by
+// direct global -> LDS copies, and its fp16 rows leave through an LDS tile in
+// stores of two whole rows per instruction.  The copies for tile t + 1 are
+// issued when tile t starts; the wave waits for them (vmcnt(0)) only after
+// tile t's output is in LDS and before its global stores, so the wait covers
+// the copies and the stores of tile t - 1, both issued a whole tile earlier.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Operand A of the decoder's products: row rho of half mh is output coordinate
+// 8 (rho / 4) + 4 mh + rho % 4; K slot t of lane group g is input coordinate
+// 8 g + t (sign product, h < 0) or 8 g + 4 h + (t & 3) (level product of code
+// group h: hi parts in slots t < 4, lo parts in t >= 4).
+__device__ __forceinline__ u32x4_t res256_operand(uint32_t j, uint32_t g, int mh, int h) {
+    const uint32_t bo = 8u * (j >> 2) + 4u * mh + (j & 3u);
+    uint32_t w[4];
+#pragma unroll
+    for (int t = 0; t < 8; t += 2) {
+        uint32_t pair = 0u;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const uint32_t tt = t + u;
+            const uint32_t bi = h < 0 ? 8u * g + tt : 8u * g + 4u * h + (tt & 3u);
+            pair |= ((__builtin_popcount(bo & bi) & 1u) ? 0xBC00u : 0x3C00u) << (16 * u);
+        }
+        w[t / 2] = pair;
+    }
+    return u32x4_t{w[0], w[1], w[2], w[3]};
+}
+
+// 16-byte chunk position of chunk c of tile row r in a staged tile with NC
+// chunks per row (the rows of one 64-bank window land on distinct banks).
+template <int NC>
+__device__ __forceinline__ uint32_t rd_chunk(uint32_t r, uint32_t c) {
+    return NC * r + (c ^ ((r * NC / 16u) & (NC - 1u)));
+}
+
+// Direct global -> LDS copy of the 16 rows at row0 (ROWB bytes each; rows past
+// the end repeat the last row).  Lane l fills chunk position l.
+template <int ROWB>
+__device__ __forceinline__ void rd_stage(const uint8_t *src, int64_t row0, int64_t n, uint8_t *tile, uint32_t lane) {
+    constexpr int NC = ROWB / 16;
+    if (lane < 16u * NC) {
+        const uint32_t r = lane / NC, cpos = lane % NC;
+        const uint32_t c = cpos ^ ((r * NC / 16u) & (NC - 1u));
+        const int64_t row = row0 + r < n ? row0 + r : n - 1;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4 *>(src + row * ROWB) + c,
+                                         (lds_void_t *)tile, 16, 0, 0);
+    }
+}
+
+// Direct copy of the norms and residual scales of the 16 rows at row0 into ft
+// (lane l < 16: ||x|| of row l; 16 <= l < 32: S_r of row l - 16; rows past the
+// end repeat the last row).
+__device__ __forceinline__ void rd_stage_scales(const DequantArgs &a, int64_t row0, float *ft, uint32_t lane) {
+    const uint32_t r = lane % kR256Rows;
+    const int64_t row = row0 + r < a.n ? row0 + r : a.n - 1;
+    if (lane < (uint32_t)kR256Rows)
+        __builtin_amdgcn_global_load_lds(a.scale + row, (lds_void_t *)ft, 4, 0, 0);
+    else if (lane < 2u * kR256Rows)
+        __builtin_amdgcn_global_load_lds(a.res_scale + row, (lds_void_t *)ft, 4, 0, 0);
+}
+
+// Byte B (or the 16-bit word at B) of tile row r.
+template <int ROWB>
+__device__ __forceinline__ uint32_t rd_byte(const uint8_t *tile, uint32_t r, uint32_t B) {
+    return tile[16u * rd_chunk<ROWB / 16>(r, B / 16u) + B % 16u];
+}
+template <int ROWB>
+__device__ __forceinline__ uint32_t rd_u16(const uint8_t *tile, uint32_t r, uint32_t B) {
+    return *reinterpret_cast<const uint16_t *>(tile + 16u * rd_chunk<ROWB / 16>(r, B / 16u) + B % 16u);
+}
+
+template <int CB>
+struct Rd256Smem {
+    static constexpr int kGroups = 1 << (4 * CB);            // four codes per table index
+    static constexpr int kCRow = 256 * CB / 8, kSRow = 32;   // code and sign bytes per row
+    u32x4_t lev[kGroups];
+    u32x4_t sgn[256];
+    u32x4_t om[32];                                         // [a][g]: D on coordinates 32 a + 8 g .. +8
+    uint8_t c[kWaves][kR256Rows * kCRow];
+    uint8_t s[kWaves][kR256Rows * kSRow];
+    float f[kWaves][2 * kR256Rows];                         // ||x|| then S_r of the staged rows
+    u32x4_t y[kWaves][kR256Rows * 32];                      // fp16 output tile, 16-byte chunks
+};
+
+// Waits on this wave's memory counters.  The direct global -> LDS copies are
+// not reliably ordered by the compiler against LDS reads of the same buffer,
+// so the kernel orders them itself: vmcnt(0) before the staged data is read,
+// lgkmcnt(0) (those reads done) before the buffer is refilled.  The "memory"
+// clobber keeps the compiler from moving memory accesses across either wait.
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_lgkm() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// The staged inputs lane (j, g) needs: code bits and sign byte of vector j for
+// coordinates 32 a + 8 g .. +8 (every block a), its norm and residual scale.
+template <int CB>
+__device__ __forceinline__ void rd256_fetch(const uint8_t *ct, const uint8_t *st, const float *ft, uint32_t j,
+                                            uint32_t g, uint32_t (&cw)[8], uint32_t (&sw)[8], float &sc, float &rs) {
+    constexpr int CROW = Rd256Smem<CB>::kCRow, SROW = Rd256Smem<CB>::kSRow;
+    wait_vm();
+#pragma unroll
+    for (int a8 = 0; a8 < 8; ++a8) {
+        cw[a8] = CB == 2 ? rd_u16<CROW>(ct, j, 8u * a8 + 2u * g) : rd_byte<CROW>(ct, j, 4u * a8 + g);
+        sw[a8] = rd_byte<SROW>(st, j, 4u * a8 + g);
+    }
+    sc = ft[j];
+    rs = ft[kR256Rows + j];
+}
+
+// One tile's arithmetic: the level and sign products per block, the per-vector
+// combination and H_8 across the blocks; z[a][mh][r] is output coordinate
+// 32 a + 8 g + 4 mh + r of vector j (before D).
+template <int CB>
+__device__ __forceinline__ void rd256_math(const Rd256Smem<CB> &sm, const u32x4_t (&Ac)[2][2], const u32x4_t (&As)[2],
+                                           const uint32_t (&cw)[8], const uint32_t (&sw)[8], float sc, float rs,
+                                           floatx4 (&z)[8][2]) {
+    constexpr int D = 256;
+    constexpr uint32_t GMASK = Rd256Smem<CB>::kGroups - 1;
+    const float alpha = sc * (1.0f / D), beta = rs * (1.0f / 16.0f);  // 1 / sqrt(256)
+#pragma unroll
+    for (int a8 = 0; a8 < 8; ++a8) {
+        const u32x4_t b0 = sm.lev[cw[a8] & GMASK];
+        const u32x4_t b1 = sm.lev[(cw[a8] >> (4 * CB)) & GMASK];
+        const u32x4_t bs = sm.sgn[sw[a8]];
+#pragma unroll
+        for (int mh = 0; mh < 2; ++mh) {
+            floatx4 p = mfma16x16x32(Ac[mh][0], b0, floatx4{0.0f, 0.0f, 0.0f, 0.0f});
+            p = mfma16x16x32(Ac[mh][1], b1, p);
+            const floatx4 q = mfma16x16x32(As[mh], bs, floatx4{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+            for (int r = 0; r < 4; ++r) z[a8][mh][r] = fmaf(alpha, p[r], beta * q[r]);
+        }
+    }
+#pragma unroll
+    for (int hs = 1; hs < 8; hs <<= 1)
+#pragma unroll
+        for (int a8 = 0; a8 < 8; ++a8)
+            if (!(a8 & hs)) {
+#pragma unroll
+                for (int mh = 0; mh < 2; ++mh) {
+                    const floatx4 u = z[a8][mh], v = z[a8 + hs][mh];
+                    z[a8][mh] = u + v;
+                    z[a8 + hs][mh] = u - v;
+                }
+            }
+}
+
+// fp16 with D applied, into the wave's LDS output tile (chunk c of row r at
+// 32 r + (c ^ r)).
+template <int CB>
+__device__ __forceinline__ void rd256_to_tile(const Rd256Smem<CB> &sm, u32x4_t *yt, const floatx4 (&z)[8][2],
+                                              uint32_t j, uint32_t g) {
+#pragma unroll
+    for (int a8 = 0; a8 < 8; ++a8) {
+        const u32x4_t om = sm.om[4 * a8 + g];
+        uint32_t o[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const _Float16 lo = (_Float16)z[a8][p >> 1][2 * (p & 1)];
+            const _Float16 hi = (_Float16)z[a8][p >> 1][2 * (p & 1) + 1];
+            o[p] = ((uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16)) ^
+                   om[p];
+        }
+        yt[32u * j + ((4u * a8 + g) ^ j)] = u32x4_t{o[0], o[1], o[2], o[3]};
+    }
+}
+
+// Copy-out of the LDS output tile: instruction k stores rows 2k and 2k + 1 whole.
+__device__ __forceinline__ void rd256_flush(const DequantArgs &a, const u32x4_t *yt, int64_t v0, uint32_t lane) {
+    u32x4_t *y = static_cast<u32x4_t *>(a.y);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t r = 2u * k + (lane >> 5), c = lane & 31u;
+        const u32x4_t val = yt[32u * r + (c ^ r)];
+        if (v0 + r < a.n) y[(v0 + r) * 32 + c] = val;
+    }
+}
+
+template <int CB>
+__global__ __launch_bounds__(kBlock) void k_residual_dequantize_mfma256(const DequantArgs a) {
+    constexpr int VPB = kWaves * kR256Rows, CROW = Rd256Smem<CB>::kCRow, SROW = Rd256Smem<CB>::kSRow;
+    constexpr int NG = Rd256Smem<CB>::kGroups;
+    __shared__ __attribute__((aligned(16))) Rd256Smem<CB> sm;
+    for (uint32_t k = threadIdx.x; k < (uint32_t)NG; k += kBlock) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const float c = a.lev[(k >> (CB * s)) & ((1u << CB) - 1u)];
+            const _Float16 h = (_Float16)c, l = (_Float16)(c - (float)h);
+            hw[s] = __builtin_bit_cast(uint16_t, h);
+            lw[s] = __builtin_bit_cast(uint16_t, l);
+        }
+        sm.lev[k] = u32x4_t{hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16), lw[0] | (lw[1] << 16), lw[2] | (lw[3] << 16)};
+    }
+    {
+        static_assert(kBlock == 256, "one sign byte per thread");
+        const uint32_t sb = threadIdx.x;
+        uint32_t w[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            w[p] = (((sb >> (2 * p)) & 1u) ? 0x3C00u : 0xBC00u) | ((((sb >> (2 * p + 1)) & 1u) ? 0x3C00u : 0xBC00u) << 16);
+        sm.sgn[sb] = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
+    if (threadIdx.x < 32) {
+        const uint32_t a8 = threadIdx.x >> 2, g = threadIdx.x & 3u;
+        const uint32_t bits8 = (a.dsign[a8] >> (8 * g)) & 0xFFu;
+        uint32_t w[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) w[p] = (((bits8 >> (2 * p)) & 1u) << 15) | (((bits8 >> (2 * p + 1)) & 1u) << 31);
+        sm.om[threadIdx.x] = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
+    __syncthreads();
+
+    const uint32_t lane = lane_id(), j = lane & 15u, g = lane >> 4;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    u32x4_t Ac[2][2], As[2];
+#pragma unroll
+    for (int mh = 0; mh < 2; ++mh) {
+        Ac[mh][0] = res256_operand(j, g, mh, 0);
+        Ac[mh][1] = res256_operand(j, g, mh, 1);
+        As[mh] = res256_operand(j, g, mh, -1);
+    }
+    const int64_t stride = (int64_t)gridDim.x * VPB;
+    const int64_t first = (int64_t)blockIdx.x * VPB + wave * kR256Rows;
+    if (first >= a.n) return;
+    uint8_t *ct = sm.c[wave];
+    uint8_t *st = sm.s[wave];
+    float *ft = sm.f[wave];
+    u32x4_t *yt = sm.y[wave];
+    rd_stage<CROW>(a.codes, first, a.n, ct, lane);
+    rd_stage<SROW>(a.signs, first, a.n, st, lane);
+    rd_stage_scales(a, first, ft, lane);
+    uint32_t cw[8], sw[8];
+    float sc, rs;
+    rd256_fetch<CB>(ct, st, ft, j, g, cw, sw, sc, rs);
+    for (int64_t v0 = first; v0 < a.n; v0 += stride) {
+        const int64_t v1 = v0 + stride;
+        // this tile's inputs are in registers: refill the staging buffers with the next tile's
+        wait_lgkm();
+        if (v1 < a.n) {
+            rd_stage<CROW>(a.codes, v1, a.n, ct, lane);
+            rd_stage<SROW>(a.signs, v1, a.n, st, lane);
+            rd_stage_scales(a, v1, ft, lane);
+        }
+        floatx4 z[8][2];
+        rd256_math<CB>(sm, Ac, As, cw, sw, sc, rs, z);
+        rd256_to_tile<CB>(sm, yt, z, j, g);
+        // the next tile's inputs, after this tile's output is in LDS (which keeps the
+        // arithmetic above the wait) and before its global stores
+        if (v1 < a.n) rd256_fetch<CB>(ct, st, ft, j, g, cw, sw, sc, rs);
+        rd256_flush(a, yt, v0, lane);
+    }
+}
+
 // Codes (and residual signs) and scales lane q needs for vector `vec`.
 template <int D, int G, int BITS, int KIND>
 __device__ __forceinline__ void fetch_codes(const DequantArgs &a, int64_t vec, uint32_t q,
@@ -1002,6 +1268,14 @@ hipError_t run_res256_cb(const QuantArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int CB>
+hipError_t run_rdq256_cb(const DequantArgs &a, hipStream_t s) {
+    static const int per_cu = resident_blocks(k_residual_dequantize_mfma256<CB>);
+    hipLaunchKernelGGL(k_residual_dequantize_mfma256<CB>, dim3(grid_for(a.n, kWaves * kR256Rows, per_cu)),
+                       dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t run_res256(int cb, const QuantArgs &a, hipStream_t s) {
     switch (cb) {
     case 1: return run_res256_cb<1>(a, s);
@@ -1081,6 +1355,10 @@ hipError_t dequant_d(bool f16, int bits, Kind kind, int layout, const DequantArg
     case kDriveUnbiased:
         return f16 ? run_dq<D, E, true, 1, kDriveBiased>(a, s) : run_dq<D, E, false, 1, kDriveBiased>(a, s);
     case kResidual:
+        if (D == 256 && f16 && hadamard_on_mfma()) {
+            if (bits == 2) return run_rdq256_cb<1>(a, s);
+            if (bits == 3) return run_rdq256_cb<2>(a, s);
+        }
         switch (bits) {
         case 2: return f16 ? run_dq<D, E, true, 2, kResidual>(a, s) : run_dq<D, E, false, 2, kResidual>(a, s);
         case 3: return f16 ? run_dq<D, E, true, 3, kResidual>(a, s) : run_dq<D, E, false, 3, kResidual>(a, s);

@@ -218,6 +218,30 @@ def test_residual_grid(d, bits, xdt):
         check_recon(y, ref, tol, "residual decode %s" % odt)
 
 
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("n", [1, 15, 17, 1000])
+def test_residual_decode_arbitrary_inputs(bits, n):
+    """The d = 256 decoder on planes no encoder produced: random codes and signs,
+    zero norms with a nonzero S_r and the reverse, norms over three decades,
+    tiles cut short (n = 1, 15, 17) and several blocks with a tail (n = 1000)."""
+    d, seed = 256, 99 + n
+    say("residual decode, arbitrary inputs, bits=%d n=%d" % (bits, n))
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=(n, d * (bits - 1) // 8), dtype=np.uint8)
+    sg = rng.integers(0, 256, size=(n, d // 8), dtype=np.uint8)
+    norms = np.exp(rng.uniform(np.log(0.1), np.log(100.0), n)).astype(np.float32)
+    rs = (norms * rng.uniform(0.0, 0.3, n)).astype(np.float32)
+    norms[::7] = 0.0
+    rs[::5] = 0.0
+    if n > 1:
+        norms[1], rs[1] = 0.0, 0.7  # residual part alone
+    for odt, tol in (("f16", RECON_F16), ("f32", RECON_F32)):
+        y = host(rht.residual_dequantize(dev(codes), dev(sg), dev(norms), dev(rs), d, bits, seed,
+                                         dtype=tdtype(odt)))
+        ref = oracle.residual_dequantize(codes, sg, norms, rs, d, bits, seed, np_dtype(odt))
+        check_recon(y, ref, tol, "residual decode (arbitrary inputs) %s" % odt)
+
+
 # ------------------------------------------------------------------ scoring
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
 @pytest.mark.parametrize("d", [64, 128, 256])
