@@ -98,6 +98,12 @@ __device__ __forceinline__ void hadamard4(floatx16 (&c)[4]) {
 // reads and writes of the MFMA layout (one row per lane) hit distinct banks.
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Wait until this wave's direct global -> LDS copies have landed.  The compiler
+// does not reliably order such copies against later LDS reads of the same
+// buffer, so every read of a staged tile is preceded by this wait (the
+// "memory" clobber keeps memory accesses from moving across it).
+__device__ __forceinline__ void wait_lds_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 constexpr int kRowsPerWave = 32;
 constexpr int kTileBytes = kRowsPerWave * 256;   // fp16 rows of one wave
 constexpr int kCodeTileBytes = kRowsPerWave * 64;
@@ -127,6 +133,7 @@ __device__ __forceinline__ void quantize_tile128(const QuantArgs &a, const uint2
     constexpr int D = 128;
     const uint32_t j = lane & 31u, h = lane >> 5;
     u32x4_t raw[4][2];
+    wait_lds_copies();
 #pragma unroll
     for (int ap = 0; ap < 4; ++ap)
 #pragma unroll
@@ -228,6 +235,7 @@ __device__ __forceinline__ void dequantize_tile128(const DequantArgs &a, const u
     constexpr int D = 128;
     const uint32_t j = lane & 31u, h = lane >> 5;
     uint2 cw[4];
+    wait_lds_copies();
 #pragma unroll
     for (int ap = 0; ap < 4; ++ap)  // code bytes 16 ap + 8 h .. +8 of row j
         cw[ap] = *reinterpret_cast<const uint2 *>(tile + 16 * c_chunk(j, ap) + 8 * h);
