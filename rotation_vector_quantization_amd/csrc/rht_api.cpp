@@ -472,6 +472,7 @@ rht_status rht_score_sign(const float *q, int32_t m, const uint8_t *bits, const 
     a.key_mult = 1.0f / std::sqrt((float)d);
     a.lev[0] = -1.0f;  // bit 0: the rotated coordinate was negative
     a.lev[1] = 1.0f;
+    a.exact = 1;
     sign_words(seed, d, a.dsign);
     return launched(launch_score(d, 1, false, a, (hipStream_t)stream));
 }

@@ -55,6 +55,7 @@ struct ScoreArgs {
     int64_t n;
     int m;
     float key_mult;          // per-key factor = norms[k] * key_mult (1/d, or 1/sqrt(d) for sign codes)
+    int exact;               // nonzero: every level is exact in fp16 (sign codes)
     float lev[16];           // levels (sign codes: -1, +1)
     uint32_t dsign[kMaxD / 32];
 };

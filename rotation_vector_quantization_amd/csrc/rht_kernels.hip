@@ -1169,32 +1169,50 @@ __global__ __launch_bounds__(kBlock) void k_dequantize(const DequantArgs a) {
 // + (S_r / sqrt(d)) sigma_{k,i}, no further factor.
 // The contraction runs on v_mfma_f32_32x32x2_f32: per wave a 64-query x
 // 32-key tile (two 32x32 accumulators sharing the key operand).
+// The block's queries rotated into LDS, transposed: qt[i * QS + j] = (H D q_j)_i
+// (Sylvester H, unnormalized) for j < 64; rows j >= m repeat the last query.
+// With qmax, qmax[j] = max_i |qt[i][j]|.
+template <int D, int QS>
+__device__ __forceinline__ void rotate_queries(const ScoreArgs &a, float *qt, float *qmax) {
+    constexpr int LPV = lanes_per_vec(D), E = D / LPV, VPW = 64 / LPV, VPB = kWaves * VPW;
+    const uint32_t lane = lane_id(), q = lane % LPV, slot = lane / LPV, wave = threadIdx.x >> 6;
+    const uint64_t lsign = lane_sign_bits<D, E>(a.dsign, q);
+    const float fq = lane_factor(q);
+    for (int j0 = 0; j0 < 64; j0 += VPB) {
+        const int j = j0 + wave * VPW + slot;
+        const bool valid = j < a.m;
+        float v[E];
+        load_signed<D, E, false>(a.q, valid ? j : a.m - 1, q, lsign, v);
+        fwht_regs<E, 0>(v);
+        fwht_lanes<LPV>(v, q);
+        float mx = 0.0f;
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+            v[r] *= fq;
+            mx = fmaxf(mx, fabsf(v[r]));
+        }
+        if (j < 64) {
+#pragma unroll
+            for (int r = 0; r < E; ++r) qt[(q * E + r) * QS + j] = v[r];
+        }
+        if (qmax) {
+#pragma unroll
+            for (int o = 1; o < LPV; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+            if (q == 0 && j < 64) qmax[j] = mx;
+        }
+    }
+}
+
 template <int D, int BITS, bool RES>
 __global__ __launch_bounds__(kBlock) void k_score(const ScoreArgs a) {
-    constexpr int LPV = lanes_per_vec(D), E = D / LPV, VPW = 64 / LPV, VPB = kWaves * VPW;
     constexpr int QS = 96;  // LDS row stride of the transposed queries (bank spread)
     constexpr int ROWW = D * BITS / 32;
     __shared__ float qt[D * QS];
     __shared__ float slev[16];
 
-    const uint32_t lane = lane_id(), q = lane % LPV, slot = lane / LPV, wave = threadIdx.x >> 6;
+    const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
     if (threadIdx.x < 16) slev[threadIdx.x] = a.lev[threadIdx.x];
-    {
-        const uint64_t lsign = lane_sign_bits<D, E>(a.dsign, q);
-        const float fq = lane_factor(q);
-        for (int j0 = 0; j0 < 64; j0 += VPB) {
-            const int j = j0 + wave * VPW + slot;
-            const bool valid = j < a.m;
-            float v[E];
-            load_signed<D, E, false>(a.q, valid ? j : a.m - 1, q, lsign, v);
-            fwht_regs<E, 0>(v);
-            fwht_lanes<LPV>(v, q);
-            if (j < 64) {
-#pragma unroll
-                for (int r = 0; r < E; ++r) qt[(q * E + r) * QS + j] = v[r] * fq;
-            }
-        }
-    }
+    rotate_queries<D, QS>(a, qt, nullptr);
     __syncthreads();
 
     const uint32_t col = lane & 31u, par = lane >> 5;
@@ -1236,6 +1254,170 @@ __global__ __launch_bounds__(kBlock) void k_score(const ScoreArgs a) {
                 const int qrow = 8 * (r / 4) + 4 * par + (r % 4);
                 if (qrow < a.m) a.logits[(int64_t)qrow * a.n + key] = acc0[r] * sc;
                 if (qrow + 32 < a.m) a.logits[(int64_t)(qrow + 32) * a.n + key] = acc1[r] * sc;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Scoring on the fp16 matrix cores at fp32-level accuracy (d <= 128).
+// logits[q][k] = f_k 2^-e_q sum_i Qs[q][i] C[k][i]: Qs = 2^e_q (H D q) with e_q
+// putting the largest |coordinate| of query q in [2^14, 2^15), split into fp16
+// hi and lo parts Qh + Ql; C[k][i] = c[code_{k,i}] split the same way (exact
+// for +-1 levels).  Each 32 x 32 x 16 step accumulates Qh Ch + Qh Cl + Ql Ch on
+// v_mfma_f32_32x32x16_f16 (the dropped Ql Cl is ~2^-22 of a product; EXACT
+// levels skip Qh Cl).  Residual chain: a second accumulator takes
+// (Qh + Ql) sigma, and f_k = ||k|| / d on the levels, S_r / sqrt(d) on the
+// signs.  A wave owns the 32 queries of one half (its A operands stay in
+// registers) and walks 32-key tiles; K slot t of lane half h in step s is
+// coordinate (d/2) h + 8 s + t, so a lane's codes are one contiguous half row.
+// A pair of codes maps to its levels' fp16 hi and lo parts through an LDS table.
+template <int N>
+__device__ __forceinline__ void load_half_row(const uint8_t *p, uint32_t (&w)[N]) {
+    // p is aligned to the largest power of two dividing both the row and half-row sizes
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int k = 0; k < N / 4; ++k) {
+            const uint4 t = reinterpret_cast<const uint4 *>(p)[k];
+            w[4 * k] = t.x; w[4 * k + 1] = t.y; w[4 * k + 2] = t.z; w[4 * k + 3] = t.w;
+        }
+    } else if constexpr (N % 2 == 0) {
+#pragma unroll
+        for (int k = 0; k < N / 2; ++k) {
+            const uint2 t = reinterpret_cast<const uint2 *>(p)[k];
+            w[2 * k] = t.x; w[2 * k + 1] = t.y;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < N; ++k) w[k] = reinterpret_cast<const uint32_t *>(p)[k];
+    }
+}
+
+__device__ __forceinline__ floatx16 mfma32x32x16(u32x4_t a, u32x4_t b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c,
+                                                  0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_half2(_Float16 lo, _Float16 hi) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
+// Lane step s of the key operands: B_h / B_l carry the fp16 hi / lo parts of the
+// levels of coordinates (d/2) h + 8 s .. +8, from four code-pair lookups.
+template <int BITS, int HW>
+__device__ __forceinline__ void key_operands(const uint2 *ptab, const uint32_t (&w)[HW], int s, u32x4_t &bh,
+                                             u32x4_t &bl) {
+    uint2 e[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) e[p] = ptab[get_code<2 * BITS, HW>(w, 4 * s + p)];
+    bh = u32x4_t{e[0].x, e[1].x, e[2].x, e[3].x};
+    bl = u32x4_t{e[0].y, e[1].y, e[2].y, e[3].y};
+}
+
+template <int D, int BITS, bool RES, bool EXACT>
+__global__ __launch_bounds__(kBlock) void k_score_mfma(const ScoreArgs a) {
+    static_assert(D == 64 || D == 128, "a query half's operands stay in registers for d <= 128");
+    constexpr int S = D / 16;                 // K steps of 16 coordinates
+    constexpr int HC = D / 2;                 // coordinates per lane half
+    constexpr int HW = HC * BITS / 32;        // code words per half row
+    constexpr int ROWB = D * BITS / 8;        // code bytes per key
+    constexpr int QS = 65;                    // LDS row stride of the transposed queries
+    __shared__ float qt[D * QS];
+    __shared__ float qmax[64];
+    __shared__ uint2 ptab[1 << (2 * BITS)];   // code pair -> {hi parts, lo parts} of its two levels
+    __shared__ u32x4_t stab[RES ? 256 : 1];   // sign byte -> eight +-1 halves
+
+    const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+    for (uint32_t k = threadIdx.x; k < (1u << (2 * BITS)); k += kBlock) {
+        const float c0 = a.lev[k & ((1u << BITS) - 1u)], c1 = a.lev[k >> BITS];
+        const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
+        ptab[k] = make_uint2(pack_half2(h0, h1), pack_half2((_Float16)(c0 - (float)h0), (_Float16)(c1 - (float)h1)));
+    }
+    if constexpr (RES) {
+        static_assert(kBlock == 256, "one sign byte per thread");
+        const uint32_t sb = threadIdx.x;
+        uint32_t w[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            w[p] = (((sb >> (2 * p)) & 1u) ? 0x3C00u : 0xBC00u) | ((((sb >> (2 * p + 1)) & 1u) ? 0x3C00u : 0xBC00u) << 16);
+        stab[sb] = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
+    rotate_queries<D, QS>(a, qt, qmax);
+    __syncthreads();
+
+    const uint32_t i = lane & 31u, h = lane >> 5;
+    const int RH = a.m > 32 ? 2 : 1;
+    const int64_t gw = (int64_t)blockIdx.x * kWaves + wave, nw = (int64_t)gridDim.x * kWaves;
+    const int rh = (int)(gw % RH);
+    // A operands of this wave's query half: row i is query 32 rh + i
+    u32x4_t Ah[S], Al[S];
+    {
+        const int Q = 32 * rh + (int)i;
+        int ex;
+        (void)frexpf(qmax[Q], &ex);
+        const int e = qmax[Q] > 0.0f ? min(max(15 - ex, -126), 126) : 0;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int t = 0; t < 8; t += 2) {
+                const float v0 = ldexpf(qt[(HC * h + 8 * s + t) * QS + Q], e);
+                const float v1 = ldexpf(qt[(HC * h + 8 * s + t + 1) * QS + Q], e);
+                const _Float16 a0 = (_Float16)v0, a1 = (_Float16)v1;
+                hw[t / 2] = pack_half2(a0, a1);
+                lw[t / 2] = pack_half2((_Float16)(v0 - (float)a0), (_Float16)(v1 - (float)a1));
+            }
+            Ah[s] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+            Al[s] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
+        }
+    }
+    // 2^-e of the queries in this lane's accumulator rows 8 (r / 4) + 4 h + r % 4
+    float qinv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int Q = 32 * rh + 8 * (r / 4) + 4 * (int)h + (r % 4);
+        int ex;
+        (void)frexpf(qmax[Q], &ex);
+        const int e = qmax[Q] > 0.0f ? min(max(15 - ex, -126), 126) : 0;
+        qinv[r] = ldexpf(1.0f, -e);
+    }
+
+    const int64_t ntiles = (a.n + 31) / 32;
+    for (int64_t tile = gw / RH; tile < ntiles; tile += nw / RH) {
+        const int64_t key = tile * 32 + i;
+        const int64_t row = key < a.n ? key : a.n - 1;
+        uint32_t w[HW];
+        load_half_row<HW>(a.codes + row * ROWB + h * (HW * 4), w);
+        uint32_t sg[RES ? (S + 3) / 4 : 1];
+        if constexpr (RES) load_half_row<(S + 3) / 4>(a.signs + row * (D / 8) + h * S, sg);
+        floatx16 acc = {}, accs = {};
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            u32x4_t bh, bl;
+            key_operands<BITS, HW>(ptab, w, s, bh, bl);
+            acc = mfma32x32x16(Ah[s], bh, acc);
+            if constexpr (!EXACT) acc = mfma32x32x16(Ah[s], bl, acc);
+            acc = mfma32x32x16(Al[s], bh, acc);
+            if constexpr (RES) {
+                const u32x4_t bs = stab[(sg[s / 4] >> (8 * (s % 4))) & 0xFFu];
+                accs = mfma32x32x16(Ah[s], bs, accs);
+                accs = mfma32x32x16(Al[s], bs, accs);
+            }
+        }
+        if (key < a.n) {
+            float fa, fb = 0.0f;
+            if constexpr (RES) {
+                fa = a.norms[key] * (1.0f / D);
+                fb = a.res_scale[key] * (1.0f / __builtin_sqrtf((float)D));
+            } else {
+                fa = a.norms[key] * a.key_mult;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int Q = 32 * rh + 8 * (r / 4) + 4 * (int)h + (r % 4);
+                float v = acc[r] * fa;
+                if constexpr (RES) v = fmaf(accs[r], fb, v);
+                if (Q < a.m) a.logits[(int64_t)Q * a.n + key] = v * qinv[r];
             }
         }
     }
@@ -1382,8 +1564,39 @@ hipError_t run_score(const ScoreArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int D, int BITS, bool RES, bool EXACT>
+hipError_t run_score_mfma(const ScoreArgs &a, hipStream_t s) {
+    static const int per_cu = resident_blocks(k_score_mfma<D, BITS, RES, EXACT>);
+    const int64_t items = ((a.n + 31) / 32) * (a.m > 32 ? 2 : 1);  // (key tile, query half) pairs
+    hipLaunchKernelGGL((k_score_mfma<D, BITS, RES, EXACT>), dim3(grid_for(items, kWaves, per_cu)), dim3(kBlock), 0,
+                       s, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t score_mfma_d(int bits, bool residual, const ScoreArgs &a, hipStream_t s) {
+    if (residual) {
+        switch (bits) {
+        case 1: return run_score_mfma<D, 1, true, false>(a, s);
+        case 2: return run_score_mfma<D, 2, true, false>(a, s);
+        case 3: return run_score_mfma<D, 3, true, false>(a, s);
+        }
+        return hipErrorInvalidValue;
+    }
+    switch (bits) {
+    case 1: return a.exact ? run_score_mfma<D, 1, false, true>(a, s) : run_score_mfma<D, 1, false, false>(a, s);
+    case 2: return run_score_mfma<D, 2, false, false>(a, s);
+    case 3: return run_score_mfma<D, 3, false, false>(a, s);
+    case 4: return run_score_mfma<D, 4, false, false>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int D>
 hipError_t score_d(int bits, bool residual, const ScoreArgs &a, hipStream_t s) {
+    if constexpr (D <= 128) {
+        if (hadamard_on_mfma()) return score_mfma_d<D>(bits, residual, a, s);
+    }
     if (residual) {
         switch (bits) {
         case 1: return run_score<D, 1, true>(a, s);
