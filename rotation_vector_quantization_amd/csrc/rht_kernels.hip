@@ -1314,20 +1314,103 @@ __device__ __forceinline__ void key_operands(const uint2 *ptab, const uint32_t (
     bl = u32x4_t{e[0].y, e[1].y, e[2].y, e[3].y};
 }
 
+// Direct global -> LDS copies of the kScoreTK key tiles from `tile` on (32 keys
+// each): code rows (chunk c of row r at position NC r + (c ^ ((r / 4) % NC))
+// when NC, the chunks per row, is a power of two), norms (and for the residual
+// chain S_r and the sign rows).  Keys past the end repeat the last chunk / key.
+constexpr int kScoreTK = 2;  // key tiles per wave item
+
+template <int ROWB, bool RES>
+__device__ __forceinline__ void stage_keys(const ScoreArgs &a, int64_t tile, uint8_t *kc, uint8_t *ks, float *kn,
+                                           uint32_t lane) {
+    constexpr int NC = ROWB / 16, CH = 32 * kScoreTK * NC;  // chunks per row, per item
+    constexpr bool SWZ = (NC & (NC - 1)) == 0;
+    const int64_t last = (a.n * ROWB) / 16 - 1;              // last code chunk of the array
+#pragma unroll
+    for (int k = 0; k < (CH + 63) / 64; ++k) {
+        const uint32_t p = 64u * k + lane;
+        if (p < (uint32_t)CH) {
+            const uint32_t r = p / NC, cp = p % NC;
+            const uint32_t c = SWZ ? (cp ^ ((r >> 2) & (NC - 1))) : cp;
+            int64_t g = tile * (32 * NC) + r * NC + c;
+            g = g < last ? g : last;
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4 *>(a.codes) + g,
+                                             (lds_void_t *)(kc + 1024 * k), 16, 0, 0);
+        }
+    }
+    static_assert(kScoreTK == 2, "one lane per key of the item");
+    const int64_t key = tile * 32 + lane < a.n ? tile * 32 + lane : a.n - 1;
+    __builtin_amdgcn_global_load_lds(a.norms + key, (lds_void_t *)kn, 4, 0, 0);
+    if constexpr (RES) {
+        __builtin_amdgcn_global_load_lds(a.res_scale + key, (lds_void_t *)(kn + 64), 4, 0, 0);
+        // sign rows: 16 bytes per key (d = 128)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4 *>(a.signs) + key, (lds_void_t *)ks, 16, 0, 0);
+    }
+}
+
+// Lane (key r of the item, half h)'s staged data: its half row of codes, sign
+// bytes, norm and residual scale.
+template <int ROWB, bool RES, int HW>
+__device__ __forceinline__ void fetch_keys(const uint8_t *kc, const uint8_t *ks, const float *kn, uint32_t r,
+                                           uint32_t h, uint32_t (&w)[HW], uint32_t (&sg)[2], float &fa, float &fb) {
+    constexpr int NC = ROWB / 16;
+    constexpr bool SWZ = (NC & (NC - 1)) == 0;
+#pragma unroll
+    for (int k = 0; k < HW; ++k) {
+        const uint32_t byte = h * (HW * 4) + 4 * k, c = byte / 16;
+        const uint32_t pos = NC * r + (SWZ ? (c ^ ((r >> 2) & (NC - 1))) : c);
+        w[k] = *reinterpret_cast<const uint32_t *>(kc + 16 * pos + byte % 16);
+    }
+    if constexpr (RES) {
+        const uint2 t = *reinterpret_cast<const uint2 *>(ks + 16 * r + 8 * h);
+        sg[0] = t.x;
+        sg[1] = t.y;
+        fb = kn[64 + r];
+    }
+    fa = kn[r];
+}
+
+template <int D, int BITS, bool RES, bool EXACT>
+__device__ __forceinline__ void score_tile(const uint2 *ptab, const u32x4_t *stab, const u32x4_t (&Ah)[D / 16],
+                                           const u32x4_t (&Al)[D / 16], const uint32_t (&w)[D * BITS / 64],
+                                           const uint32_t (&sg)[2], floatx16 &acc, floatx16 &accs) {
+    constexpr int S = D / 16, HW = D * BITS / 64;
+    acc = floatx16{};
+    accs = floatx16{};
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        u32x4_t bh, bl;
+        key_operands<BITS, HW>(ptab, w, s, bh, bl);
+        acc = mfma32x32x16(Ah[s], bh, acc);
+        if constexpr (!EXACT) acc = mfma32x32x16(Ah[s], bl, acc);
+        acc = mfma32x32x16(Al[s], bh, acc);
+        if constexpr (RES) {
+            const u32x4_t bs = stab[(sg[s / 4] >> (8 * (s % 4))) & 0xFFu];
+            accs = mfma32x32x16(Ah[s], bs, accs);
+            accs = mfma32x32x16(Al[s], bs, accs);
+        }
+    }
+}
+
 template <int D, int BITS, bool RES, bool EXACT>
 __global__ __launch_bounds__(kBlock) void k_score_mfma(const ScoreArgs a) {
-    static_assert(D == 64 || D == 128, "a query half's operands stay in registers for d <= 128");
+    static_assert(D == 128, "a query half's operands stay in registers; code rows are whole 16-byte chunks");
     constexpr int S = D / 16;                 // K steps of 16 coordinates
     constexpr int HC = D / 2;                 // coordinates per lane half
     constexpr int HW = HC * BITS / 32;        // code words per half row
     constexpr int ROWB = D * BITS / 8;        // code bytes per key
     constexpr int QS = 65;                    // LDS row stride of the transposed queries
+    constexpr int KI = 32 * kScoreTK;         // keys per wave item
     __shared__ float qt[D * QS];
     __shared__ float qmax[64];
+    __shared__ __attribute__((aligned(16))) float qinv[64];  // 2^-e_q
     __shared__ uint2 ptab[1 << (2 * BITS)];   // code pair -> {hi parts, lo parts} of its two levels
     __shared__ u32x4_t stab[RES ? 256 : 1];   // sign byte -> eight +-1 halves
+    __shared__ __attribute__((aligned(16))) uint8_t kcb[kWaves][KI * ROWB];
+    __shared__ __attribute__((aligned(16))) uint8_t ksb[kWaves][RES ? KI * (D / 8) : 16];
+    __shared__ float knb[kWaves][2 * KI];
 
-    const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+    const uint32_t lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     for (uint32_t k = threadIdx.x; k < (1u << (2 * BITS)); k += kBlock) {
         const float c0 = a.lev[k & ((1u << BITS) - 1u)], c1 = a.lev[k >> BITS];
         const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
@@ -1344,18 +1427,30 @@ __global__ __launch_bounds__(kBlock) void k_score_mfma(const ScoreArgs a) {
     }
     rotate_queries<D, QS>(a, qt, qmax);
     __syncthreads();
+    // e_q puts the largest |coordinate| of query q in [2^14, 2^15)
+    auto qexp = [&](int Q) {
+        int ex;
+        (void)frexpf(qmax[Q], &ex);
+        return qmax[Q] > 0.0f ? min(max(15 - ex, -126), 126) : 0;
+    };
+    if (threadIdx.x < 64) qinv[threadIdx.x] = ldexpf(1.0f, -qexp((int)threadIdx.x));
 
     const uint32_t i = lane & 31u, h = lane >> 5;
     const int RH = a.m > 32 ? 2 : 1;
     const int64_t gw = (int64_t)blockIdx.x * kWaves + wave, nw = (int64_t)gridDim.x * kWaves;
     const int rh = (int)(gw % RH);
+    const int64_t ntiles = (a.n + 31) / 32, istride = (nw / RH) * kScoreTK;
+    int64_t tile = (gw / RH) * kScoreTK;  // first tile of this wave's item
+    uint8_t *kc = kcb[wave];
+    uint8_t *ks = ksb[wave];
+    float *kn = knb[wave];
+    if (tile < ntiles) stage_keys<ROWB, RES>(a, tile, kc, ks, kn, lane);
+
     // A operands of this wave's query half: row i is query 32 rh + i
     u32x4_t Ah[S], Al[S];
     {
         const int Q = 32 * rh + (int)i;
-        int ex;
-        (void)frexpf(qmax[Q], &ex);
-        const int e = qmax[Q] > 0.0f ? min(max(15 - ex, -126), 126) : 0;
+        const int e = qexp(Q);
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             uint32_t hw[4], lw[4];
@@ -1371,55 +1466,55 @@ __global__ __launch_bounds__(kBlock) void k_score_mfma(const ScoreArgs a) {
             Al[s] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
         }
     }
-    // 2^-e of the queries in this lane's accumulator rows 8 (r / 4) + 4 h + r % 4
-    float qinv[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int Q = 32 * rh + 8 * (r / 4) + 4 * (int)h + (r % 4);
-        int ex;
-        (void)frexpf(qmax[Q], &ex);
-        const int e = qmax[Q] > 0.0f ? min(max(15 - ex, -126), 126) : 0;
-        qinv[r] = ldexpf(1.0f, -e);
-    }
+    __syncthreads();  // qinv; every wave of the block reaches this barrier
+    if (tile >= ntiles) return;
 
-    const int64_t ntiles = (a.n + 31) / 32;
-    for (int64_t tile = gw / RH; tile < ntiles; tile += nw / RH) {
-        const int64_t key = tile * 32 + i;
-        const int64_t row = key < a.n ? key : a.n - 1;
-        uint32_t w[HW];
-        load_half_row<HW>(a.codes + row * ROWB + h * (HW * 4), w);
-        uint32_t sg[RES ? (S + 3) / 4 : 1];
-        if constexpr (RES) load_half_row<(S + 3) / 4>(a.signs + row * (D / 8) + h * S, sg);
-        floatx16 acc = {}, accs = {};
+    uint32_t w0[HW], w1[HW], sg0[2] = {0u, 0u}, sg1[2] = {0u, 0u};
+    float fa0, fa1, fb0 = 0.0f, fb1 = 0.0f;
+    wait_vm();
+    fetch_keys<ROWB, RES, HW>(kc, ks, kn, i, h, w0, sg0, fa0, fb0);
+    fetch_keys<ROWB, RES, HW>(kc, ks, kn, 32 + i, h, w1, sg1, fa1, fb1);
+    for (;;) {
+        const int64_t next = tile + istride;
+        wait_lgkm();  // this item's staged data is in registers
+        if (next < ntiles) stage_keys<ROWB, RES>(a, next, kc, ks, kn, lane);
+        floatx16 acc0, accs0, acc1, accs1;
+        score_tile<D, BITS, RES, EXACT>(ptab, stab, Ah, Al, w0, sg0, acc0, accs0);
+        score_tile<D, BITS, RES, EXACT>(ptab, stab, Ah, Al, w1, sg1, acc1, accs1);
+        // per-key factors: ||k|| key_mult (MSE, sign), ||k|| / d and S_r / sqrt(d) (residual chain)
+        const float km = RES ? 1.0f / D : a.key_mult, kr = 1.0f / __builtin_sqrtf((float)D);
+        const float fa0_t = fa0 * km, fa1_t = fa1 * km, fb0_t = fb0 * kr, fb1_t = fb1 * kr;
+        if (next < ntiles) {
+            // the next item's data, once this item's products are issued (the wait takes
+            // the accumulators as inputs) and before its stores (so it never waits on them)
+            asm volatile("s_waitcnt vmcnt(0)" ::"v"(acc0[15]), "v"(acc1[15]), "v"(accs0[15]), "v"(accs1[15])
+                         : "memory");
+            fetch_keys<ROWB, RES, HW>(kc, ks, kn, i, h, w0, sg0, fa0, fb0);
+            fetch_keys<ROWB, RES, HW>(kc, ks, kn, 32 + i, h, w1, sg1, fa1, fb1);
+        }
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            u32x4_t bh, bl;
-            key_operands<BITS, HW>(ptab, w, s, bh, bl);
-            acc = mfma32x32x16(Ah[s], bh, acc);
-            if constexpr (!EXACT) acc = mfma32x32x16(Ah[s], bl, acc);
-            acc = mfma32x32x16(Al[s], bh, acc);
-            if constexpr (RES) {
-                const u32x4_t bs = stab[(sg[s / 4] >> (8 * (s % 4))) & 0xFFu];
-                accs = mfma32x32x16(Ah[s], bs, accs);
-                accs = mfma32x32x16(Al[s], bs, accs);
+        for (int r4 = 0; r4 < 4; ++r4) {
+            // queries 32 rh + 8 r4 + 4 h .. +4: accumulator registers 4 r4 .. +4
+            const int Q0 = 32 * rh + 8 * r4 + 4 * (int)h;
+            const float4 qi = *reinterpret_cast<const float4 *>(qinv + Q0);
+            const float qv[4] = {qi.x, qi.y, qi.z, qi.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = 4 * r4 + u, Q = Q0 + u;
+                if (Q < a.m) {
+                    const int64_t key0 = tile * 32 + i, key1 = key0 + 32;
+                    float v0 = acc0[r] * fa0_t, v1 = acc1[r] * fa1_t;
+                    if constexpr (RES) {
+                        v0 = fmaf(accs0[r], fb0_t, v0);
+                        v1 = fmaf(accs1[r], fb1_t, v1);
+                    }
+                    if (key0 < a.n) a.logits[(int64_t)Q * a.n + key0] = v0 * qv[u];
+                    if (key1 < a.n) a.logits[(int64_t)Q * a.n + key1] = v1 * qv[u];
+                }
             }
         }
-        if (key < a.n) {
-            float fa, fb = 0.0f;
-            if constexpr (RES) {
-                fa = a.norms[key] * (1.0f / D);
-                fb = a.res_scale[key] * (1.0f / __builtin_sqrtf((float)D));
-            } else {
-                fa = a.norms[key] * a.key_mult;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int Q = 32 * rh + 8 * (r / 4) + 4 * (int)h + (r % 4);
-                float v = acc[r] * fa;
-                if constexpr (RES) v = fmaf(accs[r], fb, v);
-                if (Q < a.m) a.logits[(int64_t)Q * a.n + key] = v * qinv[r];
-            }
-        }
+        tile = next;
+        if (tile >= ntiles) break;
     }
 }
 
@@ -1567,7 +1662,8 @@ hipError_t run_score(const ScoreArgs &a, hipStream_t s) {
 template <int D, int BITS, bool RES, bool EXACT>
 hipError_t run_score_mfma(const ScoreArgs &a, hipStream_t s) {
     static const int per_cu = resident_blocks(k_score_mfma<D, BITS, RES, EXACT>);
-    const int64_t items = ((a.n + 31) / 32) * (a.m > 32 ? 2 : 1);  // (key tile, query half) pairs
+    // wave items: (pair of key tiles, query half)
+    const int64_t items = ((a.n + 32 * kScoreTK - 1) / (32 * kScoreTK)) * (a.m > 32 ? 2 : 1);
     hipLaunchKernelGGL((k_score_mfma<D, BITS, RES, EXACT>), dim3(grid_for(items, kWaves, per_cu)), dim3(kBlock), 0,
                        s, a);
     return hipGetLastError();
@@ -1594,7 +1690,7 @@ hipError_t score_mfma_d(int bits, bool residual, const ScoreArgs &a, hipStream_t
 
 template <int D>
 hipError_t score_d(int bits, bool residual, const ScoreArgs &a, hipStream_t s) {
-    if constexpr (D <= 128) {
+    if constexpr (D == 128) {
         if (hadamard_on_mfma()) return score_mfma_d<D>(bits, residual, a, s);
     }
     if (residual) {
