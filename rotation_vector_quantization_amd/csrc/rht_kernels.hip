@@ -1172,8 +1172,14 @@ __global__ __launch_bounds__(kBlock) void k_dequantize(const DequantArgs a) {
 // The block's queries rotated into LDS, transposed: qt[i * QS + j] = (H D q_j)_i
 // (Sylvester H, unnormalized) for j < 64; rows j >= m repeat the last query.
 // With qmax, qmax[j] = max_i |qt[i][j]|.
-template <int D, int QS>
-__device__ __forceinline__ void rotate_queries(const ScoreArgs &a, float *qt, float *qmax) {
+// after_load() runs once the first round's query loads are issued (a caller
+// can queue its own copies behind them).
+struct NoHook {
+    __device__ void operator()() const {}
+};
+
+template <int D, int QS, typename Hook = NoHook>
+__device__ __forceinline__ void rotate_queries(const ScoreArgs &a, float *qt, float *qmax, Hook after_load = Hook{}) {
     constexpr int LPV = lanes_per_vec(D), E = D / LPV, VPW = 64 / LPV, VPB = kWaves * VPW;
     const uint32_t lane = lane_id(), q = lane % LPV, slot = lane / LPV, wave = threadIdx.x >> 6;
     const uint64_t lsign = lane_sign_bits<D, E>(a.dsign, q);
@@ -1182,7 +1188,13 @@ __device__ __forceinline__ void rotate_queries(const ScoreArgs &a, float *qt, fl
         const int j = j0 + wave * VPW + slot;
         const bool valid = j < a.m;
         float v[E];
-        load_signed<D, E, false>(a.q, valid ? j : a.m - 1, q, lsign, v);
+        {
+            uint32_t raw[Raw<D, false>::W], sw[Raw<D, false>::W];
+            load_raw<D, E, false>(a.q, valid ? j : a.m - 1, q, raw);
+            if (j0 == 0) after_load();
+            sign_words<D, false>(lsign, sw);
+            stage0<D, false>(raw, sw, v);
+        }
         fwht_regs<E, 0>(v);
         fwht_lanes<LPV>(v, q);
         float mx = 0.0f;
@@ -1411,8 +1423,24 @@ __global__ __launch_bounds__(kBlock) void k_score_mfma(const ScoreArgs a) {
     __shared__ float knb[kWaves][2 * KI];
 
     const uint32_t lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t i = lane & 31u, h = lane >> 5;
+    const int RH = a.m > 32 ? 2 : 1;
+    const int64_t gw = (int64_t)blockIdx.x * kWaves + wave, nw = (int64_t)gridDim.x * kWaves;
+    const int rh = (int)(gw % RH);
+    const int64_t ntiles = (a.n + 31) / 32, istride = (nw / RH) * kScoreTK;
+    int64_t tile = (gw / RH) * kScoreTK;  // first tile of this wave's item
+    uint8_t *kc = kcb[wave];
+    uint8_t *ks = ksb[wave];
+    float *kn = knb[wave];
     for (uint32_t k = threadIdx.x; k < (1u << (2 * BITS)); k += kBlock) {
-        const float c0 = a.lev[k & ((1u << BITS) - 1u)], c1 = a.lev[k >> BITS];
+        // the levels are selected from scalar registers (a per-lane index into the
+        // kernel arguments would be a vector load, and its wait would hold up the copies)
+        float c0 = 0.0f, c1 = 0.0f;
+#pragma unroll
+        for (uint32_t t = 0; t < (1u << BITS); ++t) {
+            c0 = (k & ((1u << BITS) - 1u)) == t ? a.lev[t] : c0;
+            c1 = (k >> BITS) == t ? a.lev[t] : c1;
+        }
         const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
         ptab[k] = make_uint2(pack_half2(h0, h1), pack_half2((_Float16)(c0 - (float)h0), (_Float16)(c1 - (float)h1)));
     }
@@ -1425,7 +1453,10 @@ __global__ __launch_bounds__(kBlock) void k_score_mfma(const ScoreArgs a) {
             w[p] = (((sb >> (2 * p)) & 1u) ? 0x3C00u : 0xBC00u) | ((((sb >> (2 * p + 1)) & 1u) ? 0x3C00u : 0xBC00u) << 16);
         stab[sb] = u32x4_t{w[0], w[1], w[2], w[3]};
     }
-    rotate_queries<D, QS>(a, qt, qmax);
+    // the first item's keys are copied while the queries are rotated
+    rotate_queries<D, QS>(a, qt, qmax, [&] {
+        if (tile < ntiles) stage_keys<ROWB, RES>(a, tile, kc, ks, kn, lane);
+    });
     __syncthreads();
     // e_q puts the largest |coordinate| of query q in [2^14, 2^15)
     auto qexp = [&](int Q) {
@@ -1434,17 +1465,6 @@ __global__ __launch_bounds__(kBlock) void k_score_mfma(const ScoreArgs a) {
         return qmax[Q] > 0.0f ? min(max(15 - ex, -126), 126) : 0;
     };
     if (threadIdx.x < 64) qinv[threadIdx.x] = ldexpf(1.0f, -qexp((int)threadIdx.x));
-
-    const uint32_t i = lane & 31u, h = lane >> 5;
-    const int RH = a.m > 32 ? 2 : 1;
-    const int64_t gw = (int64_t)blockIdx.x * kWaves + wave, nw = (int64_t)gridDim.x * kWaves;
-    const int rh = (int)(gw % RH);
-    const int64_t ntiles = (a.n + 31) / 32, istride = (nw / RH) * kScoreTK;
-    int64_t tile = (gw / RH) * kScoreTK;  // first tile of this wave's item
-    uint8_t *kc = kcb[wave];
-    uint8_t *ks = ksb[wave];
-    float *kn = knb[wave];
-    if (tile < ntiles) stage_keys<ROWB, RES>(a, tile, kc, ks, kn, lane);
 
     // A operands of this wave's query half: row i is query 32 rh + i
     u32x4_t Ah[S], Al[S];
