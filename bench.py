@@ -102,7 +102,10 @@ def time_launches(torch, stream, fn, sets, iters=20, warm_ms=50.0):
     """Per-launch times (ms) of fn(set_index), cycling through `sets` buffer
     sets, from HIP events recorded on `stream` between launches.  The kernel
     first runs untimed for about warm_ms of GPU time, so clocks that dropped
-    during host-side set-up have ramped up again."""
+    during host-side set-up have ramped up again.  Kernels shorter than 0.1 ms
+    are timed in groups of 8 launches per event interval (each value is the
+    group's mean): with an event after every launch the host's submission
+    rate, not the GPU, would set the interval."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(3):
@@ -112,14 +115,18 @@ def time_launches(torch, stream, fn, sets, iters=20, warm_ms=50.0):
     est = max(e0.elapsed_time(e1) / 3, 1e-3)
     for i in range(min(int(warm_ms / est), 5000)):
         fn(i % sets)
+    group = 8 if est < 0.1 else 1
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
     torch.cuda.synchronize()
     ev[0].record(stream)
+    k = 0
     for i in range(iters):
-        fn(i % sets)
+        for _ in range(group):
+            fn(k % sets)
+            k += 1
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    return np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(iters)])
+    return np.array([ev[i].elapsed_time(ev[i + 1]) / group for i in range(iters)])
 
 
 def stats(ms):
