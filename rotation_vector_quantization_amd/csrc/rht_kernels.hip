@@ -1190,19 +1190,21 @@ struct NoHook {
     __device__ void operator()() const {}
 };
 
-template <int D, int QS, typename Hook = NoHook>
-__device__ __forceinline__ void rotate_queries(const ScoreArgs &a, float *qt, float *qmax, Hook after_load = Hook{}) {
+// Queries q0 .. q0 + NQ - 1 go to columns 0 .. NQ - 1 of qt.
+template <int D, int QS, int NQ = 64, typename Hook = NoHook>
+__device__ __forceinline__ void rotate_queries(const ScoreArgs &a, float *qt, float *qmax, int q0 = 0,
+                                               Hook after_load = Hook{}) {
     constexpr int LPV = lanes_per_vec(D), E = D / LPV, VPW = 64 / LPV, VPB = kWaves * VPW;
     const uint32_t lane = lane_id(), q = lane % LPV, slot = lane / LPV, wave = threadIdx.x >> 6;
     const uint64_t lsign = lane_sign_bits<D, E>(a.dsign, q);
     const float fq = lane_factor(q);
-    for (int j0 = 0; j0 < 64; j0 += VPB) {
-        const int j = j0 + wave * VPW + slot;
-        const bool valid = j < a.m;
+    for (int j0 = 0; j0 < NQ; j0 += VPB) {
+        const int j = j0 + wave * VPW + slot;  // column; query q0 + j
+        const bool valid = q0 + j < a.m;
         float v[E];
         {
             uint32_t raw[Raw<D, false>::W], sw[Raw<D, false>::W];
-            load_raw<D, E, false>(a.q, valid ? j : a.m - 1, q, raw);
+            load_raw<D, E, false>(a.q, valid ? q0 + j : a.m - 1, q, raw);
             if (j0 == 0) after_load();
             sign_words<D, false>(lsign, sw);
             stage0<D, false>(raw, sw, v);
@@ -1215,14 +1217,14 @@ __device__ __forceinline__ void rotate_queries(const ScoreArgs &a, float *qt, fl
             v[r] *= fq;
             mx = fmaxf(mx, fabsf(v[r]));
         }
-        if (j < 64) {
+        if (j < NQ) {
 #pragma unroll
             for (int r = 0; r < E; ++r) qt[(q * E + r) * QS + j] = v[r];
         }
         if (qmax) {
 #pragma unroll
             for (int o = 1; o < LPV; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-            if (q == 0 && j < 64) qmax[j] = mx;
+            if (q == 0 && j < NQ) qmax[j] = mx;
         }
     }
 }
@@ -1423,11 +1425,11 @@ __global__ __launch_bounds__(kBlock) void k_score_mfma(const ScoreArgs a) {
     constexpr int HC = D / 2;                 // coordinates per lane half
     constexpr int HW = HC * BITS / 32;        // code words per half row
     constexpr int ROWB = D * BITS / 8;        // code bytes per key
-    constexpr int QS = 65;                    // LDS row stride of the transposed queries
+    constexpr int QS = 33;                    // LDS row stride of the transposed queries
     constexpr int KI = 32 * kScoreTK;         // keys per wave item
-    __shared__ float qt[D * QS];
-    __shared__ float qmax[64];
-    __shared__ __attribute__((aligned(16))) float qinv[64];  // 2^-e_q
+    __shared__ float qt[D * QS];              // this block's 32 queries
+    __shared__ float qmax[32];
+    __shared__ __attribute__((aligned(16))) float qinv[32];  // 2^-e_q
     __shared__ uint2 ptab[1 << (2 * BITS)];   // code pair -> {hi parts, lo parts} of its two levels
     __shared__ u32x4_t stab[RES ? 256 : 1];   // sign byte -> eight +-1 halves
     __shared__ __attribute__((aligned(16))) uint8_t kcb[kWaves][KI * ROWB];
@@ -1436,11 +1438,13 @@ __global__ __launch_bounds__(kBlock) void k_score_mfma(const ScoreArgs a) {
 
     const uint32_t lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t i = lane & 31u, h = lane >> 5;
+    // a block serves one half of the queries (32 each): block b takes half b % RH
+    // (the launch makes the grid a multiple of RH) and items b / RH, b / RH + grid / RH, ...
     const int RH = a.m > 32 ? 2 : 1;
-    const int64_t gw = (int64_t)blockIdx.x * kWaves + wave, nw = (int64_t)gridDim.x * kWaves;
-    const int rh = (int)(gw % RH);
-    const int64_t ntiles = (a.n + 31) / 32, istride = (nw / RH) * kScoreTK;
-    int64_t tile = (gw / RH) * kScoreTK;  // first tile of this wave's item
+    const int rh = (int)(blockIdx.x % RH);
+    const int64_t gw = (int64_t)(blockIdx.x / RH) * kWaves + wave, nw = (int64_t)(gridDim.x / RH) * kWaves;
+    const int64_t ntiles = (a.n + 31) / 32, istride = nw * kScoreTK;
+    int64_t tile = gw * kScoreTK;  // first tile of this wave's item
     uint8_t *kc = kcb[wave];
     uint8_t *ks = ksb[wave];
     float *kn = knb[wave];
@@ -1466,7 +1470,7 @@ __global__ __launch_bounds__(kBlock) void k_score_mfma(const ScoreArgs a) {
         stab[sb] = u32x4_t{w[0], w[1], w[2], w[3]};
     }
     // the first item's keys are copied while the queries are rotated
-    rotate_queries<D, QS>(a, qt, qmax, [&] {
+    rotate_queries<D, QS, 32>(a, qt, qmax, 32 * rh, [&] {
         if (tile < ntiles) stage_keys<ROWB, RES>(a, tile, kc, ks, kn, lane);
     });
     __syncthreads();
@@ -1476,12 +1480,12 @@ __global__ __launch_bounds__(kBlock) void k_score_mfma(const ScoreArgs a) {
         (void)frexpf(qmax[Q], &ex);
         return qmax[Q] > 0.0f ? min(max(15 - ex, -126), 126) : 0;
     };
-    if (threadIdx.x < 64) qinv[threadIdx.x] = ldexpf(1.0f, -qexp((int)threadIdx.x));
+    if (threadIdx.x < 32) qinv[threadIdx.x] = ldexpf(1.0f, -qexp((int)threadIdx.x));
 
-    // A operands of this wave's query half: row i is query 32 rh + i
+    // A operands of this block's query half: row i is query 32 rh + i (column i of qt)
     u32x4_t Ah[S], Al[S];
     {
-        const int Q = 32 * rh + (int)i;
+        const int Q = (int)i;
         const int e = qexp(Q);
 #pragma unroll
         for (int s = 0; s < S; ++s) {
@@ -1528,7 +1532,7 @@ __global__ __launch_bounds__(kBlock) void k_score_mfma(const ScoreArgs a) {
         for (int r4 = 0; r4 < 4; ++r4) {
             // queries 32 rh + 8 r4 + 4 h .. +4: accumulator registers 4 r4 .. +4
             const int Q0 = 32 * rh + 8 * r4 + 4 * (int)h;
-            const float4 qi = *reinterpret_cast<const float4 *>(qinv + Q0);
+            const float4 qi = *reinterpret_cast<const float4 *>(qinv + (Q0 - 32 * rh));
             const float qv[4] = {qi.x, qi.y, qi.z, qi.w};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -1694,10 +1698,13 @@ hipError_t run_score(const ScoreArgs &a, hipStream_t s) {
 template <int D, int BITS, bool RES, bool EXACT>
 hipError_t run_score_mfma(const ScoreArgs &a, hipStream_t s) {
     static const int per_cu = resident_blocks(k_score_mfma<D, BITS, RES, EXACT>);
-    // wave items: (pair of key tiles, query half)
-    const int64_t items = ((a.n + 32 * kScoreTK - 1) / (32 * kScoreTK)) * (a.m > 32 ? 2 : 1);
-    hipLaunchKernelGGL((k_score_mfma<D, BITS, RES, EXACT>), dim3(grid_for(items, kWaves, per_cu)), dim3(kBlock), 0,
-                       s, a);
+    // wave items: (pair of key tiles, query half); a block serves one half, so the grid
+    // is a multiple of the number of halves
+    const int rh = a.m > 32 ? 2 : 1;
+    const int64_t items = ((a.n + 32 * kScoreTK - 1) / (32 * kScoreTK)) * rh;
+    int blocks = grid_for(items, kWaves, per_cu);
+    blocks += (rh - blocks % rh) % rh;
+    hipLaunchKernelGGL((k_score_mfma<D, BITS, RES, EXACT>), dim3(blocks), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
