@@ -245,7 +245,7 @@ def test_residual_decode_arbitrary_inputs(bits, n):
 # ------------------------------------------------------------------ scoring
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
 @pytest.mark.parametrize("d", [64, 128, 256])
-@pytest.mark.parametrize("m,n", [(1, 1), (17, 100), (64, 1037)])
+@pytest.mark.parametrize("m,n", [(1, 1), (17, 100), (64, 1037), (33, 31), (40, 65), (32, 64)])
 def test_score_grid(d, bits, m, n):
     seed = 5 + d
     say("score grid d=%d bits=%d m=%d n=%d" % (d, bits, m, n))
@@ -261,6 +261,33 @@ def test_score_grid(d, bits, m, n):
     assert rel_l2(got[:, nz], ref[:, nz]) <= SCORE_TOL
     per_row = rel_l2(got[:, nz], ref[:, nz], axis=1)
     assert per_row.max() <= SCORE_TOL, per_row.max()
+
+
+@pytest.mark.parametrize("bits", [1, 4])
+def test_score_query_scales(bits):
+    """Queries spanning 60 decades, a zero query and one whose energy sits in a
+    single coordinate: each is scaled into fp16 range by its own power of two."""
+    d, n, seed = 128, 300, 77
+    say("score query scales bits=%d" % bits)
+    rng = np.random.default_rng(bits)
+    keys = rng.standard_normal((n, d)).astype(np.float32)
+    q = rng.standard_normal((40, d))
+    q[0] = 0.0
+    q[1] *= 1e-30
+    q[2] *= 1e30
+    q[3] = 0.0
+    q[3, 17] = 3.0
+    q[4] *= 1e-3
+    q[4, 5] = 1e4
+    q[33:] *= np.logspace(-20, 20, 7)[:, None]
+    q = q.astype(np.float32)
+    codes, norms = oracle.quantize(keys, bits, seed)
+    got = host(rht.score(dev(q), dev(codes), dev(norms), d, bits, seed))
+    ref = oracle.score(q, codes, norms, d, bits, seed)
+    assert np.all(got[0] == 0), "zero query"
+    rows = np.arange(1, len(q))
+    per_row = rel_l2(got[rows], ref[rows], axis=1)
+    assert per_row.max() <= SCORE_TOL, (per_row.max(), rows[per_row.argmax()])
 
 
 def test_zero_rows_is_a_noop():

@@ -50,7 +50,7 @@ def check(got, ref, what):
 
 @pytest.mark.parametrize("unbiased", [False, True])
 @pytest.mark.parametrize("d", [64, 128, 256])
-@pytest.mark.parametrize("m,n", [(1, 1), (17, 100), (64, 1037)])
+@pytest.mark.parametrize("m,n", [(1, 1), (17, 100), (64, 1037), (33, 31), (40, 65), (32, 64)])
 def test_sign_score_grid(unbiased, d, m, n):
     seed = 31 + d
     rng = np.random.default_rng(d * 7 + m + unbiased)
@@ -65,7 +65,7 @@ def test_sign_score_grid(unbiased, d, m, n):
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("d", [64, 128, 256])
-@pytest.mark.parametrize("m,n", [(1, 1), (17, 100), (64, 1037)])
+@pytest.mark.parametrize("m,n", [(1, 1), (17, 100), (64, 1037), (33, 31), (40, 65), (32, 64)])
 def test_residual_score_grid(bits, d, m, n):
     seed = 41 + d
     rng = np.random.default_rng(d * 11 + m + bits)
