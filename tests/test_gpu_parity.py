@@ -218,6 +218,27 @@ def test_residual_grid(d, bits, xdt):
         check_recon(y, ref, tol, "residual decode %s" % odt)
 
 
+@pytest.mark.parametrize("xdt", ["f32", "f16"])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_residual_extreme_rotated_coordinate(bits, xdt):
+    """Rows whose rotation is one-hot: x = D H e_i (entries +-1, exact in fp16), so
+    one rotated coordinate reaches the largest possible |y| = sqrt(d) and all others
+    are 0; scaled copies, and sums of two such rows."""
+    d, seed = 256, 123
+    say("residual extreme rotated coordinate bits=%d x=%s" % (bits, xdt))
+    s = oracle.signs(seed, d).astype(np.float64)
+    idx = np.arange(d)
+    rows = []
+    for i, scale in ((0, 1.0), (1, 1.0), (77, 0.25), (255, 4.0), (128, 1e-3), (3, 100.0)):
+        col = np.where(np.bitwise_count(idx & i) % 2 == 0, 1.0, -1.0)  # H[:, i] (Sylvester)
+        rows.append(scale * s * col)
+    rows.append(rows[0] + rows[1])
+    rows.append(rows[2] - 3 * rows[3])
+    x = np.array(rows * 3).astype(np_dtype(xdt))  # 24 rows: several per wave tile
+    codes, sg, norms, rs = [host(t) for t in rht.residual_quantize(dev(x), bits, seed)]
+    check_residual(x, bits, seed, codes, sg, norms, rs)
+
+
 @pytest.mark.parametrize("bits", [2, 3])
 @pytest.mark.parametrize("n", [1, 15, 17, 1000])
 def test_residual_decode_arbitrary_inputs(bits, n):
