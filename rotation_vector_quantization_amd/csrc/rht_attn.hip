@@ -120,44 +120,49 @@ __device__ __forceinline__ void load_tile(const uint8_t *kc, const uint8_t *vc, 
     t.nrm = (lane < 32 ? kn : vn)[rn];
 }
 
-// Per code byte, the fp16 hi parts (tabh) and lo parts (tabl) of its two
-// levels, low nibble in the low half.  Separate word tables let every lookup
-// land directly in its MFMA operand register.
-// kTabCopies interleaved copies (entry i of copy r at word i * kTabCopies + r);
-// lane l reads copy l % kTabCopies, so only 64 / kTabCopies lanes of a wave
-// compete for the banks of one copy's words.
-#ifndef RHT_ATTN_TAB_COPIES
-#define RHT_ATTN_TAB_COPIES 32
-#endif
-constexpr int kTabCopies = RHT_ATTN_TAB_COPIES;
+// Per code byte, the fp16 hi and lo parts of its two levels, low nibble in
+// the low half.  Entry b is a 256-byte row: kTabCopies copies of the hi word
+// (copy r at byte 4r), then kTabCopies copies of the lo word (at 128 + 4r).
+// Lane l reads copy l % kTabCopies, so the 32 lanes of a half-wave read 32
+// distinct banks whatever their bytes.  The byte address of entry b, copy r
+// is b * 256 + 4r: one v_perm_b32 places the code byte above 4r, and the lo
+// word is the same address plus a constant offset.  Separate word reads land
+// directly in the MFMA operand registers.
+constexpr int kTabCopies = 32;
+constexpr uint32_t kTabRow = 256;  // bytes per entry
 
 struct LevelTables {
-    uint32_t h[256 * kTabCopies], l[256 * kTabCopies];
+    uint32_t w[256 * kTabRow / 4];
 };
 
 // The A operands for four code bytes: hi parts and lo parts, byte i in word i.
-// The reads go through volatile pointers so the compiler keeps them as single
-// ds_read_b32 into the operand registers instead of pairing the hi and lo
-// word of a byte into one two-register read that then needs moves.
-__device__ __forceinline__ void level_operands(const LevelTables &tb, uint32_t copy, uint32_t w, u32x4_t &ah,
+// copy4 = 4 * (lane % kTabCopies).  The reads go through volatile pointers so
+// the compiler keeps them as single ds_read_b32 into the operand registers
+// instead of pairing them into two-register reads that then need moves.
+__device__ __forceinline__ void level_operands(const LevelTables &tb, uint32_t copy4, uint32_t w, u32x4_t &ah,
                                                u32x4_t &al) {
     typedef __attribute__((address_space(3))) const volatile uint32_t lds_word;
-    const lds_word *h = (const lds_word *)tb.h + copy, *l = (const lds_word *)tb.l + copy;
-    const uint32_t b0 = (w & 0xFFu) * kTabCopies, b1 = ((w >> 8) & 0xFFu) * kTabCopies;
-    const uint32_t b2 = ((w >> 16) & 0xFFu) * kTabCopies, b3 = (w >> 24) * kTabCopies;
-    ah = u32x4_t{h[b0], h[b1], h[b2], h[b3]};
-    al = u32x4_t{l[b0], l[b1], l[b2], l[b3]};
+    const char __attribute__((address_space(3))) *base = (const char __attribute__((address_space(3))) *)tb.w;
+    // result bytes: [0] = copy4, [1] = code byte k, [2], [3] = 0
+    const uint32_t o0 = __builtin_amdgcn_perm(w, copy4, 0x0C0C0400u);
+    const uint32_t o1 = __builtin_amdgcn_perm(w, copy4, 0x0C0C0500u);
+    const uint32_t o2 = __builtin_amdgcn_perm(w, copy4, 0x0C0C0600u);
+    const uint32_t o3 = __builtin_amdgcn_perm(w, copy4, 0x0C0C0700u);
+    ah = u32x4_t{*(const lds_word *)(base + o0), *(const lds_word *)(base + o1), *(const lds_word *)(base + o2),
+                 *(const lds_word *)(base + o3)};
+    al = u32x4_t{*(const lds_word *)(base + o0 + 128), *(const lds_word *)(base + o1 + 128),
+                 *(const lds_word *)(base + o2 + 128), *(const lds_word *)(base + o3 + 128)};
 }
 
 // Logits of 16 keys (one 16-byte code piece per lane) against the queries.
-__device__ __forceinline__ floatx4 key_logits(const LevelTables &tb, uint32_t copy, u32x4_t kc,
+__device__ __forceinline__ floatx4 key_logits(const LevelTables &tb, uint32_t copy4, u32x4_t kc,
                                               const u32x4_t (&bh)[4], const u32x4_t (&bl)[4]) {
     // two independent accumulation chains (even and odd K steps)
     floatx4 c[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         u32x4_t ah, al;
-        level_operands(tb, copy, kc[ks], ah, al);
+        level_operands(tb, copy4, kc[ks], ah, al);
         c[ks & 1] = mfma1632(ah, bh[ks], c[ks & 1]);
         c[ks & 1] = mfma1632(ah, bl[ks], c[ks & 1]);
         c[ks & 1] = mfma1632(al, bh[ks], c[ks & 1]);
@@ -216,8 +221,9 @@ __device__ __forceinline__ void attend_tile(const LevelTables &tb, const uint8_t
     const uint32_t j = lane & 15u, g = lane >> 4;
 
     // logits: rows 4g + r of tile 0 are keys 4g + r, of tile 1 keys 16 + 4g + r
-    const floatx4 c0 = key_logits(tb, lane % kTabCopies, k0, bh, bl);
-    const floatx4 c1 = key_logits(tb, lane % kTabCopies, k1, bh, bl);
+    const uint32_t copy4 = 4 * (lane % kTabCopies);
+    const floatx4 c0 = key_logits(tb, copy4, k0, bh, bl);
+    const floatx4 c1 = key_logits(tb, copy4, k1, bh, bl);
     const float4 kn0 = *reinterpret_cast<const float4 *>(nb + 4 * g);
     const float4 kn1 = *reinterpret_cast<const float4 *>(nb + 16 + 4 * g);
     const float4 vn0 = *reinterpret_cast<const float4 *>(nb + 32 + 4 * g);
@@ -284,7 +290,7 @@ __device__ __forceinline__ void attend_tile(const LevelTables &tb, const uint8_t
 #pragma unroll
     for (int nn = 0; nn < 8; ++nn) {
         u32x4_t ah, al;
-        level_operands(tb, lane % kTabCopies, a[nn], ah, al);
+        level_operands(tb, copy4, a[nn], ah, al);
         st.z[nn] = mfma1632(ah, ph, st.z[nn]);
         st.z[nn] = mfma1632(ah, pl, st.z[nn]);
         st.z[nn] = mfma1632(al, ph, st.z[nn]);
@@ -295,11 +301,10 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
     __shared__ LevelTables tb;
     __shared__ __attribute__((aligned(16))) uint8_t vbuf[kAWaves][32 * kVRow];
     __shared__ __attribute__((aligned(16))) float nbuf[kAWaves][64];
-    for (uint32_t k = threadIdx.x; k < 256u * kTabCopies; k += kABlock) {
-        const uint32_t v = k / kTabCopies;
+    for (uint32_t k = threadIdx.x; k < 256u * kTabRow / 4; k += kABlock) {
+        const uint32_t v = k / (kTabRow / 4), r = k % (kTabRow / 4);
         const uint2 e = split2(a.lev[v & 15u], a.lev[v >> 4]);
-        tb.h[k] = e.x;
-        tb.l[k] = e.y;
+        tb.w[k] = r < kTabCopies ? e.x : e.y;
     }
     __syncthreads();
 
