@@ -63,9 +63,6 @@ __device__ __forceinline__ uint2 split2(float x0, float x1) {
 // 2^e as a float for -126 <= e <= 127.
 __device__ __forceinline__ float pow2i(int e) { return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23); }
 
-// 2^e for e <= 0, flushed to 0 below the normal range.
-__device__ __forceinline__ float pow2i_down(int e) { return e < -126 ? 0.0f : pow2i(e); }
-
 // Exponent e with 2^(e-1) <= x < 2^e for a positive normal x.
 __device__ __forceinline__ int exponent_above(float x) {
     return (int)((__builtin_bit_cast(uint32_t, x) >> 23) & 0xFFu) - 126;
@@ -154,20 +151,49 @@ __device__ __forceinline__ void level_operands(const LevelTables &tb, uint32_t c
                  *(const lds_word *)(base + o2 + 128), *(const lds_word *)(base + o3 + 128)};
 }
 
+// B operands of the logits (the rotated queries) in one of two forms.
+//   SPLIT_N (m <= 8): the fp16 parts go to different columns.  Column c < 8
+//     holds the hi parts of query c, column 8 + c its lo parts, so the products
+//     with the hi and with the lo level parts leave sum (Ah + Al) Bh in column
+//     c and sum (Ah + Al) Bl in column 8 + c; their sum is the logit (it also
+//     carries the negligible Al Bl term).  Two MFMAs per K step.
+//   otherwise (m <= 16): column c is query c; hi*hi + hi*lo + lo*hi in one
+//     accumulator.  Three MFMAs per K step.
+template <bool SPLIT_N> struct QueryOperands;
+template <> struct QueryOperands<true> { u32x4_t b[4]; };
+template <> struct QueryOperands<false> { u32x4_t bh[4], bl[4]; };
+
+// The value held by the lane 8 places along in the same row of 16 lanes
+// (DPP row rotate by 8): the partner column of a SPLIT_N accumulator.
+__device__ __forceinline__ float row_ror8(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+}
+
 // Logits of 16 keys (one 16-byte code piece per lane) against the queries.
+template <bool SPLIT_N>
 __device__ __forceinline__ floatx4 key_logits(const LevelTables &tb, uint32_t copy4, u32x4_t kc,
-                                              const u32x4_t (&bh)[4], const u32x4_t (&bl)[4]) {
+                                              const QueryOperands<SPLIT_N> &qo) {
     // two independent accumulation chains (even and odd K steps)
     floatx4 c[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         u32x4_t ah, al;
         level_operands(tb, copy4, kc[ks], ah, al);
-        c[ks & 1] = mfma1632(ah, bh[ks], c[ks & 1]);
-        c[ks & 1] = mfma1632(ah, bl[ks], c[ks & 1]);
-        c[ks & 1] = mfma1632(al, bh[ks], c[ks & 1]);
+        if constexpr (SPLIT_N) {
+            c[ks & 1] = mfma1632(ah, qo.b[ks], c[ks & 1]);
+            c[ks & 1] = mfma1632(al, qo.b[ks], c[ks & 1]);
+        } else {
+            c[ks & 1] = mfma1632(ah, qo.bh[ks], c[ks & 1]);
+            c[ks & 1] = mfma1632(ah, qo.bl[ks], c[ks & 1]);
+            c[ks & 1] = mfma1632(al, qo.bh[ks], c[ks & 1]);
+        }
     }
-    return c[0] + c[1];
+    floatx4 r = c[0] + c[1];
+    if constexpr (SPLIT_N) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] += row_ror8(r[i]);
+    }
+    return r;
 }
 
 // Transpose of an 8 x 8 matrix of nibbles: on entry nibble n of a[t] is
@@ -199,7 +225,8 @@ __device__ __forceinline__ void transpose_nibbles8(uint32_t (&a)[8]) {
 // Per-wave running state of the online softmax.
 struct SoftmaxState {
     float M, l;
-    int ev;              // value scale exponent: P = p ||v|| 2^(14 - ev)
+    float W;             // largest weight p ||v|| seen so far, in the frame of M
+    int ev;              // value scale exponent: P = p ||v|| 2^(14 - ev), 2^(ev-1) <= W < 2^ev
     floatx4 z[8];        // z^T tile n: row 4g + r <-> coordinate 32g + 8r + n, column = query
 };
 
@@ -213,69 +240,83 @@ __device__ __forceinline__ void stage_tile(uint8_t *vb, float *nb, const TileReg
 }
 
 // One staged 32-key tile: logits on MFMA, online softmax, value sums on MFMA.
-// FULL: every key of the tile is < n.
-template <bool FULL>
+// FULL: every key of the tile is < n.  SPLIT_N: the fp16 parts of the query
+// and value weights sit in columns c and 8 + c (both lanes of a column pair
+// hold the same logits, maxima and weights).
+template <bool FULL, bool SPLIT_N>
 __device__ __forceinline__ void attend_tile(const LevelTables &tb, const uint8_t *vb, const float *nb,
-                                            u32x4_t k0, u32x4_t k1, const u32x4_t (&bh)[4], const u32x4_t (&bl)[4],
+                                            u32x4_t k0, u32x4_t k1, const QueryOperands<SPLIT_N> &qo,
                                             float fq, int64_t key0, int64_t n, uint32_t lane, SoftmaxState &st) {
     const uint32_t j = lane & 15u, g = lane >> 4;
 
     // logits: rows 4g + r of tile 0 are keys 4g + r, of tile 1 keys 16 + 4g + r
     const uint32_t copy4 = 4 * (lane % kTabCopies);
-    const floatx4 c0 = key_logits(tb, copy4, k0, bh, bl);
-    const floatx4 c1 = key_logits(tb, copy4, k1, bh, bl);
+    const floatx4 c0 = key_logits<SPLIT_N>(tb, copy4, k0, qo);
+    const floatx4 c1 = key_logits<SPLIT_N>(tb, copy4, k1, qo);
     const float4 kn0 = *reinterpret_cast<const float4 *>(nb + 4 * g);
     const float4 kn1 = *reinterpret_cast<const float4 *>(nb + 16 + 4 * g);
     const float4 vn0 = *reinterpret_cast<const float4 *>(nb + 32 + 4 * g);
     const float4 vn1 = *reinterpret_cast<const float4 *>(nb + 48 + 4 * g);
     const float knr[8] = {kn0.x, kn0.y, kn0.z, kn0.w, kn1.x, kn1.y, kn1.z, kn1.w};
     const float vnr[8] = {vn0.x, vn0.y, vn0.z, vn0.w, vn1.x, vn1.y, vn1.z, vn1.w};
-    float s[8], vmax = 0.0f, smax = -INFINITY;
+    float s[8], vr[8], smax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         const float cv = r < 4 ? c0[r] : c1[r - 4];
         s[r] = cv * knr[r] * fq;
-        float vr = vnr[r];
+        vr[r] = vnr[r];
         if (!FULL) {
             const bool live = key0 + (r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4)) < n;
             s[r] = live ? s[r] : -INFINITY;
-            vr = live ? vr : 0.0f;
+            vr[r] = live ? vr[r] : 0.0f;
         }
         smax = fmaxf(smax, s[r]);
-        vmax = fmaxf(vmax, vr);
     }
     smax = fmaxf(smax, __shfl_xor(smax, 16));
     smax = fmaxf(smax, __shfl_xor(smax, 32));
-    vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
-    vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
     const float Mn = fmaxf(st.M, smax);
-    const int evn = vmax > 0.0f ? max(st.ev, exponent_above(vmax)) : st.ev;
+    const float alpha = __builtin_amdgcn_exp2f(st.M - Mn);
+    // weights w = p ||v||; the fp16 scale of the value operand follows the
+    // largest weight of the chunk so far (not the largest norm: a key of huge
+    // norm and negligible weight must not push the others below fp16 range)
+    float w[8], wmax = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(s[r] - Mn);
+        st.l = r == 0 ? st.l * alpha + pr : st.l + pr;
+        w[r] = pr * vr[r];
+        wmax = fmaxf(wmax, w[r]);
+    }
+    wmax = fmaxf(wmax, __shfl_xor(wmax, 16));
+    wmax = fmaxf(wmax, __shfl_xor(wmax, 32));
+    const float Wn = fmaxf(st.W * alpha, wmax);
+    const int evn = Wn > 0.0f ? exponent_above(Wn) : st.ev;
     // rescale the running sums to the new max and value scale (skipped when
     // neither moved for any query of the wave)
-    const float alpha = __builtin_amdgcn_exp2f(st.M - Mn);
-    const float rz = alpha * pow2i_down(st.ev - evn);
+    const float rz = __builtin_amdgcn_ldexpf(alpha, st.ev - evn);
     st.M = Mn;
+    st.W = Wn;
     st.ev = evn;
-    st.l *= alpha;
     if (__any(rz != 1.0f)) {
 #pragma unroll
         for (int nn = 0; nn < 8; ++nn) st.z[nn] *= rz;
     }
-    const float vs = pow2i(14 - st.ev);
     float P[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(s[r] - st.M);
-        st.l += pr;
-        P[r] = pr * vnr[r] * vs;
-    }
+    for (int r = 0; r < 8; ++r) P[r] = __builtin_amdgcn_ldexpf(w[r], 14 - evn);
     // B operand of the value product: k = 8g + t <-> key (t < 4 ? 4g + t : 16 + 4g + t - 4)
+    // (SPLIT_N: hi parts in columns 0-7, lo parts in columns 8-15)
     u32x4_t ph, pl;
     {
         const uint2 s0 = split2(P[0], P[1]), s1 = split2(P[2], P[3]);
         const uint2 s2 = split2(P[4], P[5]), s3 = split2(P[6], P[7]);
-        ph = u32x4_t{s0.x, s1.x, s2.x, s3.x};
-        pl = u32x4_t{s0.y, s1.y, s2.y, s3.y};
+        if constexpr (SPLIT_N) {
+            const bool lo_col = j >= 8;
+            ph = u32x4_t{lo_col ? s0.y : s0.x, lo_col ? s1.y : s1.x, lo_col ? s2.y : s2.x, lo_col ? s3.y : s3.x};
+        } else {
+            ph = u32x4_t{s0.x, s1.x, s2.x, s3.x};
+            pl = u32x4_t{s0.y, s1.y, s2.y, s3.y};
+        }
     }
     // A operand of tile n: row j <-> coordinate 8j + n, k = 8g + t <-> the key above.
     // Code dword j of key t holds coordinates 8j .. 8j+7; transposed, byte w of
@@ -292,11 +333,12 @@ __device__ __forceinline__ void attend_tile(const LevelTables &tb, const uint8_t
         u32x4_t ah, al;
         level_operands(tb, copy4, a[nn], ah, al);
         st.z[nn] = mfma1632(ah, ph, st.z[nn]);
-        st.z[nn] = mfma1632(ah, pl, st.z[nn]);
+        if constexpr (!SPLIT_N) st.z[nn] = mfma1632(ah, pl, st.z[nn]);
         st.z[nn] = mfma1632(al, ph, st.z[nn]);
     }
 }
 
+template <bool SPLIT_N>
 __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
     __shared__ LevelTables tb;
     __shared__ __attribute__((aligned(16))) uint8_t vbuf[kAWaves][32 * kVRow];
@@ -338,7 +380,7 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
         const float sc = mx > 0.0f ? pow2i(min(14 - exponent_above(mx), 126)) : 1.0f;
         v0 *= sc;
         v1 *= sc;
-        const bool mine = (uint32_t)i == j;
+        const bool mine = (uint32_t)i == (SPLIT_N ? j % 8 : j);
         if (mine) qscale_mine = sc;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
@@ -350,7 +392,7 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
                 qp[ks][w][1] = mine ? p1 : qp[ks][w][1];
             }
     }
-    u32x4_t bh[4], bl[4];
+    QueryOperands<SPLIT_N> qo;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         uint32_t h[4], l[4];
@@ -360,8 +402,13 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
             h[w] = sp.x;
             l[w] = sp.y;
         }
-        bh[ks] = u32x4_t{h[0], h[1], h[2], h[3]};
-        bl[ks] = u32x4_t{l[0], l[1], l[2], l[3]};
+        if constexpr (SPLIT_N) {
+            const bool lo_col = j >= 8;
+            qo.b[ks] = u32x4_t{lo_col ? l[0] : h[0], lo_col ? l[1] : h[1], lo_col ? l[2] : h[2], lo_col ? l[3] : h[3]};
+        } else {
+            qo.bh[ks] = u32x4_t{h[0], h[1], h[2], h[3]};
+            qo.bl[ks] = u32x4_t{l[0], l[1], l[2], l[3]};
+        }
     }
     // logits in base-2 units: s = C * ||k|| * fq
     const float fq = a.scale * 1.4426950408889634f / ((float)kAD * qscale_mine);
@@ -376,7 +423,8 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
     SoftmaxState st;
     st.M = -INFINITY;
     st.l = 0.0f;
-    st.ev = -100;
+    st.W = 0.0f;
+    st.ev = 0;
 #pragma unroll
     for (int nn = 0; nn < 8; ++nn) st.z[nn] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
@@ -389,19 +437,26 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
     while (tile < t_full) {
         stage_tile(vb, nb, ra, lane);
         if (tile + 1 < t_full) load_tile<true>(kc, vc, kn, vn, n, (tile + 1) * 32, lane, rb);
-        attend_tile<true>(tb, vb, nb, ra.k0, ra.k1, bh, bl, fq, tile * 32, n, lane, st);
+        attend_tile<true, SPLIT_N>(tb, vb, nb, ra.k0, ra.k1, qo, fq, tile * 32, n, lane, st);
         if (++tile >= t_full) break;
         stage_tile(vb, nb, rb, lane);
         if (tile + 1 < t_full) load_tile<true>(kc, vc, kn, vn, n, (tile + 1) * 32, lane, ra);
-        attend_tile<true>(tb, vb, nb, rb.k0, rb.k1, bh, bl, fq, tile * 32, n, lane, st);
+        attend_tile<true, SPLIT_N>(tb, vb, nb, rb.k0, rb.k1, qo, fq, tile * 32, n, lane, st);
         ++tile;
     }
     if (t_full < t_end) {
         load_tile<false>(kc, vc, kn, vn, n, t_full * 32, lane, ra);
         stage_tile(vb, nb, ra, lane);
-        attend_tile<false>(tb, vb, nb, ra.k0, ra.k1, bh, bl, fq, t_full * 32, n, lane, st);
+        attend_tile<false, SPLIT_N>(tb, vb, nb, ra.k0, ra.k1, qo, fq, t_full * 32, n, lane, st);
     }
 
+    // SPLIT_N: column j + 8 holds the lo-part sums of query j (DPP, all lanes)
+    if constexpr (SPLIT_N) {
+#pragma unroll
+        for (int nn = 0; nn < 8; ++nn)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st.z[nn][r] += row_ror8(st.z[nn][r]);
+    }
     // l: each lane group g summed its own keys
     float l = st.l;
     l += __shfl_xor(l, 16);
@@ -409,7 +464,7 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
     if ((int)j < a.m) {
         float *rec = a.ws + ((head * a.chunks + chunk) * a.m + j) * kAttnRecord;
         // accumulator row 4g + r of tile n is coordinate 32g + 8r + n
-        const float zs = pow2i(st.ev - 14) * (1.0f / (float)kAD);
+        const float zs = __builtin_amdgcn_ldexpf(1.0f / (float)kAD, st.ev - 14);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float4 lo, hi;
@@ -461,7 +516,11 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(const AttnArgs a) {
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
     const int64_t waves = a.heads * a.chunks;
-    hipLaunchKernelGGL(k_attn_partial, dim3((unsigned)((waves + kAWaves - 1) / kAWaves)), dim3(kABlock), 0, s, a);
+    const dim3 grid((unsigned)((waves + kAWaves - 1) / kAWaves));
+    if (a.m <= 8)
+        hipLaunchKernelGGL(k_attn_partial<true>, grid, dim3(kABlock), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_attn_partial<false>, grid, dim3(kABlock), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t rows = a.heads * a.m;

@@ -25,7 +25,11 @@ def split(x):
     return hi, lo
 
 
-def emulate(q, kc, kn, vc, vn, sk, sv, scale, drop_query_lo=False):
+def emulate(q, kc, kn, vc, vn, sk, sv, scale, drop_query_lo=False, value_scale="weight"):
+    """value_scale: the power of two that brings the value weights p ||v|| into
+    fp16 range comes from the largest weight ("weight", as the kernel does) or
+    from the largest norm alone ("norm", which loses the weights of ordinary
+    keys when a negligible one has a huge norm)."""
     lv = oracle.lloyd_max(BITS)[0].astype(np.float32)
     ch, cl = split(lv)
     Hm = scipy.linalg.hadamard(D).astype(np.float64)
@@ -48,8 +52,8 @@ def emulate(q, kc, kn, vc, vn, sk, sv, scale, drop_query_lo=False):
             fq = np.float32(scale * LOG2E / (D * sq))
             s = c * kn[h] * fq
             p = np.exp2(s - s.max()).astype(np.float32)
-            vmax = vn[h].max()
-            vs = np.float32(2.0 ** (14 - math.frexp(float(vmax))[1])) if vmax > 0 else np.float32(1)
+            wmax = (p * vn[h]).max() if value_scale == "weight" else vn[h].max()
+            vs = np.float32(2.0 ** (14 - math.frexp(float(wmax))[1])) if wmax > 0 else np.float32(1)
             P = p * vn[h] * vs
             ph, pl = split(P)
             z = ((ph[:, None] * ch[vcode]).sum(0, dtype=np.float32) + (pl[:, None] * ch[vcode]).sum(0, dtype=np.float32)
@@ -85,3 +89,27 @@ def test_bound_separates_rounding_from_a_lost_term(scale, qmul):
     # a lost term shows wherever the output depends on the logits at all
     assert (bad / bound).max() > 10, (bad / bound).max()
     assert (good / bound).max() < 0.25, (good / bound).max()
+
+
+def test_value_scale_follows_the_weights():
+    # value norms over 40 decades and near-hard attention: the key that wins the
+    # softmax has an ordinary norm while keys of negligible weight reach 1e20
+    rng = np.random.default_rng(7)
+    heads, m, n = 2, 3, 300
+    x = rng.standard_normal((2 * heads * n, D)).astype(np.float32)
+    x[heads * n:] *= (10.0 ** rng.uniform(-20, 20, heads * n)).astype(np.float32)[:, None]
+    kc, kn = oracle.quantize(x[: heads * n], BITS, 91)
+    vc, vn = oracle.quantize(x[heads * n:], BITS, 92)
+    kc, vc = kc.reshape(heads, n, -1), vc.reshape(heads, n, -1)
+    kn, vn = kn.reshape(heads, n), vn.reshape(heads, n)
+    q = rng.standard_normal((heads, m, D)).astype(np.float32)
+    q[:, 1] *= 1e4
+    scale = 1 / math.sqrt(D)
+    ref = oracle.attention(q, kc, kn, vc, vn, D, BITS, 91, 92, scale)
+    qt, kterm = attention_terms(q, kc, kn, D, BITS, 91, oracle.lloyd_max(BITS)[0],
+                                oracle.signs(91, D).astype(np.float64), scipy.linalg.hadamard(D))
+    bound = attention_bound(q, qt, kterm, decoded(kc, kn, 91), decoded(vc, vn, 92), ref, scale)
+    good = np.linalg.norm(emulate(q, kc, kn, vc, vn, 91, 92, scale) - ref, axis=2)
+    bad = np.linalg.norm(emulate(q, kc, kn, vc, vn, 91, 92, scale, value_scale="norm") - ref, axis=2)
+    assert np.all(good <= bound), (good / bound).max()
+    assert (bad / bound).max() > 10, (bad / bound).max()

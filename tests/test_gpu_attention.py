@@ -88,8 +88,9 @@ def check(got, want, what, q, kc, kn, vc, vn, sk, sv, scale):
     assert np.all(np.isfinite(got))
 
 
+# m <= 8 and m > 8 take different operand layouts: both sides of the switch are covered
 @pytest.mark.parametrize("heads,m,n", [(1, 1, 1), (1, 4, 31), (3, 4, 32), (2, 16, 33), (3, 5, 100),
-                                       (2, 8, 1000), (1, 4, 4099), (5, 3, 257)])
+                                       (2, 8, 1000), (1, 4, 4099), (5, 3, 257), (1, 7, 40), (2, 9, 65)])
 @pytest.mark.parametrize("scale", [1.0 / math.sqrt(D), 1.0])
 def test_attention_grid(heads, m, n, scale):
     rng = np.random.default_rng(heads * 1000 + m * 10 + n)
@@ -102,9 +103,10 @@ def test_attention_grid(heads, m, n, scale):
           q, kc, kn, vc, vn, 51, 52, scale)
 
 
-def test_attention_degenerate_queries_and_values():
+@pytest.mark.parametrize("m", [6, 12])
+def test_attention_degenerate_queries_and_values(m):
     rng = np.random.default_rng(3)
-    heads, m, n = 4, 6, 300
+    heads, n = 4, 300
     kc, kn = coded(rng, heads, n, 61)
     vn_scale = np.ones(heads * n)
     vn_scale[:n] = 0.0                                           # head 0: every value is zero
@@ -115,7 +117,7 @@ def test_attention_degenerate_queries_and_values():
     q[:, 0] = 0.0                                                # uniform weights
     q[:, 1] *= 1e4                                               # hard attention
     q[:, 2] *= 1e-30                                             # tiny query
-    say("attention degenerate cases")
+    say("attention degenerate cases m=%d" % m)
     want = oracle.attention(q, kc, kn, vc, vn, D, BITS, 61, 62, 1.0 / math.sqrt(D))
     got = run(q, kc, kn, vc, vn, 61, 62, 1.0 / math.sqrt(D))
     assert np.all(got[0] == 0.0)
