@@ -82,6 +82,24 @@ __device__ __forceinline__ void fwht128_pairs(float &v0, float &v1, uint32_t lan
     }
 }
 
+// Maximum over the four 16-lane rows of the wave, in every lane (the
+// butterflies across lanes l ^ 16 and l ^ 32) without a trip through LDS.
+// v_permlane16_swap exchanges the odd rows of its first register with the
+// even rows of its second: applied to two copies of x it leaves rows
+// (0, 0, 2, 2) of x in one and rows (1, 1, 3, 3) in the other;
+// v_permlane32_swap does the same with halves of the wave.  Written in asm
+// with both registers as in-out operands (the s_nop covers the wait states
+// between a VALU write and the swap's read).
+__device__ __forceinline__ float max_over_rows(float x) {
+    float a = x, b = x;
+    asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    x = fmaxf(a, b);
+    a = x;
+    b = x;
+    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    return fmaxf(a, b);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
@@ -151,14 +169,19 @@ __device__ __forceinline__ void level_operands(const LevelTables &tb, uint32_t c
                  *(const lds_word *)(base + o2 + 128), *(const lds_word *)(base + o3 + 128)};
 }
 
-// B operands of the logits (the rotated queries) in one of two forms.
-//   SPLIT_N (m <= 8): the fp16 parts go to different columns.  Column c < 8
+// Column layouts of the MFMA B operands (the 16 columns of a 16x16 tile),
+// by the number of query columns QG a layout has room for:
+//   QG = 16 (m <= 16): column c is query c; hi*hi + hi*lo + lo*hi go into
+//     one accumulator, three MFMAs per K step.
+//   QG = 8 (m <= 8): the fp16 parts go to different columns.  Column c < 8
 //     holds the hi parts of query c, column 8 + c its lo parts, so the products
 //     with the hi and with the lo level parts leave sum (Ah + Al) Bh in column
-//     c and sum (Ah + Al) Bl in column 8 + c; their sum is the logit (it also
+//     c and sum (Ah + Al) Bl in column 8 + c; their sum is the result (it also
 //     carries the negligible Al Bl term).  Two MFMAs per K step.
-//   otherwise (m <= 16): column c is query c; hi*hi + hi*lo + lo*hi in one
-//     accumulator.  Three MFMAs per K step.
+//   QG = 4 (m <= 4): as QG = 8 for the logits (columns c and c + 4 repeat
+//     query c % 4).  In the value product, bit 2 of the column is a coordinate
+//     parity: column 8 * part + 4 * parity + query, so that an A row can be a
+//     pair of coordinates of one key, which is one code byte as stored.
 template <bool SPLIT_N> struct QueryOperands;
 template <> struct QueryOperands<true> { u32x4_t b[4]; };
 template <> struct QueryOperands<false> { u32x4_t bh[4], bl[4]; };
@@ -223,12 +246,31 @@ __device__ __forceinline__ void transpose_nibbles8(uint32_t (&a)[8]) {
 }
 
 // Per-wave running state of the online softmax.
+//   QG = 16, 8: z[n] row 4g + r <-> coordinate 32g + 8r + n.
+//   QG = 4:     z[T] row 4g + r <-> coordinates 32g + 8r + 2T + parity.
+template <int QG>
 struct SoftmaxState {
+    static constexpr int kZ = QG == 4 ? 4 : 8;
     float M, l;
     float W;             // largest weight p ||v|| seen so far, in the frame of M
     int ev;              // value scale exponent: P = p ||v|| 2^(14 - ev), 2^(ev-1) <= W < 2^ev
-    floatx4 z[8];        // z^T tile n: row 4g + r <-> coordinate 32g + 8r + n, column = query
+    floatx4 z[kZ];       // rotated value sums in the accumulator layout above
 };
+
+// The A operands for byte T of four code words (word t -> register t): the
+// hi and lo level parts of the two nibbles, as level_operands.
+__device__ __forceinline__ void level_operands_byte(const LevelTables &tb, uint32_t copy4, uint32_t w0, uint32_t w1,
+                                                    uint32_t w2, uint32_t w3, uint32_t sel, u32x4_t &ah,
+                                                    u32x4_t &al) {
+    typedef __attribute__((address_space(3))) const volatile uint32_t lds_word;
+    const char __attribute__((address_space(3))) *base = (const char __attribute__((address_space(3))) *)tb.w;
+    const uint32_t o0 = __builtin_amdgcn_perm(w0, copy4, sel), o1 = __builtin_amdgcn_perm(w1, copy4, sel);
+    const uint32_t o2 = __builtin_amdgcn_perm(w2, copy4, sel), o3 = __builtin_amdgcn_perm(w3, copy4, sel);
+    ah = u32x4_t{*(const lds_word *)(base + o0), *(const lds_word *)(base + o1), *(const lds_word *)(base + o2),
+                 *(const lds_word *)(base + o3)};
+    al = u32x4_t{*(const lds_word *)(base + o0 + 128), *(const lds_word *)(base + o1 + 128),
+                 *(const lds_word *)(base + o2 + 128), *(const lds_word *)(base + o3 + 128)};
+}
 
 // Copy a tile's value codes (key r at vb + r * kVRow) and norms into LDS.
 // Done before the next tile's loads are issued: waiting for this tile's
@@ -240,13 +282,16 @@ __device__ __forceinline__ void stage_tile(uint8_t *vb, float *nb, const TileReg
 }
 
 // One staged 32-key tile: logits on MFMA, online softmax, value sums on MFMA.
-// FULL: every key of the tile is < n.  SPLIT_N: the fp16 parts of the query
-// and value weights sit in columns c and 8 + c (both lanes of a column pair
-// hold the same logits, maxima and weights).
-template <bool FULL, bool SPLIT_N>
+// FULL: every key of the tile is < n.  QG: the column layout (every lane of a
+// column group of one query holds the same logits, maxima and weights).
+// psel (QG = 4): per-lane byte selectors that place the lane's fp16 part of an
+// even or odd weight of a pair in the half of the B word its parity names.
+template <bool FULL, int QG>
 __device__ __forceinline__ void attend_tile(const LevelTables &tb, const uint8_t *vb, const float *nb,
-                                            u32x4_t k0, u32x4_t k1, const QueryOperands<SPLIT_N> &qo,
-                                            float fq, int64_t key0, int64_t n, uint32_t lane, SoftmaxState &st) {
+                                            u32x4_t k0, u32x4_t k1, const QueryOperands<(QG <= 8)> &qo,
+                                            uint2 psel, float fq, int64_t key0, int64_t n, uint32_t lane,
+                                            SoftmaxState<QG> &st) {
+    constexpr bool SPLIT_N = QG <= 8;
     const uint32_t j = lane & 15u, g = lane >> 4;
 
     // logits: rows 4g + r of tile 0 are keys 4g + r, of tile 1 keys 16 + 4g + r
@@ -272,8 +317,7 @@ __device__ __forceinline__ void attend_tile(const LevelTables &tb, const uint8_t
         }
         smax = fmaxf(smax, s[r]);
     }
-    smax = fmaxf(smax, __shfl_xor(smax, 16));
-    smax = fmaxf(smax, __shfl_xor(smax, 32));
+    smax = max_over_rows(smax);
     const float Mn = fmaxf(st.M, smax);
     const float alpha = __builtin_amdgcn_exp2f(st.M - Mn);
     // weights w = p ||v||; the fp16 scale of the value operand follows the
@@ -287,8 +331,7 @@ __device__ __forceinline__ void attend_tile(const LevelTables &tb, const uint8_t
         w[r] = pr * vr[r];
         wmax = fmaxf(wmax, w[r]);
     }
-    wmax = fmaxf(wmax, __shfl_xor(wmax, 16));
-    wmax = fmaxf(wmax, __shfl_xor(wmax, 32));
+    wmax = max_over_rows(wmax);
     const float Wn = fmaxf(st.W * alpha, wmax);
     const int evn = Wn > 0.0f ? exponent_above(Wn) : st.ev;
     // rescale the running sums to the new max and value scale (skipped when
@@ -299,11 +342,43 @@ __device__ __forceinline__ void attend_tile(const LevelTables &tb, const uint8_t
     st.ev = evn;
     if (__any(rz != 1.0f)) {
 #pragma unroll
-        for (int nn = 0; nn < 8; ++nn) st.z[nn] *= rz;
+        for (int nn = 0; nn < SoftmaxState<QG>::kZ; ++nn) st.z[nn] *= rz;
     }
     float P[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) P[r] = __builtin_amdgcn_ldexpf(w[r], 14 - evn);
+    // value codes: word tt = code dword j (coordinates 8j .. 8j+7) of key
+    // (tt < 4 ? 4g + tt : 16 + 4g + tt - 4), the keys of this lane's P values
+    uint32_t a[8];
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+        const uint32_t key = tt < 4 ? 4 * g + tt : 16 + 4 * g + (tt - 4);
+        a[tt] = *reinterpret_cast<const uint32_t *>(vb + key * kVRow + 4 * j);
+    }
+    if constexpr (QG == 4) {
+        // K step s covers keys 16s + 4g + t (t = 0..3), slots 2t + parity.
+        // B: slot 2t + parity holds the lane's fp16 part of P[4s + t] if the
+        // parity is the column's, else 0.  A for tile T, row j: coordinates
+        // 8j + 2T + parity, byte T of the key's code dword j.
+        const uint2 q0 = split2(P[0], P[1]), q1 = split2(P[2], P[3]);
+        const uint2 q2 = split2(P[4], P[5]), q3 = split2(P[6], P[7]);
+        const u32x4_t b0 = u32x4_t{__builtin_amdgcn_perm(q0.y, q0.x, psel.x), __builtin_amdgcn_perm(q0.y, q0.x, psel.y),
+                                   __builtin_amdgcn_perm(q1.y, q1.x, psel.x), __builtin_amdgcn_perm(q1.y, q1.x, psel.y)};
+        const u32x4_t b1 = u32x4_t{__builtin_amdgcn_perm(q2.y, q2.x, psel.x), __builtin_amdgcn_perm(q2.y, q2.x, psel.y),
+                                   __builtin_amdgcn_perm(q3.y, q3.x, psel.x), __builtin_amdgcn_perm(q3.y, q3.x, psel.y)};
+#pragma unroll
+        for (int T = 0; T < 4; ++T) {
+            const uint32_t sel = 0x0C0C0000u | ((4u + T) << 8);  // [0] = copy4, [1] = byte T
+            u32x4_t ah, al;
+            level_operands_byte(tb, copy4, a[0], a[1], a[2], a[3], sel, ah, al);
+            st.z[T] = mfma1632(ah, b0, st.z[T]);
+            st.z[T] = mfma1632(al, b0, st.z[T]);
+            level_operands_byte(tb, copy4, a[4], a[5], a[6], a[7], sel, ah, al);
+            st.z[T] = mfma1632(ah, b1, st.z[T]);
+            st.z[T] = mfma1632(al, b1, st.z[T]);
+        }
+        return;
+    } else {
     // B operand of the value product: k = 8g + t <-> key (t < 4 ? 4g + t : 16 + 4g + t - 4)
     // (SPLIT_N: hi parts in columns 0-7, lo parts in columns 8-15)
     u32x4_t ph, pl;
@@ -319,14 +394,8 @@ __device__ __forceinline__ void attend_tile(const LevelTables &tb, const uint8_t
         }
     }
     // A operand of tile n: row j <-> coordinate 8j + n, k = 8g + t <-> the key above.
-    // Code dword j of key t holds coordinates 8j .. 8j+7; transposed, byte w of
-    // word n holds coordinate 8j + n of keys 2w, 2w+1: one table entry each.
-    uint32_t a[8];
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-        const uint32_t key = tt < 4 ? 4 * g + tt : 16 + 4 * g + (tt - 4);
-        a[tt] = *reinterpret_cast<const uint32_t *>(vb + key * kVRow + 4 * j);
-    }
+    // Transposed, byte w of word n holds coordinate 8j + n of keys 2w, 2w+1:
+    // one table entry each.
     transpose_nibbles8(a);
 #pragma unroll
     for (int nn = 0; nn < 8; ++nn) {
@@ -336,10 +405,12 @@ __device__ __forceinline__ void attend_tile(const LevelTables &tb, const uint8_t
         if constexpr (!SPLIT_N) st.z[nn] = mfma1632(ah, pl, st.z[nn]);
         st.z[nn] = mfma1632(al, ph, st.z[nn]);
     }
+    }
 }
 
-template <bool SPLIT_N>
+template <int QG>
 __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
+    constexpr bool SPLIT_N = QG <= 8;
     __shared__ LevelTables tb;
     __shared__ __attribute__((aligned(16))) uint8_t vbuf[kAWaves][32 * kVRow];
     __shared__ __attribute__((aligned(16))) float nbuf[kAWaves][64];
@@ -380,7 +451,7 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
         const float sc = mx > 0.0f ? pow2i(min(14 - exponent_above(mx), 126)) : 1.0f;
         v0 *= sc;
         v1 *= sc;
-        const bool mine = (uint32_t)i == (SPLIT_N ? j % 8 : j);
+        const bool mine = (uint32_t)i == j % (uint32_t)QG;
         if (mine) qscale_mine = sc;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
@@ -420,13 +491,22 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
     uint8_t *vb = vbuf[wave];
     float *nb = nbuf[wave];
 
-    SoftmaxState st;
+    SoftmaxState<QG> st;
     st.M = -INFINITY;
     st.l = 0.0f;
     st.W = 0.0f;
     st.ev = 0;
 #pragma unroll
-    for (int nn = 0; nn < 8; ++nn) st.z[nn] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int nn = 0; nn < SoftmaxState<QG>::kZ; ++nn) st.z[nn] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    // QG = 4: byte selectors of this lane's B words (bytes 0-3 of the perm
+    // source are the hi pair, 4-7 the lo pair; an even weight is the low half)
+    uint2 psel = make_uint2(0u, 0u);
+    if constexpr (QG == 4) {
+        const uint32_t b = j >= 8 ? 4u : 0u, par = (j >> 2) & 1u;
+        const uint32_t ev16 = b | ((b + 1) << 8), od16 = (b + 2) | ((b + 3) << 8);
+        psel.x = par ? (ev16 << 16) | 0x0C0Cu : 0x0C0C0000u | ev16;
+        psel.y = par ? (od16 << 16) | 0x0C0Cu : 0x0C0C0000u | od16;
+    }
 
     // full tiles with the next one's loads in flight (two register sets), then
     // the partial last tile if n is not a multiple of 32
@@ -437,23 +517,23 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
     while (tile < t_full) {
         stage_tile(vb, nb, ra, lane);
         if (tile + 1 < t_full) load_tile<true>(kc, vc, kn, vn, n, (tile + 1) * 32, lane, rb);
-        attend_tile<true, SPLIT_N>(tb, vb, nb, ra.k0, ra.k1, qo, fq, tile * 32, n, lane, st);
+        attend_tile<true, QG>(tb, vb, nb, ra.k0, ra.k1, qo, psel, fq, tile * 32, n, lane, st);
         if (++tile >= t_full) break;
         stage_tile(vb, nb, rb, lane);
         if (tile + 1 < t_full) load_tile<true>(kc, vc, kn, vn, n, (tile + 1) * 32, lane, ra);
-        attend_tile<true, SPLIT_N>(tb, vb, nb, rb.k0, rb.k1, qo, fq, tile * 32, n, lane, st);
+        attend_tile<true, QG>(tb, vb, nb, rb.k0, rb.k1, qo, psel, fq, tile * 32, n, lane, st);
         ++tile;
     }
     if (t_full < t_end) {
         load_tile<false>(kc, vc, kn, vn, n, t_full * 32, lane, ra);
         stage_tile(vb, nb, ra, lane);
-        attend_tile<false, SPLIT_N>(tb, vb, nb, ra.k0, ra.k1, qo, fq, t_full * 32, n, lane, st);
+        attend_tile<false, QG>(tb, vb, nb, ra.k0, ra.k1, qo, psel, fq, t_full * 32, n, lane, st);
     }
 
-    // SPLIT_N: column j + 8 holds the lo-part sums of query j (DPP, all lanes)
+    // SPLIT_N: column j + 8 holds the lo-part sums of column j (DPP, all lanes)
     if constexpr (SPLIT_N) {
 #pragma unroll
-        for (int nn = 0; nn < 8; ++nn)
+        for (int nn = 0; nn < SoftmaxState<QG>::kZ; ++nn)
 #pragma unroll
             for (int r = 0; r < 4; ++r) st.z[nn][r] += row_ror8(st.z[nn][r]);
     }
@@ -461,7 +541,22 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
     float l = st.l;
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    if ((int)j < a.m) {
+    if constexpr (QG == 4) {
+        // lane (column j < 8): query j % 4, coordinates of parity j / 4
+        const uint32_t qi = j & 3u, par = j >> 2;
+        if (j < 8 && (int)qi < a.m) {
+            float *rec = a.ws + ((head * a.chunks + chunk) * a.m + qi) * kAttnRecord;
+            const float zs = __builtin_amdgcn_ldexpf(1.0f / (float)kAD, st.ev - 14);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int T = 0; T < 4; ++T) rec[32 * g + 8 * r + 2 * T + par] = st.z[T][r] * zs;
+            if (g == 0 && par == 0) {
+                rec[kAD] = st.M;
+                rec[kAD + 1] = l;
+            }
+        }
+    } else if ((int)j < a.m) {
         float *rec = a.ws + ((head * a.chunks + chunk) * a.m + j) * kAttnRecord;
         // accumulator row 4g + r of tile n is coordinate 32g + 8r + n
         const float zs = __builtin_amdgcn_ldexpf(1.0f / (float)kAD, st.ev - 14);
@@ -517,10 +612,12 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(const AttnArgs a) {
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
     const int64_t waves = a.heads * a.chunks;
     const dim3 grid((unsigned)((waves + kAWaves - 1) / kAWaves));
-    if (a.m <= 8)
-        hipLaunchKernelGGL(k_attn_partial<true>, grid, dim3(kABlock), 0, s, a);
+    if (a.m <= 4)
+        hipLaunchKernelGGL(k_attn_partial<4>, grid, dim3(kABlock), 0, s, a);
+    else if (a.m <= 8)
+        hipLaunchKernelGGL(k_attn_partial<8>, grid, dim3(kABlock), 0, s, a);
     else
-        hipLaunchKernelGGL(k_attn_partial<false>, grid, dim3(kABlock), 0, s, a);
+        hipLaunchKernelGGL(k_attn_partial<16>, grid, dim3(kABlock), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t rows = a.heads * a.m;
