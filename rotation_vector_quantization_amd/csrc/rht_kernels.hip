@@ -268,14 +268,22 @@ __device__ __forceinline__ void build_lut_lev(u32x4_t *lut, const float *thr, co
 
 // nearest_code on the level-carrying table of NCELL cells at offset OFF; also
 // returns l16 = 16 c[code].
+// The table cell of y16, and the code and level within a cell: split so that
+// a caller can issue several cell reads before it uses them.
 template <int NCELL, int OFF, bool CLAMP>
-__device__ __forceinline__ uint32_t nearest_code_lev_t(const u32x4_t *lut, float y16, float &l16) {
+__device__ __forceinline__ u32x4_t lut_cell(const u32x4_t *lut, float y16) {
     int b = __builtin_bit_cast(int, y16 + (8388608.0f + (float)OFF));
     if constexpr (CLAMP) b = min(max(b, 0x4B000000), 0x4B000000 + NCELL - 1);
-    const u32x4_t e = lut[b - 0x4B000000];
+    return lut[b - 0x4B000000];
+}
+__device__ __forceinline__ uint32_t code_in_cell(const u32x4_t &e, float y16, float &l16) {
     const bool up = y16 >= __builtin_bit_cast(float, e[0]);
     l16 = __builtin_bit_cast(float, up ? e[3] : e[2]);
     return e[1] + (up ? 1u : 0u);
+}
+template <int NCELL, int OFF, bool CLAMP>
+__device__ __forceinline__ uint32_t nearest_code_lev_t(const u32x4_t *lut, float y16, float &l16) {
+    return code_in_cell(lut_cell<NCELL, OFF, CLAMP>(lut, y16), y16, l16);
 }
 template <int D>
 __device__ __forceinline__ uint32_t nearest_code_lev(const u32x4_t *lut, float y16, float &l16) {
@@ -690,13 +698,21 @@ __global__ __launch_bounds__(kBlock) void k_residual_quantize_mfma256(const Quan
         float r2 = 0.0f, r1 = 0.0f;
 #pragma unroll
         for (int blk = 0; blk < 8; ++blk) {
-            // coordinates 32 blk + 8 g + 4 mh + r, in order t = 4 mh + r
+            // coordinates 32 blk + 8 g + 4 mh + r, in order t = 4 mh + r; the
+            // eight table reads of a block are issued together, then used
+            float y[8];
+            u32x4_t e[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                y[t] = c[blk][t >> 2][t & 3] * inv16;
+                e[t] = lut_cell<LT::kCells, LT::kOff, false>(lutl, y[t]);
+            }
             uint32_t code = 0u, neg = 0u;
 #pragma unroll
             for (int t = 7; t >= 0; --t) {
-                const float y16 = c[blk][t >> 2][t & 3] * inv16;
+                const float y16 = y[t];
                 float l16;
-                const uint32_t cd = nearest_code_lev_t<LT::kCells, LT::kOff, false>(lutl, y16, l16);
+                const uint32_t cd = code_in_cell(e[t], y16, l16);
                 code |= cd << (CB * t);
                 const float rho = y16 - l16;
                 r2 = fmaf(rho, rho, r2);
