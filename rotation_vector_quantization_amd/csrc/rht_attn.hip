@@ -281,6 +281,61 @@ __device__ __forceinline__ void stage_tile(uint8_t *vb, float *nb, const TileReg
     nb[lane] = t.nrm;
 }
 
+// Value sums of a tile, layout QG = 4.  K step s covers keys 16s + 4g + t
+// (t = 0..3), slots 2t + parity.  B: slot 2t + parity holds the lane's fp16
+// part of P[4s + t] if the parity is the column's, else 0.  A for tile T, row
+// j: coordinates 8j + 2T + parity, byte T of the key's code dword j (a[t] for
+// s = 0, a[4 + t] for s = 1).
+__device__ __forceinline__ void value_sums_by_parity(const LevelTables &tb, uint32_t copy4, const uint32_t (&a)[8],
+                                                     const float (&P)[8], uint2 psel, floatx4 (&z)[4]) {
+    const uint2 q0 = split2(P[0], P[1]), q1 = split2(P[2], P[3]);
+    const uint2 q2 = split2(P[4], P[5]), q3 = split2(P[6], P[7]);
+    const u32x4_t b0 = u32x4_t{__builtin_amdgcn_perm(q0.y, q0.x, psel.x), __builtin_amdgcn_perm(q0.y, q0.x, psel.y),
+                               __builtin_amdgcn_perm(q1.y, q1.x, psel.x), __builtin_amdgcn_perm(q1.y, q1.x, psel.y)};
+    const u32x4_t b1 = u32x4_t{__builtin_amdgcn_perm(q2.y, q2.x, psel.x), __builtin_amdgcn_perm(q2.y, q2.x, psel.y),
+                               __builtin_amdgcn_perm(q3.y, q3.x, psel.x), __builtin_amdgcn_perm(q3.y, q3.x, psel.y)};
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+        const uint32_t sel = 0x0C0C0000u | ((4u + T) << 8);  // [0] = copy4, [1] = byte T
+        u32x4_t ah, al;
+        level_operands_byte(tb, copy4, a[0], a[1], a[2], a[3], sel, ah, al);
+        z[T] = mfma1632(ah, b0, z[T]);
+        z[T] = mfma1632(al, b0, z[T]);
+        level_operands_byte(tb, copy4, a[4], a[5], a[6], a[7], sel, ah, al);
+        z[T] = mfma1632(ah, b1, z[T]);
+        z[T] = mfma1632(al, b1, z[T]);
+    }
+}
+
+// Value sums of a tile, layouts QG = 8 (SPLIT_N) and 16.  B: k = 8g + t <->
+// key (t < 4 ? 4g + t : 16 + 4g + t - 4) (SPLIT_N: hi parts in columns 0-7, lo
+// parts in columns 8-15).  A of tile n: row j <-> coordinate 8j + n, k = 8g + t
+// <-> the key above; after the transpose, byte w of word n holds coordinate
+// 8j + n of keys 2w, 2w+1: one table entry each.
+template <bool SPLIT_N>
+__device__ __forceinline__ void value_sums_transposed(const LevelTables &tb, uint32_t copy4, uint32_t (&a)[8],
+                                                      const float (&P)[8], uint32_t j, floatx4 (&z)[8]) {
+    const uint2 s0 = split2(P[0], P[1]), s1 = split2(P[2], P[3]);
+    const uint2 s2 = split2(P[4], P[5]), s3 = split2(P[6], P[7]);
+    u32x4_t ph, pl;
+    if constexpr (SPLIT_N) {
+        const bool lo_col = j >= 8;
+        ph = u32x4_t{lo_col ? s0.y : s0.x, lo_col ? s1.y : s1.x, lo_col ? s2.y : s2.x, lo_col ? s3.y : s3.x};
+    } else {
+        ph = u32x4_t{s0.x, s1.x, s2.x, s3.x};
+        pl = u32x4_t{s0.y, s1.y, s2.y, s3.y};
+    }
+    transpose_nibbles8(a);
+#pragma unroll
+    for (int nn = 0; nn < 8; ++nn) {
+        u32x4_t ah, al;
+        level_operands(tb, copy4, a[nn], ah, al);
+        z[nn] = mfma1632(ah, ph, z[nn]);
+        if constexpr (!SPLIT_N) z[nn] = mfma1632(ah, pl, z[nn]);
+        z[nn] = mfma1632(al, ph, z[nn]);
+    }
+}
+
 // One staged 32-key tile: logits on MFMA, online softmax, value sums on MFMA.
 // FULL: every key of the tile is < n.  QG: the column layout (every lane of a
 // column group of one query holds the same logits, maxima and weights).
@@ -355,57 +410,10 @@ __device__ __forceinline__ void attend_tile(const LevelTables &tb, const uint8_t
         const uint32_t key = tt < 4 ? 4 * g + tt : 16 + 4 * g + (tt - 4);
         a[tt] = *reinterpret_cast<const uint32_t *>(vb + key * kVRow + 4 * j);
     }
-    if constexpr (QG == 4) {
-        // K step s covers keys 16s + 4g + t (t = 0..3), slots 2t + parity.
-        // B: slot 2t + parity holds the lane's fp16 part of P[4s + t] if the
-        // parity is the column's, else 0.  A for tile T, row j: coordinates
-        // 8j + 2T + parity, byte T of the key's code dword j.
-        const uint2 q0 = split2(P[0], P[1]), q1 = split2(P[2], P[3]);
-        const uint2 q2 = split2(P[4], P[5]), q3 = split2(P[6], P[7]);
-        const u32x4_t b0 = u32x4_t{__builtin_amdgcn_perm(q0.y, q0.x, psel.x), __builtin_amdgcn_perm(q0.y, q0.x, psel.y),
-                                   __builtin_amdgcn_perm(q1.y, q1.x, psel.x), __builtin_amdgcn_perm(q1.y, q1.x, psel.y)};
-        const u32x4_t b1 = u32x4_t{__builtin_amdgcn_perm(q2.y, q2.x, psel.x), __builtin_amdgcn_perm(q2.y, q2.x, psel.y),
-                                   __builtin_amdgcn_perm(q3.y, q3.x, psel.x), __builtin_amdgcn_perm(q3.y, q3.x, psel.y)};
-#pragma unroll
-        for (int T = 0; T < 4; ++T) {
-            const uint32_t sel = 0x0C0C0000u | ((4u + T) << 8);  // [0] = copy4, [1] = byte T
-            u32x4_t ah, al;
-            level_operands_byte(tb, copy4, a[0], a[1], a[2], a[3], sel, ah, al);
-            st.z[T] = mfma1632(ah, b0, st.z[T]);
-            st.z[T] = mfma1632(al, b0, st.z[T]);
-            level_operands_byte(tb, copy4, a[4], a[5], a[6], a[7], sel, ah, al);
-            st.z[T] = mfma1632(ah, b1, st.z[T]);
-            st.z[T] = mfma1632(al, b1, st.z[T]);
-        }
-        return;
-    } else {
-    // B operand of the value product: k = 8g + t <-> key (t < 4 ? 4g + t : 16 + 4g + t - 4)
-    // (SPLIT_N: hi parts in columns 0-7, lo parts in columns 8-15)
-    u32x4_t ph, pl;
-    {
-        const uint2 s0 = split2(P[0], P[1]), s1 = split2(P[2], P[3]);
-        const uint2 s2 = split2(P[4], P[5]), s3 = split2(P[6], P[7]);
-        if constexpr (SPLIT_N) {
-            const bool lo_col = j >= 8;
-            ph = u32x4_t{lo_col ? s0.y : s0.x, lo_col ? s1.y : s1.x, lo_col ? s2.y : s2.x, lo_col ? s3.y : s3.x};
-        } else {
-            ph = u32x4_t{s0.x, s1.x, s2.x, s3.x};
-            pl = u32x4_t{s0.y, s1.y, s2.y, s3.y};
-        }
-    }
-    // A operand of tile n: row j <-> coordinate 8j + n, k = 8g + t <-> the key above.
-    // Transposed, byte w of word n holds coordinate 8j + n of keys 2w, 2w+1:
-    // one table entry each.
-    transpose_nibbles8(a);
-#pragma unroll
-    for (int nn = 0; nn < 8; ++nn) {
-        u32x4_t ah, al;
-        level_operands(tb, copy4, a[nn], ah, al);
-        st.z[nn] = mfma1632(ah, ph, st.z[nn]);
-        if constexpr (!SPLIT_N) st.z[nn] = mfma1632(ah, pl, st.z[nn]);
-        st.z[nn] = mfma1632(al, ph, st.z[nn]);
-    }
-    }
+    if constexpr (QG == 4)
+        value_sums_by_parity(tb, copy4, a, P, psel, st.z);
+    else
+        value_sums_transposed<SPLIT_N>(tb, copy4, a, P, j, st.z);
 }
 
 template <int QG>
