@@ -403,6 +403,9 @@ def main():
     achieved = per_launch_bytes / (kern[dom] / 1e3) / 1e9
     kname = {"quantize": "k_quantize", "dequantize": "k_dequantize"}[dom]
     traffic = load_traffic(kname)
+    # the kernel the library dispatches for d = 128 fp16 (the generic one if
+    # RHT_HADAMARD=valu moves the transform off MFMA)
+    kfull = kname + ("<128, ...> (generic)" if os.environ.get("RHT_HADAMARD") == "valu" else "_mfma128")
 
     out = {
         "metric": "vectors/s + achieved HBM GB/s (% of peak), RHT 4-bit quant/dequant d=128",
@@ -424,7 +427,7 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBS,
+            "bound": "hbm", "kernel": kfull, "achieved": achieved, "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
         },
