@@ -175,7 +175,8 @@ rht_status rht_residual_score(const float *q, int32_t m, const uint8_t *codes, c
  *              m, n, d) bytes, owned by the caller; its contents on entry are
  *              ignored and on return unspecified.  Calls that may run at the
  *              same time must not share it.
- *   d = 128 and bits = 4 only.  n >= 1 when heads > 0; heads = 0 is a no-op.
+ *   d = 128 and bits = 4 only.  1 <= n <= 2^26 keys per head when heads > 0
+ *   (RHT_E_COUNT otherwise); heads = 0 is a no-op.
  * Returns RHT_E_WORKSPACE (after the other checks) when workspace_bytes is
  * too small. */
 rht_status rht_attention(const float *q, int32_t m, const uint8_t *k_codes, const float *k_norms,

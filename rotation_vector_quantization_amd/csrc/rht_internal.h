@@ -65,6 +65,9 @@ struct ScoreArgs {
 // two pad floats) per (head, chunk, query) in `ws`.
 constexpr int kAttnRecord = 132;
 constexpr int kAttnMaxQueries = 16;
+// Keys per head: the attention kernel addresses a head's code rows with
+// 32-bit byte offsets (row * 64 < 2^32).
+constexpr int64_t kAttnMaxKeys = int64_t(1) << 26;
 
 struct AttnArgs {
     const float *q;      // [heads][m][128]

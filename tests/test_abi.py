@@ -127,6 +127,8 @@ def test_attention_validation_order(lib):
     for m in (0, 17, -1):
         assert _att(lib, m=m, d=64) == E_COUNT
     assert _att(lib, n=0, d=64) == E_COUNT
+    assert _att(lib, n=(1 << 26) + 1, d=64) == E_COUNT        # 32-bit row offsets per head
+    assert _att(lib, n=1 << 26, d=64) == E_DIM                # largest n passes the count check
     for d in (64, 256, 100):
         assert _att(lib, d=d, bits=2) == E_DIM
     for b in (1, 2, 3, 5):
@@ -149,6 +151,7 @@ def test_attention_workspace_bytes(lib):
     assert rht.rht_attention_workspace_bytes(0, 4, 100, 128) == 0
     assert rht.rht_attention_workspace_bytes(1, 17, 100, 128) == 0
     assert rht.rht_attention_workspace_bytes(1, 4, 100, 64) == 0
+    assert rht.rht_attention_workspace_bytes(1, 4, (1 << 26) + 1, 128) == 0
 
 
 def test_sign_and_residual_score_validation(lib):
