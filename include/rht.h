@@ -167,7 +167,8 @@ rht_status rht_residual_score(const float *q, int32_t m, const uint8_t *codes, c
  *   out[h][i] = sum_j softmax_j(scale * <q[h][i], k~[h][j]>) v~[h][j]
  * where k~, v~ are the vectors rht_dequantize would decode (keys with seed_k,
  * values with seed_v).  No mask; scale is applied as given (e.g. 1/sqrt(d)).
- *   q          [heads][m][d] fp32, 1 <= m <= 16.
+ *   q          [heads][m][d] fp32, 1 <= m <= 16, heads * m <= 2^24
+ *              (RHT_E_COUNT otherwise).
  *   k_codes, v_codes [heads][n][bits*d/8] and k_norms, v_norms [heads][n]
  *              fp32, as written by rht_quantize(..., RHT_SCALE_NORM, seed, ...).
  *   out        [heads][m][d] fp32, written.

@@ -232,7 +232,8 @@ int64_t attention_chunks(int64_t heads, int64_t n) {
 }
 
 bool attention_args_ok(int64_t heads, int32_t m, int64_t n) {
-    return heads >= 0 && m >= 1 && m <= kAttnMaxQueries && (heads == 0 || (n >= 1 && n <= kAttnMaxKeys));
+    return heads >= 0 && m >= 1 && m <= kAttnMaxQueries && heads <= kAttnMaxRows / m &&
+           (heads == 0 || (n >= 1 && n <= kAttnMaxKeys));
 }
 
 std::atomic<int> g_cu[64];

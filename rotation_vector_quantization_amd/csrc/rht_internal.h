@@ -68,6 +68,10 @@ constexpr int kAttnMaxQueries = 16;
 // Keys per head: the attention kernel addresses a head's code rows with
 // 32-bit byte offsets (row * 64 < 2^32).
 constexpr int64_t kAttnMaxKeys = int64_t(1) << 26;
+// (head, query) rows per call: keeps both attention grids far below 2^32
+// work-items per dimension (the partial kernel launches ~64 work-items per
+// head, the combine kernel 64 per row).
+constexpr int64_t kAttnMaxRows = int64_t(1) << 24;
 
 struct AttnArgs {
     const float *q;      // [heads][m][128]

@@ -129,6 +129,9 @@ def test_attention_validation_order(lib):
     assert _att(lib, n=0, d=64) == E_COUNT
     assert _att(lib, n=(1 << 26) + 1, d=64) == E_COUNT        # 32-bit row offsets per head
     assert _att(lib, n=1 << 26, d=64) == E_DIM                # largest n passes the count check
+    assert _att(lib, heads=(1 << 22) + 1, m=4, d=64) == E_COUNT  # heads * m above 2^24 rows
+    assert _att(lib, heads=1 << 22, m=4, d=64) == E_DIM
+    assert _att(lib, heads=(1 << 63) - 1, m=16, d=64) == E_COUNT
     for d in (64, 256, 100):
         assert _att(lib, d=d, bits=2) == E_DIM
     for b in (1, 2, 3, 5):
