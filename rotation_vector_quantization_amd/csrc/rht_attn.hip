@@ -106,6 +106,12 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
 // Global loads of one 32-key tile for a lane: K code bytes 16g..16g+15 of keys
 // key0 + l%16 and key0 + 16 + l%16; the lane's two 16-byte pieces of the value
 // tile (chunks l and 64 + l of the 32 x 64-byte tile); one norm (lanes 0-31:
@@ -593,16 +599,23 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(const AttnArgs a) {
     const int i = (int)(qi % a.m);
     const float *rec0 = a.ws + (head * a.chunks * a.m + i) * kAttnRecord;
     const int64_t step = (int64_t)a.m * kAttnRecord;
+    // chunk maxima and weighted sums, one chunk per lane (the loads of all
+    // chunks are in flight together instead of one round trip per chunk)
     float M = -INFINITY;
-    for (int c = 0; c < a.chunks; ++c) M = fmaxf(M, rec0[c * step + kAD]);
-    float z0 = 0.0f, z1 = 0.0f, l = 0.0f;
+    for (int c = (int)lane; c < a.chunks; c += 64) M = fmaxf(M, rec0[c * step + kAD]);
+    M = wave_max(M);
+    float l = 0.0f;
+    for (int c = (int)lane; c < a.chunks; c += 64)
+        l = fmaf(__builtin_amdgcn_exp2f(rec0[c * step + kAD] - M), rec0[c * step + kAD + 1], l);
+    l = wave_sum(l);
+    float z0 = 0.0f, z1 = 0.0f;
+#pragma unroll 4
     for (int c = 0; c < a.chunks; ++c) {
         const float *rec = rec0 + c * step;
         const float w = __builtin_amdgcn_exp2f(rec[kAD] - M);
         const float2 zv = reinterpret_cast<const float2 *>(rec)[lane];
         z0 = fmaf(w, zv.x, z0);
         z1 = fmaf(w, zv.y, z1);
-        l = fmaf(w, rec[kAD + 1], l);
     }
     const float inv = 1.0f / l;
     z0 *= inv;
