@@ -103,7 +103,7 @@ def test_attention_grid(heads, m, n, scale):
           q, kc, kn, vc, vn, 51, 52, scale)
 
 
-@pytest.mark.parametrize("m", [6, 12])
+@pytest.mark.parametrize("m", [4, 6, 12])   # one m per operand layout (<= 4, <= 8, <= 16)
 def test_attention_degenerate_queries_and_values(m):
     rng = np.random.default_rng(3)
     heads, n = 4, 300
