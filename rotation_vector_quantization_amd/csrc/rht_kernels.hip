@@ -1597,11 +1597,19 @@ hipError_t run_q(const QuantArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Grid of the generic decoder, whose traffic is mostly writes: at most two
+// blocks per CU, since HBM write throughput drops with many concurrent
+// writers (DRIVE d = 1024 fp32 decode: 0.054 -> 0.052 ms), unless
+// RHT_BLOCKS_PER_CU sets the cap for every kernel.
+inline int write_heavy_grid(int64_t n, int vpb, int per_cu) {
+    return grid_for(n, vpb, blocks_per_cu_cap() > 0 ? per_cu : min(per_cu, 2));
+}
+
 template <int D, int G, bool F16, int BITS, int KIND>
 hipError_t run_dq(const DequantArgs &a, hipStream_t s) {
     static const int per_cu = resident_blocks(k_dequantize<D, G, F16, BITS, KIND>);
     hipLaunchKernelGGL((k_dequantize<D, G, F16, BITS, KIND>),
-                       dim3(grid_for(a.n, vecs_per_block<D>(), per_cu)), dim3(kBlock), 0, s, a);
+                       dim3(write_heavy_grid(a.n, vecs_per_block<D>(), per_cu)), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
