@@ -18,15 +18,17 @@
 //
 // Both contractions run on v_mfma_f32_16x16x32_f16.  fp32 accuracy comes
 // from splitting every operand into fp16 hi + lo parts (x = hi + lo to about
-// 2^-22 relative) and summing hi*hi + hi*lo + lo*hi in the fp32 accumulator.
+// 2^-22 relative); the products hi*hi, hi*lo and lo*hi are summed in fp32.
 //   logits:  C[key][query] = sum_k A[key][k] B[k][query], A = code levels of
-//            16 keys (hi/lo from a 256-entry byte table), B = H D_k q scaled by
-//            a power of two into fp16 range.
+//            16 keys (hi/lo from a table indexed by code byte), B = H D_k q
+//            scaled by a power of two into fp16 range.
 //   values:  z^T[coord][query] += sum_key Cv^T[coord][key] P[key][query],
 //            P = p_j ||v_j|| times a running power of two; the accumulator
-//            layout of the logits tiles is exactly the B layout P needs; the
-//            value codes of a tile pass through LDS and an 8 x 8 nibble
-//            transpose so each lane holds eight keys' codes per coordinate.
+//            layout of the logits tiles is exactly the B layout P needs.
+// Three column layouts, by the number of queries per head m (QueryOperands):
+// m <= 16 one column per query; m <= 8 the hi and lo parts of the queries and
+// of P in separate columns; m <= 4 also a coordinate parity in the value
+// columns, so the value codes are used as stored instead of transposed.
 // Lane layout of the 16x16x32 instruction (lane l, g = l / 16): A holds
 // A[l % 16][8 g + t], B holds B[8 g + t][l % 16], C holds C[4 g + r][l % 16].
 #include "rht_device.h"
