@@ -1470,11 +1470,16 @@ __global__ __launch_bounds__(kBlock) void k_score_mfma(const ScoreArgs a) {
 
     const uint32_t lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t i = lane & 31u, h = lane >> 5;
-    // a block serves one half of the queries (32 each): block b takes half b % RH
-    // (the launch makes the grid a multiple of RH) and items b / RH, b / RH + grid / RH, ...
+    // a block serves one half of the queries (32 each).  With two halves, blocks
+    // b and b + 8 (the launch makes the grid a multiple of 16) take the same
+    // items, one half each: blocks are dispatched to the eight XCDs in turn, so
+    // the pair shares an XCD and the second block's code reads can hit that
+    // XCD's L2.  Item group ib = 8 (b / 16) + b % 8 takes items ib, ib + grid / 2, ...
     const int RH = a.m > 32 ? 2 : 1;
-    const int rh = (int)(blockIdx.x % RH);
-    const int64_t gw = (int64_t)(blockIdx.x / RH) * kWaves + wave, nw = (int64_t)(gridDim.x / RH) * kWaves;
+    const uint32_t b = blockIdx.x;
+    const int rh = RH == 2 ? (int)((b >> 3) & 1u) : 0;
+    const uint32_t ib = RH == 2 ? ((b >> 4) << 3) + (b & 7u) : b;
+    const int64_t gw = (int64_t)ib * kWaves + wave, nw = (int64_t)(gridDim.x / RH) * kWaves;
     const int64_t ntiles = (a.n + 31) / 32, istride = nw * kScoreTK;
     int64_t tile = gw * kScoreTK;  // first tile of this wave's item
     uint8_t *kc = kcb[wave];
@@ -1739,15 +1744,14 @@ hipError_t run_score(const ScoreArgs &a, hipStream_t s) {
 template <int D, int BITS, bool RES, bool EXACT>
 hipError_t run_score_mfma(const ScoreArgs &a, hipStream_t s) {
     static const int per_cu = resident_blocks(k_score_mfma<D, BITS, RES, EXACT>);
-    // wave items: (pair of key tiles, query half); a block serves one half, so the grid
-    // is a multiple of the number of halves
+    // wave items: (pair of key tiles, query half); a block serves one half
     const int rh = a.m > 32 ? 2 : 1;
     const int64_t items = ((a.n + 32 * kScoreTK - 1) / (32 * kScoreTK)) * rh;
     // two blocks per CU: each block rotates its query half once, and fewer,
     // longer blocks repeat that less (sign codes: 13.5 -> 12.9 us on 131072
     // keys; MSE and residual codes unchanged)
     int blocks = capped_grid(items, kWaves, per_cu, 2);
-    blocks += (rh - blocks % rh) % rh;
+    if (rh == 2) blocks = (blocks + 15) / 16 * 16;  // the kernel pairs blocks b and b + 8
     hipLaunchKernelGGL((k_score_mfma<D, BITS, RES, EXACT>), dim3(blocks), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
