@@ -144,13 +144,16 @@ __device__ __forceinline__ void load_tile(const uint8_t *kc, const uint8_t *vc, 
 }
 
 // Per code byte, the fp16 hi and lo parts of its two levels, low nibble in
-// the low half.  Entry b is a 256-byte row: kTabCopies copies of the hi word
-// (copy r at byte 4r), then kTabCopies copies of the lo word (at 128 + 4r).
-// Lane l reads copy l % kTabCopies, so the 32 lanes of a half-wave read 32
-// distinct banks whatever their bytes.  The byte address of entry b, copy r
-// is b * 256 + 4r: one v_perm_b32 places the code byte above 4r, and the lo
-// word is the same address plus a constant offset.  Separate word reads land
-// directly in the MFMA operand registers.
+// the low half.  Entry b is a 256-byte row holding kTabCopies copies; lane l
+// reads copy l % kTabCopies, so the lanes an LDS pass serves hit distinct
+// banks whatever their bytes.  Two row layouts:
+//   split (m > 4): the hi words (copy r at byte 4r), then the lo words (at
+//     128 + 4r); the address b * 256 + 4r is one v_perm_b32 (code byte above
+//     4r), the lo word the same address plus 128, each a ds_read_b32 straight
+//     into an MFMA operand register;
+//   paired (m <= 4): {hi, lo} of copy r at byte 8r, one ds_read_b64 per code
+//     byte (half the LDS instructions: the wave's lookups were waiting to
+//     issue); the level operand of a K step is {hi, lo} of two bytes.
 constexpr int kTabCopies = 32;
 constexpr uint32_t kTabRow = 256;  // bytes per entry
 
@@ -189,15 +192,51 @@ __device__ __forceinline__ void level_operands(const LevelTables &tb, uint32_t c
 //   QG = 4 (m <= 4): as QG = 8 for the logits (columns c and c + 4 repeat
 //     query c % 4).  In the value product, bit 2 of the column is a coordinate
 //     parity: column 8 * part + 4 * parity + query, so that an A row can be a
-//     pair of coordinates of one key, which is one code byte as stored.
+//     pair of coordinates of one key, which is one code byte as stored.  The
+//     level operands hold {hi, lo} pairs (paired table rows), so every B word
+//     appears twice in its operand (QueryPairs).
 template <bool SPLIT_N> struct QueryOperands;
 template <> struct QueryOperands<true> { u32x4_t b[4]; };
 template <> struct QueryOperands<false> { u32x4_t bh[4], bl[4]; };
+// QG = 4: the level operand of a K step holds {hi, lo} word pairs of two code
+// bytes (one ds_read_b64 each), so each query word appears twice.
+struct QueryPairs { u32x4_t b[8]; };
+template <int QG> struct QueryOps { typedef QueryOperands<(QG <= 8)> type; };
+template <> struct QueryOps<4> { typedef QueryPairs type; };
+
+// {hi, lo} words of code byte k of w, from the pair-layout table (entry b,
+// copy r at byte b * 256 + 8 r); copy8 = 8 * (lane % 32).
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 level_pair(const LevelTables &tb, uint32_t copy8, uint32_t w, uint32_t sel) {
+    typedef __attribute__((address_space(3))) const volatile u32x2_t lds_pair;
+    const char __attribute__((address_space(3))) *base = (const char __attribute__((address_space(3))) *)tb.w;
+    const u32x2_t v = *(const lds_pair *)(base + __builtin_amdgcn_perm(w, copy8, sel));
+    return make_uint2(v.x, v.y);
+}
 
 // The value held by the lane 8 places along in the same row of 16 lanes
 // (DPP row rotate by 8): the partner column of a SPLIT_N accumulator.
 __device__ __forceinline__ float row_ror8(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+}
+
+// Logits of 16 keys against the queries, pair layout (QG = 4): K step (ks, h)
+// covers code bytes 2h, 2h + 1 of word ks, slots {hi, lo} of each.
+__device__ __forceinline__ floatx4 key_logits_pairs(const LevelTables &tb, uint32_t copy8, u32x4_t kc,
+                                                    const QueryPairs &qo) {
+    floatx4 c[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint2 p0 = level_pair(tb, copy8, kc[ks], 0x0C0C0000u | ((4u + 2 * h) << 8));
+            const uint2 p1 = level_pair(tb, copy8, kc[ks], 0x0C0C0000u | ((5u + 2 * h) << 8));
+            c[h] = mfma1632(u32x4_t{p0.x, p0.y, p1.x, p1.y}, qo.b[2 * ks + h], c[h]);
+        }
+    floatx4 r = c[0] + c[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] += row_ror8(r[i]);
+    return r;
 }
 
 // Logits of 16 keys (one 16-byte code piece per lane) against the queries.
@@ -265,21 +304,6 @@ struct SoftmaxState {
     floatx4 z[kZ];       // rotated value sums in the accumulator layout above
 };
 
-// The A operands for byte T of four code words (word t -> register t): the
-// hi and lo level parts of the two nibbles, as level_operands.
-__device__ __forceinline__ void level_operands_byte(const LevelTables &tb, uint32_t copy4, uint32_t w0, uint32_t w1,
-                                                    uint32_t w2, uint32_t w3, uint32_t sel, u32x4_t &ah,
-                                                    u32x4_t &al) {
-    typedef __attribute__((address_space(3))) const volatile uint32_t lds_word;
-    const char __attribute__((address_space(3))) *base = (const char __attribute__((address_space(3))) *)tb.w;
-    const uint32_t o0 = __builtin_amdgcn_perm(w0, copy4, sel), o1 = __builtin_amdgcn_perm(w1, copy4, sel);
-    const uint32_t o2 = __builtin_amdgcn_perm(w2, copy4, sel), o3 = __builtin_amdgcn_perm(w3, copy4, sel);
-    ah = u32x4_t{*(const lds_word *)(base + o0), *(const lds_word *)(base + o1), *(const lds_word *)(base + o2),
-                 *(const lds_word *)(base + o3)};
-    al = u32x4_t{*(const lds_word *)(base + o0 + 128), *(const lds_word *)(base + o1 + 128),
-                 *(const lds_word *)(base + o2 + 128), *(const lds_word *)(base + o3 + 128)};
-}
-
 // Copy a tile's value codes (key r at vb + r * kVRow) and norms into LDS.
 // Done before the next tile's loads are issued: waiting for this tile's
 // registers then does not wait for the prefetch behind them.
@@ -289,29 +313,33 @@ __device__ __forceinline__ void stage_tile(uint8_t *vb, float *nb, const TileReg
     nb[lane] = t.nrm;
 }
 
-// Value sums of a tile, layout QG = 4.  K step s covers keys 16s + 4g + t
-// (t = 0..3), slots 2t + parity.  B: slot 2t + parity holds the lane's fp16
-// part of P[4s + t] if the parity is the column's, else 0.  A for tile T, row
-// j: coordinates 8j + 2T + parity, byte T of the key's code dword j (a[t] for
-// s = 0, a[4 + t] for s = 1).
-__device__ __forceinline__ void value_sums_by_parity(const LevelTables &tb, uint32_t copy4, const uint32_t (&a)[8],
+// Value sums of a tile, layout QG = 4.  K step i covers keys 2i and 2i + 1 of
+// the lane's eight (a[2i], a[2i + 1]: 4g + t for t < 4, 16 + 4g + t - 4 after),
+// slots {hi par 0, hi par 1, lo par 0, lo par 1} of each.  A for tile T, row j:
+// the {hi, lo} pair of byte T of the key's code dword j, i.e. coordinates
+// 8j + 2T and 8j + 2T + 1.  B: the lane's fp16 part of that key's P in the
+// half of the word its parity names, the same word for the hi and lo slots.
+__device__ __forceinline__ void value_sums_by_parity(const LevelTables &tb, uint32_t copy8, const uint32_t (&a)[8],
                                                      const float (&P)[8], uint2 psel, floatx4 (&z)[4]) {
     const uint2 q0 = split2(P[0], P[1]), q1 = split2(P[2], P[3]);
     const uint2 q2 = split2(P[4], P[5]), q3 = split2(P[6], P[7]);
-    const u32x4_t b0 = u32x4_t{__builtin_amdgcn_perm(q0.y, q0.x, psel.x), __builtin_amdgcn_perm(q0.y, q0.x, psel.y),
-                               __builtin_amdgcn_perm(q1.y, q1.x, psel.x), __builtin_amdgcn_perm(q1.y, q1.x, psel.y)};
-    const u32x4_t b1 = u32x4_t{__builtin_amdgcn_perm(q2.y, q2.x, psel.x), __builtin_amdgcn_perm(q2.y, q2.x, psel.y),
-                               __builtin_amdgcn_perm(q3.y, q3.x, psel.x), __builtin_amdgcn_perm(q3.y, q3.x, psel.y)};
+    uint32_t bw[8];
+    bw[0] = __builtin_amdgcn_perm(q0.y, q0.x, psel.x); bw[1] = __builtin_amdgcn_perm(q0.y, q0.x, psel.y);
+    bw[2] = __builtin_amdgcn_perm(q1.y, q1.x, psel.x); bw[3] = __builtin_amdgcn_perm(q1.y, q1.x, psel.y);
+    bw[4] = __builtin_amdgcn_perm(q2.y, q2.x, psel.x); bw[5] = __builtin_amdgcn_perm(q2.y, q2.x, psel.y);
+    bw[6] = __builtin_amdgcn_perm(q3.y, q3.x, psel.x); bw[7] = __builtin_amdgcn_perm(q3.y, q3.x, psel.y);
+    // key r's weight word twice: slots {hi, lo} of its level pair share it
+    u32x4_t bb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bb[i] = u32x4_t{bw[2 * i], bw[2 * i], bw[2 * i + 1], bw[2 * i + 1]};
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
-        const uint32_t sel = 0x0C0C0000u | ((4u + T) << 8);  // [0] = copy4, [1] = byte T
-        u32x4_t ah, al;
-        level_operands_byte(tb, copy4, a[0], a[1], a[2], a[3], sel, ah, al);
-        z[T] = mfma1632(ah, b0, z[T]);
-        z[T] = mfma1632(al, b0, z[T]);
-        level_operands_byte(tb, copy4, a[4], a[5], a[6], a[7], sel, ah, al);
-        z[T] = mfma1632(ah, b1, z[T]);
-        z[T] = mfma1632(al, b1, z[T]);
+        const uint32_t sel = 0x0C0C0000u | ((4u + T) << 8);  // [0] = copy8, [1] = byte T
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint2 p0 = level_pair(tb, copy8, a[2 * i], sel), p1 = level_pair(tb, copy8, a[2 * i + 1], sel);
+            z[T] = mfma1632(u32x4_t{p0.x, p0.y, p1.x, p1.y}, bb[i], z[T]);
+        }
     }
 }
 
@@ -351,7 +379,7 @@ __device__ __forceinline__ void value_sums_transposed(const LevelTables &tb, uin
 // even or odd weight of a pair in the half of the B word its parity names.
 template <bool FULL, int QG>
 __device__ __forceinline__ void attend_tile(const LevelTables &tb, const uint8_t *vb, const float *nb,
-                                            u32x4_t k0, u32x4_t k1, const QueryOperands<(QG <= 8)> &qo,
+                                            u32x4_t k0, u32x4_t k1, const typename QueryOps<QG>::type &qo,
                                             uint2 psel, float fq, int64_t key0, int64_t n, uint32_t lane,
                                             SoftmaxState<QG> &st) {
     constexpr bool SPLIT_N = QG <= 8;
@@ -359,8 +387,14 @@ __device__ __forceinline__ void attend_tile(const LevelTables &tb, const uint8_t
 
     // logits: rows 4g + r of tile 0 are keys 4g + r, of tile 1 keys 16 + 4g + r
     const uint32_t copy4 = 4 * (lane % kTabCopies);
-    const floatx4 c0 = key_logits<SPLIT_N>(tb, copy4, k0, qo);
-    const floatx4 c1 = key_logits<SPLIT_N>(tb, copy4, k1, qo);
+    floatx4 c0, c1;
+    if constexpr (QG == 4) {
+        c0 = key_logits_pairs(tb, 2 * copy4, k0, qo);
+        c1 = key_logits_pairs(tb, 2 * copy4, k1, qo);
+    } else {
+        c0 = key_logits<SPLIT_N>(tb, copy4, k0, qo);
+        c1 = key_logits<SPLIT_N>(tb, copy4, k1, qo);
+    }
     const float4 kn0 = *reinterpret_cast<const float4 *>(nb + 4 * g);
     const float4 kn1 = *reinterpret_cast<const float4 *>(nb + 16 + 4 * g);
     const float4 vn0 = *reinterpret_cast<const float4 *>(nb + 32 + 4 * g);
@@ -419,7 +453,7 @@ __device__ __forceinline__ void attend_tile(const LevelTables &tb, const uint8_t
         a[tt] = *reinterpret_cast<const uint32_t *>(vb + key * kVRow + 4 * j);
     }
     if constexpr (QG == 4)
-        value_sums_by_parity(tb, copy4, a, P, psel, st.z);
+        value_sums_by_parity(tb, 2 * copy4, a, P, psel, st.z);
     else
         value_sums_transposed<SPLIT_N>(tb, copy4, a, P, j, st.z);
 }
@@ -433,7 +467,7 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
     for (uint32_t k = threadIdx.x; k < 256u * kTabRow / 4; k += kABlock) {
         const uint32_t v = k / (kTabRow / 4), r = k % (kTabRow / 4);
         const uint2 e = split2(a.lev[v & 15u], a.lev[v >> 4]);
-        tb.w[k] = r < kTabCopies ? e.x : e.y;
+        tb.w[k] = QG == 4 ? ((r & 1u) ? e.y : e.x) : (r < kTabCopies ? e.x : e.y);
     }
     __syncthreads();
 
@@ -479,7 +513,7 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
                 qp[ks][w][1] = mine ? p1 : qp[ks][w][1];
             }
     }
-    QueryOperands<SPLIT_N> qo;
+    typename QueryOps<QG>::type qo;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         uint32_t h[4], l[4];
@@ -489,7 +523,13 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
             h[w] = sp.x;
             l[w] = sp.y;
         }
-        if constexpr (SPLIT_N) {
+        if constexpr (QG == 4) {
+            const bool lo_col = j >= 8;
+            const uint32_t b0 = lo_col ? l[0] : h[0], b1 = lo_col ? l[1] : h[1];
+            const uint32_t b2 = lo_col ? l[2] : h[2], b3 = lo_col ? l[3] : h[3];
+            qo.b[2 * ks] = u32x4_t{b0, b0, b1, b1};
+            qo.b[2 * ks + 1] = u32x4_t{b2, b2, b3, b3};
+        } else if constexpr (SPLIT_N) {
             const bool lo_col = j >= 8;
             qo.b[ks] = u32x4_t{lo_col ? l[0] : h[0], lo_col ? l[1] : h[1], lo_col ? l[2] : h[2], lo_col ? l[3] : h[3]};
         } else {
