@@ -25,10 +25,11 @@
 //   values:  z^T[coord][query] += sum_key Cv^T[coord][key] P[key][query],
 //            P = p_j ||v_j|| times a running power of two; the accumulator
 //            layout of the logits tiles is exactly the B layout P needs.
-// Three column layouts, by the number of queries per head m (QueryOperands):
+// Three column layouts, by the number of queries per head m (QueryOps):
 // m <= 16 one column per query; m <= 8 the hi and lo parts of the queries and
-// of P in separate columns; m <= 4 also a coordinate parity in the value
-// columns, so the value codes are used as stored instead of transposed.
+// of P in separate columns and {hi, lo} level pairs in the K dimension; m <= 4
+// also a coordinate parity in the value columns, so the value codes are used
+// as stored instead of transposed.
 // Lane layout of the 16x16x32 instruction (lane l, g = l / 16): A holds
 // A[l % 16][8 g + t], B holds B[8 g + t][l % 16], C holds C[4 g + r][l % 16].
 #include "rht_device.h"
@@ -147,11 +148,11 @@ __device__ __forceinline__ void load_tile(const uint8_t *kc, const uint8_t *vc, 
 // the low half.  Entry b is a 256-byte row holding kTabCopies copies; lane l
 // reads copy l % kTabCopies, so the lanes an LDS pass serves hit distinct
 // banks whatever their bytes.  Two row layouts:
-//   split (m > 4): the hi words (copy r at byte 4r), then the lo words (at
+//   split (m > 8): the hi words (copy r at byte 4r), then the lo words (at
 //     128 + 4r); the address b * 256 + 4r is one v_perm_b32 (code byte above
 //     4r), the lo word the same address plus 128, each a ds_read_b32 straight
 //     into an MFMA operand register;
-//   paired (m <= 4): {hi, lo} of copy r at byte 8r, one ds_read_b64 per code
+//   paired (m <= 8): {hi, lo} of copy r at byte 8r, one ds_read_b64 per code
 //     byte (half the LDS instructions: the wave's lookups were waiting to
 //     issue); the level operand of a K step is {hi, lo} of two bytes.
 constexpr int kTabCopies = 32;
@@ -185,24 +186,22 @@ __device__ __forceinline__ void level_operands(const LevelTables &tb, uint32_t c
 //   QG = 16 (m <= 16): column c is query c; hi*hi + hi*lo + lo*hi go into
 //     one accumulator, three MFMAs per K step.
 //   QG = 8 (m <= 8): the fp16 parts go to different columns.  Column c < 8
-//     holds the hi parts of query c, column 8 + c its lo parts, so the products
-//     with the hi and with the lo level parts leave sum (Ah + Al) Bh in column
-//     c and sum (Ah + Al) Bl in column 8 + c; their sum is the result (it also
-//     carries the negligible Al Bl term).  Two MFMAs per K step.
+//     holds the hi parts of query c, column 8 + c its lo parts, and the A
+//     operand of a K step holds the {hi, lo} level pairs of two code bytes
+//     (paired table rows), each B word twice (QueryPairs): one product leaves
+//     sum (Ah + Al) Bh in column c and sum (Ah + Al) Bl in column 8 + c; their
+//     sum is the result (it also carries the negligible Al Bl term).
 //   QG = 4 (m <= 4): as QG = 8 for the logits (columns c and c + 4 repeat
 //     query c % 4).  In the value product, bit 2 of the column is a coordinate
 //     parity: column 8 * part + 4 * parity + query, so that an A row can be a
-//     pair of coordinates of one key, which is one code byte as stored.  The
-//     level operands hold {hi, lo} pairs (paired table rows), so every B word
-//     appears twice in its operand (QueryPairs).
-template <bool SPLIT_N> struct QueryOperands;
-template <> struct QueryOperands<true> { u32x4_t b[4]; };
-template <> struct QueryOperands<false> { u32x4_t bh[4], bl[4]; };
-// QG = 4: the level operand of a K step holds {hi, lo} word pairs of two code
-// bytes (one ds_read_b64 each), so each query word appears twice.
+//     pair of coordinates of one key, which is one code byte as stored.
+// QG = 16: hi and lo parts of the queries, one column per query.
+struct QueryTriple { u32x4_t bh[4], bl[4]; };
+// QG = 8, 4: the level operand of a K step holds {hi, lo} word pairs of two
+// code bytes (one ds_read_b64 each), so each query word appears twice.
 struct QueryPairs { u32x4_t b[8]; };
-template <int QG> struct QueryOps { typedef QueryOperands<(QG <= 8)> type; };
-template <> struct QueryOps<4> { typedef QueryPairs type; };
+template <int QG> struct QueryOps { typedef QueryPairs type; };
+template <> struct QueryOps<16> { typedef QueryTriple type; };
 
 // {hi, lo} words of code byte k of w, from the pair-layout table (entry b,
 // copy r at byte b * 256 + 8 r); copy8 = 8 * (lane % 32).
@@ -239,31 +238,21 @@ __device__ __forceinline__ floatx4 key_logits_pairs(const LevelTables &tb, uint3
     return r;
 }
 
-// Logits of 16 keys (one 16-byte code piece per lane) against the queries.
-template <bool SPLIT_N>
-__device__ __forceinline__ floatx4 key_logits(const LevelTables &tb, uint32_t copy4, u32x4_t kc,
-                                              const QueryOperands<SPLIT_N> &qo) {
+// Logits of 16 keys (one 16-byte code piece per lane) against the queries,
+// layout QG = 16 (split table, three products per K step).
+__device__ __forceinline__ floatx4 key_logits_triple(const LevelTables &tb, uint32_t copy4, u32x4_t kc,
+                                                     const QueryTriple &qo) {
     // two independent accumulation chains (even and odd K steps)
     floatx4 c[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         u32x4_t ah, al;
         level_operands(tb, copy4, kc[ks], ah, al);
-        if constexpr (SPLIT_N) {
-            c[ks & 1] = mfma1632(ah, qo.b[ks], c[ks & 1]);
-            c[ks & 1] = mfma1632(al, qo.b[ks], c[ks & 1]);
-        } else {
-            c[ks & 1] = mfma1632(ah, qo.bh[ks], c[ks & 1]);
-            c[ks & 1] = mfma1632(ah, qo.bl[ks], c[ks & 1]);
-            c[ks & 1] = mfma1632(al, qo.bh[ks], c[ks & 1]);
-        }
+        c[ks & 1] = mfma1632(ah, qo.bh[ks], c[ks & 1]);
+        c[ks & 1] = mfma1632(ah, qo.bl[ks], c[ks & 1]);
+        c[ks & 1] = mfma1632(al, qo.bh[ks], c[ks & 1]);
     }
-    floatx4 r = c[0] + c[1];
-    if constexpr (SPLIT_N) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] += row_ror8(r[i]);
-    }
-    return r;
+    return c[0] + c[1];
 }
 
 // Transpose of an 8 x 8 matrix of nibbles: on entry nibble n of a[t] is
@@ -347,7 +336,8 @@ __device__ __forceinline__ void value_sums_by_parity(const LevelTables &tb, uint
 // key (t < 4 ? 4g + t : 16 + 4g + t - 4) (SPLIT_N: hi parts in columns 0-7, lo
 // parts in columns 8-15).  A of tile n: row j <-> coordinate 8j + n, k = 8g + t
 // <-> the key above; after the transpose, byte w of word n holds coordinate
-// 8j + n of keys 2w, 2w+1: one table entry each.
+// 8j + n of keys 2w, 2w+1: one table entry each (SPLIT_N: a {hi, lo} pair, two
+// bytes per K step, each weight word twice).
 template <bool SPLIT_N>
 __device__ __forceinline__ void value_sums_transposed(const LevelTables &tb, uint32_t copy4, uint32_t (&a)[8],
                                                       const float (&P)[8], uint32_t j, floatx4 (&z)[8]) {
@@ -362,13 +352,27 @@ __device__ __forceinline__ void value_sums_transposed(const LevelTables &tb, uin
         pl = u32x4_t{s0.y, s1.y, s2.y, s3.y};
     }
     transpose_nibbles8(a);
+    if constexpr (SPLIT_N) {
+        // paired table rows: bytes 0, 1 then 2, 3 of a word, {hi, lo} each; the
+        // weight word of a key pair appears twice
+        const u32x4_t b01 = u32x4_t{ph[0], ph[0], ph[1], ph[1]}, b23 = u32x4_t{ph[2], ph[2], ph[3], ph[3]};
+        const uint32_t copy8 = 2 * copy4;
 #pragma unroll
-    for (int nn = 0; nn < 8; ++nn) {
-        u32x4_t ah, al;
-        level_operands(tb, copy4, a[nn], ah, al);
-        z[nn] = mfma1632(ah, ph, z[nn]);
-        if constexpr (!SPLIT_N) z[nn] = mfma1632(ah, pl, z[nn]);
-        z[nn] = mfma1632(al, ph, z[nn]);
+        for (int nn = 0; nn < 8; ++nn) {
+            const uint2 p0 = level_pair(tb, copy8, a[nn], 0x0C0C0400u), p1 = level_pair(tb, copy8, a[nn], 0x0C0C0500u);
+            const uint2 p2 = level_pair(tb, copy8, a[nn], 0x0C0C0600u), p3 = level_pair(tb, copy8, a[nn], 0x0C0C0700u);
+            z[nn] = mfma1632(u32x4_t{p0.x, p0.y, p1.x, p1.y}, b01, z[nn]);
+            z[nn] = mfma1632(u32x4_t{p2.x, p2.y, p3.x, p3.y}, b23, z[nn]);
+        }
+    } else {
+#pragma unroll
+        for (int nn = 0; nn < 8; ++nn) {
+            u32x4_t ah, al;
+            level_operands(tb, copy4, a[nn], ah, al);
+            z[nn] = mfma1632(ah, ph, z[nn]);
+            z[nn] = mfma1632(ah, pl, z[nn]);
+            z[nn] = mfma1632(al, ph, z[nn]);
+        }
     }
 }
 
@@ -388,12 +392,12 @@ __device__ __forceinline__ void attend_tile(const LevelTables &tb, const uint8_t
     // logits: rows 4g + r of tile 0 are keys 4g + r, of tile 1 keys 16 + 4g + r
     const uint32_t copy4 = 4 * (lane % kTabCopies);
     floatx4 c0, c1;
-    if constexpr (QG == 4) {
+    if constexpr (SPLIT_N) {
         c0 = key_logits_pairs(tb, 2 * copy4, k0, qo);
         c1 = key_logits_pairs(tb, 2 * copy4, k1, qo);
     } else {
-        c0 = key_logits<SPLIT_N>(tb, copy4, k0, qo);
-        c1 = key_logits<SPLIT_N>(tb, copy4, k1, qo);
+        c0 = key_logits_triple(tb, copy4, k0, qo);
+        c1 = key_logits_triple(tb, copy4, k1, qo);
     }
     const float4 kn0 = *reinterpret_cast<const float4 *>(nb + 4 * g);
     const float4 kn1 = *reinterpret_cast<const float4 *>(nb + 16 + 4 * g);
@@ -467,7 +471,7 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
     for (uint32_t k = threadIdx.x; k < 256u * kTabRow / 4; k += kABlock) {
         const uint32_t v = k / (kTabRow / 4), r = k % (kTabRow / 4);
         const uint2 e = split2(a.lev[v & 15u], a.lev[v >> 4]);
-        tb.w[k] = QG == 4 ? ((r & 1u) ? e.y : e.x) : (r < kTabCopies ? e.x : e.y);
+        tb.w[k] = SPLIT_N ? ((r & 1u) ? e.y : e.x) : (r < kTabCopies ? e.x : e.y);
     }
     __syncthreads();
 
@@ -523,15 +527,12 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
             h[w] = sp.x;
             l[w] = sp.y;
         }
-        if constexpr (QG == 4) {
+        if constexpr (SPLIT_N) {
             const bool lo_col = j >= 8;
             const uint32_t b0 = lo_col ? l[0] : h[0], b1 = lo_col ? l[1] : h[1];
             const uint32_t b2 = lo_col ? l[2] : h[2], b3 = lo_col ? l[3] : h[3];
             qo.b[2 * ks] = u32x4_t{b0, b0, b1, b1};
             qo.b[2 * ks + 1] = u32x4_t{b2, b2, b3, b3};
-        } else if constexpr (SPLIT_N) {
-            const bool lo_col = j >= 8;
-            qo.b[ks] = u32x4_t{lo_col ? l[0] : h[0], lo_col ? l[1] : h[1], lo_col ? l[2] : h[2], lo_col ? l[3] : h[3]};
         } else {
             qo.bh[ks] = u32x4_t{h[0], h[1], h[2], h[3]};
             qo.bl[ks] = u32x4_t{l[0], l[1], l[2], l[3]};
