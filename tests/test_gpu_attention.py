@@ -139,9 +139,10 @@ def test_attention_workspace_reused_by_a_smaller_call():
               q, kc, kn, vc, vn, 71, 72, 0.1)
 
 
-def test_attention_kv_block_full_size_sampled_heads():
-    # the benchmark's shape: 32 layers x 8 KV heads = 256 heads, 32768 tokens, 4 queries per head
-    heads, n, m = 256, 32768, 4
+@pytest.mark.parametrize("m", [4, 8, 16])   # the benchmark's m, and the other two operand layouts
+def test_attention_kv_block_full_size_sampled_heads(m):
+    # the benchmark's shape: 32 layers x 8 KV heads = 256 heads, 32768 tokens
+    heads, n = 256, 32768
     rng = np.random.default_rng(20250)
     kc = rng.integers(0, 256, (heads, n, D // 2), dtype=np.uint8)
     vc = rng.integers(0, 256, (heads, n, D // 2), dtype=np.uint8)
