@@ -189,19 +189,21 @@ const FloatBook &book(int bits) {
     return g_books[bits];
 }
 
-// Signs of D: top bit of the i-th SplitMix64 output (Steele, Lea, Flood 2014)
-// from state `seed`; a set bit means -1.
+// Sign i of D: top bit of the i-th SplitMix64 output (Steele, Lea, Flood 2014)
+// from state `seed`; 1 means -1.  The generator's state after i + 1 steps is
+// seed + (i + 1) * 0x9E3779B97F4A7C15 (mod 2^64), so each output stands alone.
+uint32_t sign_bit(uint64_t seed, int i) {
+    uint64_t z = seed + (uint64_t)(i + 1) * 0x9E3779B97F4A7C15ULL;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    z ^= z >> 31;
+    return (uint32_t)(z >> 63);
+}
+
+// The signs of D as bit words, bit i % 32 of word i / 32.
 void sign_words(uint64_t seed, int d, uint32_t *words) {
     std::memset(words, 0, sizeof(uint32_t) * (size_t)((d + 31) / 32));
-    uint64_t state = seed;
-    for (int i = 0; i < d; ++i) {
-        state += 0x9E3779B97F4A7C15ULL;
-        uint64_t z = state;
-        z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
-        z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
-        z ^= z >> 31;
-        if (z >> 63) words[i >> 5] |= 1u << (i & 31);
-    }
+    for (int i = 0; i < d; ++i) words[i >> 5] |= sign_bit(seed, i) << (i & 31);
 }
 
 bool pow2_dim(int32_t d) { return d >= kMinD && d <= kMaxD && (d & (d - 1)) == 0; }
@@ -313,10 +315,7 @@ rht_status rht_codebook_beta(int32_t bits, int32_t d, float *levels, float *thre
 rht_status rht_signs(uint64_t seed, int32_t d, int8_t *signs) {
     if (!signs) return RHT_E_NULL;
     if (d < 1 || d > (1 << 20)) return RHT_E_DIM;
-    uint32_t *w = new uint32_t[(size_t)(d + 31) / 32];
-    sign_words(seed, d, w);
-    for (int i = 0; i < d; ++i) signs[i] = ((w[i >> 5] >> (i & 31)) & 1u) ? (int8_t)-1 : (int8_t)1;
-    delete[] w;
+    for (int i = 0; i < d; ++i) signs[i] = sign_bit(seed, i) ? (int8_t)-1 : (int8_t)1;
     return RHT_OK;
 }
 
