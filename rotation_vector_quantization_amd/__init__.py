@@ -7,8 +7,8 @@ arguments:
 * ``rht_quantize`` ... ``rht_signs`` mirror the C functions one to one (raw
   integer pointers, sizes, a stream handle) and raise ``RhtError`` on a
   non-OK status;
-* ``quantize``, ``dequantize``, ``residual_quantize``, ``residual_dequantize``
-  and ``score`` take torch tensors that already live on the GPU, allocate the
+* ``quantize``, ``dequantize``, ``residual_quantize``, ``residual_dequantize``,
+  ``score``, ``score_sign``, ``residual_score`` and ``attention`` take torch tensors that already live on the GPU, allocate the
   outputs with ``torch.empty`` on the same device and queue the work on the
   current stream.
 
@@ -26,9 +26,10 @@ __all__ = [
     "RhtError", "F32", "F16", "SCALE_NORM", "SCALE_SIGN_BIASED", "SCALE_SIGN_UNBIASED", "SCALE_EDEN",
     "SCALE_NORM_BETA",
     "library_path", "load", "rht_quantize", "rht_dequantize", "rht_residual_quantize",
-    "rht_residual_dequantize", "rht_score", "rht_codebook", "rht_signs", "rht_status_str",
-    "rht_abi_version", "quantize", "dequantize", "residual_quantize", "residual_dequantize",
-    "score", "codebook", "signs",
+    "rht_residual_dequantize", "rht_score", "rht_score_sign", "rht_residual_score", "rht_attention",
+    "rht_attention_workspace_bytes", "rht_codebook", "rht_codebook_beta", "rht_signs",
+    "rht_status_str", "rht_abi_version", "quantize", "dequantize", "residual_quantize",
+    "residual_dequantize", "score", "score_sign", "residual_score", "attention", "codebook", "signs",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

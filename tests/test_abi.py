@@ -38,6 +38,13 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), name
 
 
+def test_binding_has_every_declared_function():
+    # the Python binding keeps the C names, one wrapper per declared function
+    for name in declared_functions():
+        assert callable(getattr(rht, name, None)), name
+        assert name in rht.__all__, name
+
+
 def test_abi_version(lib):
     assert rht.rht_abi_version() == 4
     for s in range(10):
