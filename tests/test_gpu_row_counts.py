@@ -1,15 +1,16 @@
 """GPU parity at row counts on and around the kernels' tile edges (wave tiles of
-16 rows, blocks of 64 rows, and their multiples), through the raw C ABI with
-output buffers longer than n: every row past n must keep its sentinel bytes,
-and the first n rows must match the oracle under the rules of tests/parity.py.
+16 rows, blocks of 64 rows, 32-key scoring tiles, and their multiples), through
+the raw C ABI with output buffers longer than needed: every byte past the
+output must keep its sentinel value, and the output must match the oracle
+under the rules of tests/parity.py.
 """
 import numpy as np
 import pytest
 
 import oracle
 import rotation_vector_quantization_amd as rht
-from parity import (RECON_F16, RECON_F32, NORM_RTOL, SCALE_RTOL, check_codes, check_recon, check_rel,
-                    unpack)
+from parity import (RECON_F16, RECON_F32, NORM_RTOL, SCALE_RTOL, SCORE_TOL, check_codes, check_recon,
+                    check_rel, rel_l2, unpack)
 from test_gpu_parity import check_residual, small_input, say
 
 pytestmark = pytest.mark.gpu
@@ -125,3 +126,61 @@ def test_residual_row_counts(d, dt, bits):
                                         bits, seed, y.data_ptr(), yt, stream())
             ref = oracle.residual_dequantize(gc, gsg, gn, grs, d, bits, seed, ydt)
             check_recon(split(y, n, yb, ydt), ref, tol, "residual decode %s" % np.dtype(ydt).name)
+
+
+SCORE_N = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 511, 512, 513, 1025]
+
+
+@pytest.mark.parametrize("kind", ["mse4", "mse2", "sign", "res3"])
+@pytest.mark.parametrize("m", [1, 32, 33, 64])
+@pytest.mark.parametrize("d", [64, 128])
+def test_score_key_counts(d, m, kind):
+    """Logits [m][n] for key counts around the 32-key tiles and 64-key items; the
+    buffer carries sentinel bytes past m * n.  Every logit <q, k^> must be within
+    SCORE_TOL * ||q|| * ||k^|| of the oracle's (the Cauchy-Schwarz scale of the
+    dot product; k^ is the decoded key); the relative-L2 rules, overall and per
+    query row, apply once a row holds a whole 32-key tile, since over one or two
+    logits a relative error measures only the cancellation inside a dot product."""
+    seed = 60 + d + m
+    rng = np.random.default_rng(d + 3 * m + len(kind))
+    K = rng.standard_normal((max(SCORE_N), d)).astype(np.float32)
+    K[0] = 0.0
+    q = rng.standard_normal((m, d)).astype(np.float32)
+    qd = to_dev(q)
+    for n in SCORE_N:
+        say("score key counts d=%d m=%d kind=%s n=%d" % (d, m, kind, n))
+        keys = K[:n]
+        out = torch.full((m * n * 4 + PAD * 256,), SENT, dtype=torch.uint8, device="cuda:0")
+        if kind.startswith("mse"):
+            bits = int(kind[3:])
+            c, nr = oracle.quantize(keys, bits, seed)
+            cd, nd = to_dev(c), to_dev(nr)
+            rht.rht_score(qd.data_ptr(), m, cd.data_ptr(), nd.data_ptr(), n, d, bits, seed, out.data_ptr(), stream())
+            ref = oracle.score(q, c, nr, d, bits, seed)
+            khat = oracle.dequantize(c, nr, d, bits, seed, np.float32)
+        elif kind == "sign":
+            b, S = oracle.sign_quantize(keys, True, seed)
+            bd, Sd = to_dev(b), to_dev(S)
+            rht.rht_score_sign(qd.data_ptr(), m, bd.data_ptr(), Sd.data_ptr(), n, d, seed, out.data_ptr(), stream())
+            ref = oracle.score_sign(q, b, S, d, seed)
+            khat = oracle.sign_dequantize(b, S, d, seed, np.float32)
+        else:
+            bits = int(kind[3:])
+            c, g, nr, rs = oracle.residual_quantize(keys, bits, seed)
+            cd, gd, nd, rd = to_dev(c), to_dev(g), to_dev(nr), to_dev(rs)
+            rht.rht_residual_score(qd.data_ptr(), m, cd.data_ptr(), gd.data_ptr(), nd.data_ptr(), rd.data_ptr(), n,
+                                   d, bits, seed, out.data_ptr(), stream())
+            ref = oracle.score_residual(q, c, g, nr, rs, d, bits, seed)
+            khat = oracle.residual_dequantize(c, g, nr, rs, d, bits, seed, np.float32)
+        torch.cuda.synchronize()
+        b = out.cpu().numpy()
+        assert np.all(b[m * n * 4:] == SENT), "scoring wrote past m * n logits"
+        got = b[:m * n * 4].view(np.float32).reshape(m, n)
+        nz = np.abs(ref).sum(0) > 0
+        assert np.all(got[:, ~nz] == 0)
+        scale = np.linalg.norm(q.astype(np.float64), axis=1)[:, None] * \
+            np.linalg.norm(khat.astype(np.float64), axis=1)[None, :]
+        assert np.all(np.abs(got.astype(np.float64) - ref) <= SCORE_TOL * scale)
+        if n >= 32:
+            assert rel_l2(got[:, nz], ref[:, nz]) <= SCORE_TOL
+            assert rel_l2(got[:, nz], ref[:, nz], axis=1).max() <= SCORE_TOL
