@@ -157,3 +157,32 @@ def test_attention_kv_block_full_size_sampled_heads(m):
                                 42, 43, 1.0 / math.sqrt(D))
         check(got[h:h + 1], want, "full size head %d" % h, q[h:h + 1], kc[h:h + 1], kn[h:h + 1],
               vc[h:h + 1], vn[h:h + 1], 42, 43, 1.0 / math.sqrt(D))
+
+
+@pytest.mark.parametrize("m", [1, 4, 5, 8, 9, 16])   # both sides of every operand-layout switch
+def test_attention_key_counts_and_buffer_bounds(m):
+    """Key counts on and around the 32-key tiles and the per-head chunking, through
+    the raw C ABI: the output [heads][m][d] and the workspace carry sentinel bytes
+    past their ends (the workspace past rht_attention_workspace_bytes), which must
+    survive; the output must meet the error bound."""
+    heads, sk, sv, scale = 2, 81, 82, 1.0 / math.sqrt(D)
+    rng = np.random.default_rng(300 + m)
+    for n in (1, 2, 31, 32, 33, 63, 64, 65, 1023, 1025, 3073):
+        say("attention key counts heads=%d m=%d n=%d" % (heads, m, n))
+        kc, kn = coded(rng, heads, n, sk)
+        vc, vn = coded(rng, heads, n, sv)
+        q = (2 * rng.standard_normal((heads, m, D))).astype(np.float32)
+        ob = heads * m * D * 4
+        need = rht.rht_attention_workspace_bytes(heads, m, n, D)
+        out = torch.full((ob + 4096,), 0xA5, dtype=torch.uint8, device="cuda:0")
+        ws = torch.full((need + 4096,), 0xA5, dtype=torch.uint8, device="cuda:0")
+        qd, kcd, knd, vcd, vnd = dev(q), dev(kc), dev(kn), dev(vc), dev(vn)
+        rht.rht_attention(qd.data_ptr(), m, kcd.data_ptr(), knd.data_ptr(), vcd.data_ptr(), vnd.data_ptr(),
+                          heads, n, D, BITS, sk, sv, scale, out.data_ptr(), ws.data_ptr(), need,
+                          torch.cuda.current_stream().cuda_stream)
+        o, w = host(out), host(ws)
+        assert np.all(o[ob:] == 0xA5), "attention wrote past its output"
+        assert np.all(w[need:] == 0xA5), "attention wrote past its workspace"
+        want = oracle.attention(q, kc, kn, vc, vn, D, BITS, sk, sv, scale)
+        check(o[:ob].view(np.float32).reshape(heads, m, D), want, "key counts m=%d n=%d" % (m, n),
+              q, kc, kn, vc, vn, sk, sv, scale)
