@@ -81,6 +81,42 @@ def test_mse_row_counts(d, dt, bits):
                         "dequant %s" % np.dtype(ydt).name)
 
 
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("mode", [rht.SCALE_EDEN, rht.SCALE_NORM_BETA])
+@pytest.mark.parametrize("d,dt", [(128, np.float16), (1024, np.float32)])
+def test_eden_and_finite_d_row_counts(d, dt, mode, bits):
+    seed = 700 + d + bits + mode
+    X = small_input(max(EDGES), d, dt, seed)
+    if mode == rht.SCALE_EDEN:
+        lv, th, _, _ = oracle.lloyd_max(bits)
+    else:
+        lv, th, _, _ = oracle.lloyd_max_beta(bits, d)
+    cb = d * bits // 8
+    for n in EDGES:
+        say("%s row counts d=%d bits=%d n=%d" % ("eden" if mode == rht.SCALE_EDEN else "beta", d, bits, n))
+        x = X[:n]
+        xd = to_dev(x)
+        codes, scale = padded(n, cb), padded(n, 4)
+        rht.rht_quantize(xd.data_ptr(), xcode(dt), n, d, bits, mode, seed, codes.data_ptr(), scale.data_ptr(),
+                         stream())
+        gc, gs = split(codes, n, cb), split(scale, n, 4, np.float32)[:, 0]
+        if mode == rht.SCALE_EDEN:
+            oc, os_ = oracle.quantize_eden(x, bits, seed)
+            ys = lambda rows: oracle.quantize(x[rows], bits, seed, want_y=True)[2]
+        else:
+            oc, os_ = oracle.quantize_cb(x, bits, seed, lv, th)
+            ys = lambda rows: oracle.quantize_cb(x[rows], bits, seed, lv, th, want_y=True)[2]
+        gu, ou = unpack(gc, bits, d), unpack(oc, bits, d)
+        check_codes(gu, ou, ys, th, "codes")
+        same = (gu == ou).all(1)  # EDEN's S sums over every code of its row
+        check_rel(gs[same], os_[same], SCALE_RTOL if mode == rht.SCALE_EDEN else NORM_RTOL, "scale")
+        y = padded(n, 4 * d)
+        rht.rht_dequantize(codes.data_ptr(), scale.data_ptr(), n, d, bits, mode, seed, y.data_ptr(), rht.F32,
+                           stream())
+        ref = oracle.dequantize_cb(gc, gs, d, bits, seed, lv, np.float32)
+        check_recon(split(y, n, 4 * d, np.float32), ref, RECON_F32, "decode")
+
+
 @pytest.mark.parametrize("mode", [rht.SCALE_SIGN_BIASED, rht.SCALE_SIGN_UNBIASED])
 def test_drive_row_counts(mode):
     d, dt, seed = 1024, np.float32, 77
