@@ -245,6 +245,28 @@ def test_fp16_codec_against_numpy():
     np.testing.assert_array_equal(ours, want)
 
 
+def test_fp16_encoder_rounds_exact_ties_to_even():
+    """Values exactly halfway between two fp16 numbers, (2k+1) 2^(e-11) for a
+    in [2^e, 2^(e+1)), over the whole normal range and in the subnormal range
+    ((2k+1) 2^-25): round-to-nearest-even picks the neighbour with an even
+    significand, which numpy's conversion fixes independently."""
+    ties = []
+    for e in (-14, -13, -7, -1, 0, 1, 4, 10, 14, 15):
+        k = np.arange(1024, 2048, dtype=np.float64)       # significand m, a = (m + 1/2) 2^(e-10)
+        ties.append((2 * k + 1) * 2.0 ** (e - 11))
+    ties.append((2 * np.arange(0, 1024, dtype=np.float64) + 1) * 2.0 ** -25)
+    v = np.concatenate(ties)
+    v = v[v < 65520.0]                                    # 65520 itself rounds to infinity
+    v = np.concatenate([v, -v])
+    ours = np.array([oracle.f64_to_f16(float(t)) for t in v], dtype=np.uint16)
+    want = v.astype(np.float16).view(np.uint16)
+    np.testing.assert_array_equal(ours, want)
+    # each tie went to the even significand, not away from zero
+    assert np.all((ours & 1) == 0)
+    up = np.abs(v) < np.abs(ours.view(np.float16).astype(np.float64))
+    assert 0 < up.mean() < 1                              # both directions occur
+
+
 # ---------------------------------------------------------------- decoders
 @pytest.mark.parametrize("bits", [1, 2, 4])
 def test_dequantize_dense_and_rotated_domain_error(bits):
@@ -344,6 +366,87 @@ def test_residual_chain_closed_forms(bits):
     f = oracle.residual_quantize(x, bits, seed, forced_codes=codes)
     for a, b in zip(f, (codes, sg, norms, rs)):
         np.testing.assert_array_equal(a, b)
+
+
+# ------------------------------------------- edge readings of the sign codes
+# The pages give no rule for a rotated coordinate that is exactly 0 or for a
+# zero vector.  The readings: a sign bit is [v >= 0], so +0 and -0 both give
+# bit 1 (the 1-bit code then equals the 1-bit Lloyd-Max code index, whose
+# middle threshold 0 goes up); a scale whose definition is 0/0 is 0, so a
+# zero vector decodes to exactly 0.  Each value below is fixed by that
+# reading, computed here by hand, not by the oracle.
+def _exact_zero_rows(d, seed):
+    """x = s_0 e_0 + s_1 e_1 with s the rotation signs: D x = e_0 + e_1 and
+    (H D x)_i = 1 + (-1)^i, so every odd rotated coordinate is exactly 0 and
+    every even one is exactly 2.  Also its negation (odd coordinates -0 after
+    the sign flips) and a zero row (its rotation holds both +0 and -0)."""
+    s = oracle.signs(seed, d).astype(np.float32)
+    x = np.zeros((3, d), np.float32)
+    x[0, 0], x[0, 1] = s[0], s[1]
+    x[1] = -x[0]
+    return x
+
+
+@pytest.mark.parametrize("dt", [np.float32, np.float16])
+@pytest.mark.parametrize("unbiased", [False, True])
+def test_drive_sign_bit_at_exact_zero_and_zero_vector(unbiased, dt):
+    d, seed = 64, 19
+    x = _exact_zero_rows(d, seed).astype(dt)
+    b, S = oracle.sign_quantize(x, unbiased, seed)
+    bits = unpack_fields(b, 1, d)
+    odd = np.arange(d) % 2 == 1
+    # row 0: H D x = 2 on even, +0 on odd -> every bit 1
+    np.testing.assert_array_equal(bits[0], np.ones(d, np.int64))
+    # row 1: -2 on even (bit 0), exact zero on odd (bit 1)
+    np.testing.assert_array_equal(bits[1], odd.astype(np.int64))
+    # row 2: the zero vector -> every bit 1, S = 0 in both modes
+    np.testing.assert_array_equal(bits[2], np.ones(d, np.int64))
+    # ||Pi x||_1 = (d/2) 2 / sqrt(d) = sqrt(d); ||x||^2 = 2
+    want = 2.0 / math.sqrt(d) if unbiased else math.sqrt(d) / d
+    np.testing.assert_allclose(S[:2], [want, want], rtol=1e-7)
+    assert S[2] == 0.0 and not np.signbit(S[2])
+    xh = oracle.sign_dequantize(b, S, d, seed)
+    assert np.all(xh[2] == 0.0)
+    # <x, x^> = S <Pi x, sigma> = S ||Pi x||_1: ||x||^2 = 2 (unbiased), ||Pi x||_1^2 / d = 1 (biased)
+    np.testing.assert_allclose(float((x[0].astype(np.float64) * xh[0].astype(np.float64)).sum()),
+                               2.0 if unbiased else 1.0, rtol=1e-6)
+
+
+@pytest.mark.parametrize("dt", [np.float32, np.float16])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_residual_sign_bit_and_scale_at_zero(bits, dt):
+    d, seed = 64, 23
+    x = _exact_zero_rows(d, seed).astype(dt)
+    codes, sg, norms, rs = oracle.residual_quantize(x, bits, seed)
+    K1 = 1 << (bits - 1)
+    # zero vector: stage-1 codes K1/2, norm 0, residual +-0 everywhere -> every
+    # sign bit 1, S_r = 0/0 = 0, and the decode is exactly 0
+    assert np.all(unpack_fields(codes[2:], bits - 1, d) == K1 // 2)
+    assert norms[2] == 0.0 and rs[2] == 0.0 and not np.signbit(rs[2])
+    np.testing.assert_array_equal(unpack_fields(sg[2:], 1, d)[0], np.ones(d, np.int64))
+    y = oracle.residual_dequantize(codes, sg, norms, rs, d, bits, seed)
+    assert np.all(y[2] == 0.0)
+    # row 0: y = sqrt(2) on even coordinates, exact 0 on odd ones; the odd
+    # coordinates take the first level above 0 and their residual is negative
+    lv, _, _, _ = oracle.lloyd_max(bits - 1)
+    c = unpack_fields(codes[:1], bits - 1, d)[0]
+    assert np.all(c[1::2] == K1 // 2)
+    sb = unpack_fields(sg[:1], 1, d)[0]
+    assert np.all(sb[1::2] == 0)
+    yev = math.sqrt(2.0)
+    assert np.all(sb[0::2] == (1 if yev >= lv[c[0]] else 0))
+
+
+def test_quantize_and_eden_zero_vector_scales():
+    """MSE and EDEN codes of a zero vector: code K/2 everywhere, scale 0 (EDEN's
+    d ||x||^2 / <c, H D x> is 0/0), decode exactly 0."""
+    d = 32
+    x = np.zeros((2, d), np.float16)
+    for bits in (1, 2, 3, 4):
+        c, S = oracle.quantize_eden(x, bits, 7)
+        assert np.all(unpack_fields(c, bits, d) == (1 << bits) // 2)
+        assert np.all(S == 0.0)
+        assert np.all(oracle.dequantize(c, S, d, bits, 7, np.float16).astype(np.float64) == 0.0)
 
 
 def test_residual_chain_removes_inner_product_shrinkage():
