@@ -36,13 +36,14 @@
 #ifndef RHT_H
 #define RHT_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define RHT_ABI_VERSION 4
+#define RHT_ABI_VERSION 5
 
 typedef enum {
     RHT_OK = 0,
@@ -188,6 +189,30 @@ rht_status rht_attention(const float *q, int32_t m, const uint8_t *k_codes, cons
 /* Device workspace bytes rht_attention needs for these sizes; 0 when
  * rht_attention would reject them or has nothing to do.  Host-only. */
 size_t rht_attention_workspace_bytes(int64_t heads, int32_t m, int64_t n, int32_t d);
+
+/* rht_attention without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Arguments, validation order, kernels and results are
+ * those of rht_attention; the partial records go to a device array inside the
+ * library instead, RHT_ATTENTION_NOALLOC_MAX_BYTES bytes, one per device,
+ * held from the first call on that device until the process ends.  The call
+ * itself allocates nothing: no hipMalloc, no hipFree, no allocating library
+ * routine.
+ *   Returns RHT_E_WORKSPACE (after the other checks) when these sizes need
+ *   more than RHT_ATTENTION_NOALLOC_MAX_BYTES, i.e. when
+ *   rht_attention_workspace_bytes(heads, m, n, d) exceeds it (for example
+ *   heads * m > 63550 with one key chunk per head).
+ *   Every call on a device shares that device's array, and calls whose work
+ *   can overlap on one device (different streams, or host threads queueing at
+ *   once) race on it and give wrong results: serialize them, for example on
+ *   one stream.  No array contents need clearing: each call writes every
+ *   record it reads.  RHT_E_DEVICE when the array's device address cannot be
+ *   looked up. */
+#define RHT_ATTENTION_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+rht_status rht_attention_noalloc(const float *q, int32_t m, const uint8_t *k_codes, const float *k_norms,
+                                 const uint8_t *v_codes, const float *v_norms, int64_t heads, int64_t n,
+                                 int32_t d, int32_t bits, uint64_t seed_k, uint64_t seed_v, float scale,
+                                 float *out, void *stream);
 
 /* ---- host-side helpers: HOST pointers, synchronous, no GPU needed ---- */
 

@@ -27,7 +27,7 @@ __all__ = [
     "SCALE_NORM_BETA",
     "library_path", "load", "rht_quantize", "rht_dequantize", "rht_residual_quantize",
     "rht_residual_dequantize", "rht_score", "rht_score_sign", "rht_residual_score", "rht_attention",
-    "rht_attention_workspace_bytes", "rht_codebook", "rht_codebook_beta", "rht_signs",
+    "rht_attention_workspace_bytes", "rht_attention_noalloc", "rht_codebook", "rht_codebook_beta", "rht_signs",
     "rht_status_str", "rht_abi_version", "quantize", "dequantize", "residual_quantize",
     "residual_dequantize", "score", "score_sign", "residual_score", "attention", "codebook", "signs",
 ]
@@ -37,7 +37,7 @@ _LIB_PATH = os.path.join(_HERE, "librht.so")
 
 F32, F16 = 0, 1
 SCALE_NORM, SCALE_SIGN_BIASED, SCALE_SIGN_UNBIASED, SCALE_EDEN, SCALE_NORM_BETA = 0, 1, 2, 3, 4
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _lib = None
 
@@ -71,6 +71,8 @@ def load():
     L.rht_residual_score.argtypes = [vp, i32, vp, vp, vp, vp, i64, i32, i32, u64, vp, vp]
     L.rht_attention.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i32, i32, u64, u64, ctypes.c_float,
                                 vp, vp, ctypes.c_size_t, vp]
+    L.rht_attention_noalloc.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i32, i32, u64, u64, ctypes.c_float,
+                                        vp, vp]
     L.rht_attention_workspace_bytes.argtypes = [i64, i32, i64, i32]
     L.rht_attention_workspace_bytes.restype = ctypes.c_size_t
     L.rht_codebook.argtypes = [i32, vp, vp]
@@ -80,7 +82,8 @@ def load():
     L.rht_status_str.restype = ctypes.c_char_p
     L.rht_abi_version.restype = i32
     for f in ("rht_quantize", "rht_dequantize", "rht_residual_quantize", "rht_residual_dequantize",
-              "rht_score", "rht_score_sign", "rht_residual_score", "rht_attention", "rht_codebook",
+              "rht_score", "rht_score_sign", "rht_residual_score", "rht_attention", "rht_attention_noalloc",
+              "rht_codebook",
               "rht_codebook_beta", "rht_signs"):
         getattr(L, f).restype = i32
     if L.rht_abi_version() != ABI_VERSION:
@@ -131,6 +134,12 @@ def rht_attention(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, bits, s
                   out, workspace, workspace_bytes, stream=0):
     _ok(load().rht_attention(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, bits, seed_k, seed_v,
                              scale, out, workspace, workspace_bytes, stream), "rht_attention")
+
+
+def rht_attention_noalloc(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, bits, seed_k, seed_v, scale,
+                          out, stream=0):
+    _ok(load().rht_attention_noalloc(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, bits, seed_k,
+                                     seed_v, scale, out, stream), "rht_attention_noalloc")
 
 
 def rht_attention_workspace_bytes(heads, m, n, d) -> int:

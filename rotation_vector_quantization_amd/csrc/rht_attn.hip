@@ -34,8 +34,21 @@
 // A[l % 16][8 g + t], B holds B[8 g + t][l % 16], C holds C[4 g + r][l % 16].
 #include "rht_device.h"
 
+#include <atomic>
+#include <mutex>
+
 namespace rht {
 namespace {
+
+// Partial records of rht_attention_noalloc (which takes no workspace): one
+// array per device, in the code object, shared by every such call on that
+// device.  Host code never uses its name as an address; attention_scratch()
+// looks up each device's copy once with hipGetSymbolAddress.
+static __device__ __align__(256) float scratch[kAttnScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
 
 constexpr int kAD = 128;           // coordinates per vector
 constexpr int kACodeBytes = 64;    // 4-bit codes per row
@@ -672,6 +685,27 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(const AttnArgs a) {
 }
 
 }  // namespace
+
+hipError_t attention_scratch(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            // with device `dev` current: this device's copy of the array
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
+}
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
     const int64_t waves = a.heads * a.chunks;

@@ -73,6 +73,10 @@ constexpr int64_t kAttnMaxKeys = int64_t(1) << 26;
 // head, the combine kernel 64 per row).
 constexpr int64_t kAttnMaxRows = int64_t(1) << 24;
 
+// Size of the device array rht_attention_noalloc uses in place of a
+// workspace (one per device, for the life of the process).
+constexpr size_t kAttnScratchBytes = size_t(32) << 20;
+
 struct AttnArgs {
     const float *q;      // [heads][m][128]
     const uint8_t *kc;   // [heads][n][64]
@@ -101,6 +105,9 @@ hipError_t launch_dequantize(int d, bool f16out, int bits, Kind kind, int layout
 // plus the sign plane.
 hipError_t launch_score(int d, int bits, bool residual, const ScoreArgs &a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
+// Device address of the current device's attention scratch array
+// (kAttnScratchBytes), looked up on the first call per device.
+hipError_t attention_scratch(void **ptr);
 
 // The d = 128, fp16, 4-bit MSE encoder and decoder with the H_32 factor on
 // MFMA (launch_quantize / launch_dequantize pick them for that case).

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -46,7 +46,7 @@ def test_binding_has_every_declared_function():
 
 
 def test_abi_version(lib):
-    assert rht.rht_abi_version() == 4
+    assert rht.rht_abi_version() == 5
     for s in range(10):
         assert isinstance(rht.rht_status_str(s), str) and rht.rht_status_str(s)
 
@@ -151,6 +151,31 @@ def test_attention_validation_order(lib):
     need = rht.rht_attention_workspace_bytes(2, 4, 100, 128)
     assert need > 0
     assert _att(lib, wsb=need - 1) == E_WORKSPACE
+
+
+def _att_na(lib, q=FAKE, m=4, kc=FAKE, kn=FAKE, vc=FAKE, vn=FAKE, heads=2, n=100, d=128, bits=4, out=FAKE):
+    return lib.rht_attention_noalloc(q, m, kc, kn, vc, vn, heads, n, d, bits, 1, 2, 0.1, out, None)
+
+
+def test_attention_noalloc_validation_order(lib):
+    # the checks of rht_attention, in the same order, then the size of the
+    # library's own array; every case here returns before any device call
+    assert _att_na(lib, heads=-1, d=64) == E_COUNT
+    for m in (0, 17):
+        assert _att_na(lib, m=m, d=64) == E_COUNT
+    assert _att_na(lib, n=(1 << 26) + 1, d=64) == E_COUNT
+    assert _att_na(lib, d=64) == E_DIM
+    assert _att_na(lib, bits=3) == E_BITS
+    assert _att_na(lib, heads=0, q=0, kc=0, kn=0, vc=0, vn=0, out=0, n=0) == OK
+    for kw in ("q", "kc", "kn", "vc", "vn", "out"):
+        assert _att_na(lib, **{kw: 0}) == E_NULL, kw
+        assert _att_na(lib, **{kw: FAKE + 4}) == E_ALIGN, kw
+    cap = 32 << 20
+    # one key chunk per head beyond 3072 heads: 528 bytes per (head, query)
+    assert rht.rht_attention_workspace_bytes(4096, 16, 100, 128) == 4096 * 16 * 528 > cap
+    assert _att_na(lib, heads=4096, m=16) == E_WORKSPACE
+    assert _att_na(lib, heads=1 << 20, m=16, n=5) == E_WORKSPACE
+    assert rht.rht_attention_workspace_bytes(256, 4, 32768, 128) <= cap   # the KV-cache block fits
 
 
 def test_attention_workspace_bytes(lib):
