@@ -11,8 +11,10 @@ Prints one JSON line.  `value` is vectors per second through the whole step
 (every vector is encoded and decoded once per step).  `roofline` is for the
 slower of the two kernels, from HIP events on the stream the kernels run on;
 algorithmic bytes are 256 B in + 64 B codes + 4 B norm per vector for the
-encoder and the same 324 B for the decoder.  `cpu_baseline` times the oracle
-(single thread) on a bounded sample of the same rows.
+encoder and the same 324 B for the decoder.  `shape_ceiling` times trivial
+streaming kernels with each direction's exact traffic (the achievable
+ceiling of these shapes).  `cpu_baseline` times the oracle on every host
+thread over the whole K tensor (and on one thread over a bounded sample).
 """
 import argparse
 import hashlib
@@ -275,19 +277,99 @@ def attention_workload(torch, rht, dev, stream, ck, nk, cv, nv, n_vec, d):
                        "workspace_bytes": need})
 
 
-def cpu_baseline(rows):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads():
+    """Worker threads for the all-cores oracle leg: the CPUs this process may
+    run on, at most 16 (one GPU's share of a GPU host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(x_host, rows_single):
+    """The oracle (plain fp64 C, unchanged) on the K tensor of the KV block:
+    quantize + dequantize to fp16.  One thread on the first `rows_single`
+    rows, then every host thread on the whole tensor, the rows split into
+    equal contiguous shards (each vector is independent; the ctypes calls
+    release the GIL, so the shards run in parallel)."""
+    import concurrent.futures
+
     import oracle
     import testdata
 
     w = testdata.WORKLOADS["c2k"]
-    x = testdata.generate(w, 0, rows)
+
+    def run(lo, hi):
+        codes, norms = oracle.quantize(x_host[lo:hi], w.bits, w.rot_seed)
+        oracle.dequantize(codes, norms, w.d, w.bits, w.rot_seed, np.float16)
+
     t0 = time.perf_counter()
-    codes, norms = oracle.quantize(x, w.bits, w.rot_seed)
-    oracle.dequantize(codes, norms, w.d, w.bits, w.rot_seed, np.float16)
-    dt = time.perf_counter() - t0
-    return {"value": rows / dt, "unit": "vectors/s", "cores": 1, "kind": "oracle",
-            "sample": "first %d K vectors of the KV-cache block, quantize + dequantize, "
-                      "single-threaded fp64 oracle (%.1f s)" % (rows, dt)}
+    run(0, rows_single)
+    dt1 = time.perf_counter() - t0
+    threads = host_threads()
+    rows = x_host.shape[0]
+    edges = np.linspace(0, rows, 4 * threads + 1).astype(np.int64)
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda i: run(int(edges[i]), int(edges[i + 1])), range(len(edges) - 1)))
+    dtn = time.perf_counter() - t0
+    return {"value": rows / dtn, "unit": "vectors/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": "all %d K vectors of the KV-cache block, quantize + dequantize to fp16, fp64 oracle "
+                      "on %d threads over %d equal row shards (%.1f s)" % (rows, threads, len(edges) - 1, dtn),
+            "single_thread": {"value": rows_single / dt1, "unit": "vectors/s", "cores": 1,
+                              "sample": "first %d K vectors, same work, one thread (%.1f s)" % (rows_single, dt1)}}
+
+
+def ceiling(torch, dev, stream, xk, ck, nk, yk, n):
+    """Trivial streaming kernels with each direction's exact traffic (encode
+    shape: 256 B in, 64 + 4 B out per vector; decode shape: the reverse), on
+    the same buffers, at 1-8 blocks of 256 threads per CU.  The fastest
+    occupancy is each shape's achievable ceiling."""
+    import ctypes
+
+    import rotation_vector_quantization_amd.build as rb
+
+    if not os.path.exists(rb.CEIL_LIB):
+        return None
+    L = ctypes.CDLL(rb.CEIL_LIB)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.ceiling_encode_shape.argtypes = [vp, vp, vp, i64, i32, vp]
+    L.ceiling_decode_shape.argtypes = [vp, vp, vp, i64, i32, vp]
+    sh = stream.cuda_stream
+    c2 = torch.empty_like(ck)
+    n2 = torch.empty_like(nk)
+    out = {}
+    per_launch = n * BYTES_PER_VECTOR
+    for shape, fn in (("encode_shape", lambda bpc: L.ceiling_encode_shape(xk.data_ptr(), c2.data_ptr(),
+                                                                           n2.data_ptr(), n, bpc, sh)),
+                      ("decode_shape", lambda bpc: L.ceiling_decode_shape(ck.data_ptr(), nk.data_ptr(),
+                                                                           yk.data_ptr(), n, bpc, sh))):
+        sweep = {}
+        for bpc in (1, 2, 3, 4, 6, 8):
+            if fn(bpc) != 0:
+                raise RuntimeError("ceiling kernel %s failed to launch" % shape)
+            ms = float(np.median(time_launches(torch, stream, lambda i: fn(bpc), 1)))
+            sweep[bpc] = ms
+        best = min(sweep, key=sweep.get)
+        gbs = per_launch / (sweep[best] / 1e3) / 1e9
+        out[shape] = {"ms_median_by_blocks_per_cu": sweep, "best_blocks_per_cu": best,
+                      "ms_median": sweep[best], "GB_per_s": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS,
+                      "bytes_per_launch": per_launch}
+    del c2, n2
+    return out
 
 
 def main():
@@ -295,7 +377,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=25)
-    ap.add_argument("--cpu-rows", type=int, default=3 << 20)
+    ap.add_argument("--cpu-rows", type=int, default=1 << 20,
+                    help="rows of the single-thread oracle leg (the all-cores leg takes every K row)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip timing the DRIVE, residual and scoring workloads")
@@ -324,7 +407,8 @@ def main():
     wk, wv = testdata.WORKLOADS["c2k"], testdata.WORKLOADS["c2v"]
     n, d, bits = wk.n, wk.d, wk.bits
     print("generating K and V (%d x %d fp16 each)" % (n, d), file=sys.stderr, flush=True)
-    xk = torch.from_numpy(testdata.generate(wk)).to(dev)
+    xk_host = testdata.generate(wk)
+    xk = torch.from_numpy(xk_host).to(dev)
     xv = torch.from_numpy(testdata.generate(wv)).to(dev)
     ck = torch.empty((n, d * bits // 8), dtype=torch.uint8, device=dev)
     cv = torch.empty_like(ck)
@@ -436,12 +520,17 @@ def main():
             ("quantize_K", "quantize_V", "dequantize_K", "dequantize_V"))},
         "copy_ceiling": {"GB_per_s": copy_gbs, "frac_of_peak": copy_gbs / HBM_PEAK_GBS,
                          "bytes": 2 * COPY_BYTES, "kernel": "torch device copy"},
+        "shape_ceiling": None,
         "wall_s_timed_region": wall,
         "cpu_baseline": None,
     }
+    attn = None
     if not args.no_other_workloads:
         print("timing attention over the KV block", file=sys.stderr, flush=True)
         attn = attention_workload(torch, rht, dev, stream, ck, nk, cv, nv, n, d)
+    print("timing the streaming ceiling kernels", file=sys.stderr, flush=True)
+    out["shape_ceiling"] = ceiling(torch, dev, stream, xk, ck, nk, yk, n)
+    if not args.no_other_workloads:
         del xk, xv, ck, cv, nk, nv, yk, yv
         torch.cuda.empty_cache()
         print("timing the DRIVE, residual and scoring workloads", file=sys.stderr, flush=True)
@@ -449,7 +538,7 @@ def main():
         out["other_workloads"]["attention"] = attn
     if not args.no_cpu_baseline:
         print("timing the CPU oracle on %d vectors" % args.cpu_rows, file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(xk_host, min(args.cpu_rows, n))
     print(json.dumps(out), flush=True)
 
 

@@ -1,4 +1,5 @@
-"""Build librht.so in-tree: hipcc for gfx950, no JIT, no torch extension."""
+"""Build librht.so (and the benchmark's libstream_ceiling.so) in-tree: hipcc for gfx950,
+no JIT, no torch extension."""
 from __future__ import annotations
 
 import concurrent.futures
@@ -10,6 +11,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librht.so")
+# trivial streaming kernels the benchmark times as the achievable ceiling of
+# the KV-block shapes (not part of librht or its ABI)
+CEIL_SRC = os.path.join(HERE, "bench_kernels", "stream_ceiling.hip")
+CEIL_LIB = os.path.join(HERE, "libstream_ceiling.so")
 ARCH = os.environ.get("RHT_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 instructions stay off: hipcc -O3 would otherwise form
@@ -42,10 +47,13 @@ def build(verbose: bool = False) -> str:
         flags = DEVICE_FLAGS if ext == ".hip" else HOST_FLAGS
         jobs.append(["hipcc"] + flags + ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    ceil_tmp = CEIL_LIB + ".tmp%d" % os.getpid()
+    jobs.append(["hipcc"] + DEVICE_FLAGS + ["-shared", CEIL_SRC, "-o", ceil_tmp])
     with concurrent.futures.ThreadPoolExecutor(min(len(jobs), 8)) as ex:
         for out in ex.map(_run, jobs):
             if verbose and out.strip():
                 print(out)
+    os.replace(ceil_tmp, CEIL_LIB)
     tmp = LIB + ".tmp%d" % os.getpid()
     _run(["hipcc", "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs)
     os.replace(tmp, LIB)
