@@ -24,8 +24,10 @@
  *     (RHT_E_MODE), element type (RHT_E_DTYPE); then n == 0 (or m == 0)
  *     returns RHT_OK without touching any pointer; then NULL pointers
  *     (RHT_E_NULL) and alignment (RHT_E_ALIGN).  The first failing check is
- *     returned and nothing is launched.  Launch failures come back as
- *     RHT_E_DEVICE.  No call prints, aborts or throws.
+ *     returned and nothing is launched.  A failed launch comes back as
+ *     RHT_E_DEVICE: the status of the call's own launches, not an error
+ *     some earlier HIP call left pending on the thread (that stays for the
+ *     caller's hipGetLastError).  No call prints, aborts or throws.
  *   - The same (d, bits, seed) must be used to encode and to decode.  The
  *     rotation depends on the seed only (signs = top bits of the SplitMix64
  *     stream started at `seed`, see rht_signs), never on the data.
@@ -132,7 +134,7 @@ rht_status rht_residual_dequantize(const uint8_t *codes, const uint8_t *signs, c
  * attention scale, no softmax.
  *   q      [m][d] fp32, 0 <= m <= 64;  codes [n][bits*d/8], norms [n] fp32 as
  *          written by rht_quantize(..., RHT_SCALE_NORM, seed, ...).
- *   logits [m][n] fp32 written.  d in {64, 128, 256}; bits 1..4. */
+ *   logits [m][n] fp32 written.  d a power of two in [32, 4096]; bits 1..4. */
 rht_status rht_score(const float *q, int32_t m, const uint8_t *codes, const float *norms, int64_t n,
                      int32_t d, int32_t bits, uint64_t seed, float *logits, void *stream);
 
@@ -144,7 +146,7 @@ rht_status rht_score(const float *q, int32_t m, const uint8_t *codes, const floa
  *   logits[j][k] = (S_k / sqrt(d)) * sum_i (H D q_j)_i sigma_{k,i},  sigma = +-1.
  * With the unbiased scale their mean over rotation seeds is <q_j, x_k>.
  *   q [m][d] fp32, 0 <= m <= 64; bits [n][d/8]; scale [n] fp32;
- *   logits [m][n] fp32 written.  d in {64, 128, 256}. */
+ *   logits [m][n] fp32 written.  d a power of two in [32, 4096]. */
 rht_status rht_score_sign(const float *q, int32_t m, const uint8_t *bits, const float *scale, int64_t n,
                           int32_t d, uint64_t seed, float *logits, void *stream);
 
@@ -154,7 +156,7 @@ rht_status rht_score_sign(const float *q, int32_t m, const uint8_t *bits, const 
  *                + (S_r,k / sqrt(d)) sum_i (H D q_j)_i sigma_{k,i}
  * = <q_j, x^_k> for the vectors rht_residual_dequantize returns.  Arguments
  * as written by rht_residual_quantize (total bits 2..4); q [m][d] fp32,
- * 0 <= m <= 64; logits [m][n] fp32 written; d in {64, 128, 256}. */
+ * 0 <= m <= 64; logits [m][n] fp32 written; d a power of two in [32, 4096]. */
 rht_status rht_residual_score(const float *q, int32_t m, const uint8_t *codes, const uint8_t *signs,
                               const float *norms, const float *res_scale, int64_t n, int32_t d, int32_t bits,
                               uint64_t seed, float *logits, void *stream);

@@ -433,7 +433,7 @@ rht_status rht_residual_dequantize(const uint8_t *codes, const uint8_t *signs, c
 rht_status rht_score(const float *q, int32_t m, const uint8_t *codes, const float *norms, int64_t n,
                      int32_t d, int32_t bits, uint64_t seed, float *logits, void *stream) {
     if (n < 0 || m < 0 || m > 64) return RHT_E_COUNT;
-    if (d != 64 && d != 128 && d != 256) return RHT_E_DIM;
+    if (!pow2_dim(d)) return RHT_E_DIM;
     if (bits < 1 || bits > 4) return RHT_E_BITS;
     if (n == 0 || m == 0) return RHT_OK;
     if (!q || !codes || !norms || !logits) return RHT_E_NULL;
@@ -456,7 +456,7 @@ rht_status rht_score(const float *q, int32_t m, const uint8_t *codes, const floa
 rht_status rht_score_sign(const float *q, int32_t m, const uint8_t *bits, const float *scale, int64_t n,
                           int32_t d, uint64_t seed, float *logits, void *stream) {
     if (n < 0 || m < 0 || m > 64) return RHT_E_COUNT;
-    if (d != 64 && d != 128 && d != 256) return RHT_E_DIM;
+    if (!pow2_dim(d)) return RHT_E_DIM;
     if (n == 0 || m == 0) return RHT_OK;
     if (!q || !bits || !scale || !logits) return RHT_E_NULL;
     if (!aligned(q) || !aligned(bits) || !aligned(scale) || !aligned(logits)) return RHT_E_ALIGN;
@@ -481,7 +481,7 @@ rht_status rht_residual_score(const float *q, int32_t m, const uint8_t *codes, c
                               const float *norms, const float *res_scale, int64_t n, int32_t d, int32_t bits,
                               uint64_t seed, float *logits, void *stream) {
     if (n < 0 || m < 0 || m > 64) return RHT_E_COUNT;
-    if (d != 64 && d != 128 && d != 256) return RHT_E_DIM;
+    if (!pow2_dim(d)) return RHT_E_DIM;
     if (bits < 2 || bits > 4) return RHT_E_BITS;
     if (n == 0 || m == 0) return RHT_OK;
     if (!q || !codes || !signs || !norms || !res_scale || !logits) return RHT_E_NULL;

@@ -710,17 +710,12 @@ hipError_t attention_scratch(void **ptr) {
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
     const int64_t waves = a.heads * a.chunks;
     const dim3 grid((unsigned)((waves + kAWaves - 1) / kAWaves));
-    if (a.m <= 4)
-        hipLaunchKernelGGL(k_attn_partial<4>, grid, dim3(kABlock), 0, s, a);
-    else if (a.m <= 8)
-        hipLaunchKernelGGL(k_attn_partial<8>, grid, dim3(kABlock), 0, s, a);
-    else
-        hipLaunchKernelGGL(k_attn_partial<16>, grid, dim3(kABlock), 0, s, a);
-    hipError_t e = hipGetLastError();
+    const hipError_t e = a.m <= 4   ? launch(k_attn_partial<4>, grid, dim3(kABlock), s, a)
+                         : a.m <= 8 ? launch(k_attn_partial<8>, grid, dim3(kABlock), s, a)
+                                    : launch(k_attn_partial<16>, grid, dim3(kABlock), s, a);
     if (e != hipSuccess) return e;
     const int64_t rows = a.heads * a.m;
-    hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)((rows + kWaves - 1) / kWaves)), dim3(kBlock), 0, s, a);
-    return hipGetLastError();
+    return launch(k_attn_combine, dim3((unsigned)((rows + kWaves - 1) / kWaves)), dim3(kBlock), s, a);
 }
 
 }  // namespace rht

@@ -68,6 +68,17 @@ __device__ __forceinline__ uint32_t nearest_code(const uint2 *lut, float y16) {
     return e.y + (y16 >= __builtin_bit_cast(float, e.x) ? 1u : 0u);
 }
 
+// Queue kernel(args...) on `s` and return the status of this launch itself:
+// hipLaunchKernel reports the launch it was handed, where hipGetLastError
+// would also return (and clear) an error that an earlier, unrelated HIP call
+// on this thread left behind.
+template <typename... P, typename... A>
+inline hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t s, const A &...args) {
+    static_assert(sizeof...(P) == sizeof...(A), "one argument per kernel parameter");
+    void *argv[] = {const_cast<void *>(static_cast<const void *>(&args))...};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, 0, s);
+}
+
 // ---------------------------------------------------------------------------
 // Grid sizing.  Grids are sized to what is resident at once (CUs x
 // blocks per CU from the occupancy calculator), so every block of the

@@ -1318,6 +1318,97 @@ __global__ __launch_bounds__(kBlock) void k_score(const ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Scoring for d >= 512.  The rotated queries of a whole block do not fit in
+// LDS at these d, so a block serves a group of QG queries (QG * d fp32 in LDS,
+// QG = 32, 16, 8, 4 at d = 512 ... 4096) and the m queries take ceil(m / QG)
+// groups.  A wave's lane (key col, K half par) walks its key's code row in
+// chunks of 256 coordinates (whole words for every code width), so only one
+// chunk of codes is in registers at a time; the contraction is
+// v_mfma_f32_32x32x2_f32 as in k_score (query rows past QG repeat the group's
+// last query and are not stored).  Blocks are placed so that the G groups
+// scoring the same key tiles sit on one XCD (blocks are dispatched to the eight
+// XCDs in turn: block b runs on XCD b % 8): the G reads of a code row after
+// the first can hit that XCD's L2.
+template <int N>
+__device__ __forceinline__ void load_words_x4(const uint32_t *src, uint32_t (&w)[N]) {
+    static_assert(N % 4 == 0, "whole 16-byte pieces");
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) {
+        const uint4 t = reinterpret_cast<const uint4 *>(src)[k];
+        w[4 * k] = t.x; w[4 * k + 1] = t.y; w[4 * k + 2] = t.z; w[4 * k + 3] = t.w;
+    }
+}
+
+template <int D>
+constexpr int wide_score_group() { return D >= 4096 ? 4 : 16384 / D; }
+
+template <int D, int BITS, bool RES>
+__global__ __launch_bounds__(kBlock) void k_score_wide(const ScoreArgs a) {
+    constexpr int QG = wide_score_group<D>();
+    constexpr int QS = QG + 1;               // LDS stride of a coordinate row of qt
+    constexpr int KC = 256;                  // coordinates per chunk of a code row
+    constexpr int CW = KC * BITS / 32;       // code words per chunk
+    constexpr int ROWW = D * BITS / 32;      // code words per key
+    static_assert(D >= 512 && CW % 4 == 0, "chunks are whole 16-byte pieces");
+    __shared__ float qt[D * QS];
+    __shared__ float slev[16];
+
+    const uint32_t lane = lane_id(), wave = threadIdx.x >> 6;
+    const int G = (a.m + QG - 1) / QG;
+    const uint32_t b = blockIdx.x, slot = b / 8, xcd = b % 8;
+    const int grp = (int)(slot % (uint32_t)G);
+    const int64_t tb = (int64_t)(slot / (uint32_t)G) * 8 + xcd, ntb = gridDim.x / G;
+    if (threadIdx.x < 16) slev[threadIdx.x] = a.lev[threadIdx.x];
+    rotate_queries<D, QS, QG>(a, qt, nullptr, grp * QG);
+    __syncthreads();
+
+    const uint32_t col = lane & 31u, par = lane >> 5;
+    const uint32_t qcol = col < (uint32_t)QG ? col : (uint32_t)QG - 1;
+    const int64_t ntiles = (a.n + 31) / 32;
+    for (int64_t tile = tb * kWaves + wave; tile < ntiles; tile += ntb * kWaves) {
+        const int64_t key = tile * 32 + col;
+        const bool valid = key < a.n;
+        const int64_t row = valid ? key : a.n - 1;
+        float na = 0.0f, nb = 0.0f;
+        if constexpr (RES) {
+            na = a.norms[row] * (1.0f / D);
+            nb = a.res_scale[row] * (1.0f / __builtin_sqrtf((float)D));
+        }
+        const uint32_t *crow = reinterpret_cast<const uint32_t *>(a.codes) + row * ROWW;
+        floatx16 acc = {};
+        for (int c = 0; c < D / KC; ++c) {
+            uint32_t w[CW];
+            load_words_x4<CW>(crow + c * CW, w);
+            uint32_t sw[RES ? KC / 32 : 4];
+            if constexpr (RES)
+                load_words_x4<KC / 32>(reinterpret_cast<const uint32_t *>(a.signs) + row * (D / 32) + c * (KC / 32),
+                                       sw);
+            const float *qc = qt + (size_t)c * KC * QS;
+#pragma unroll
+            for (int s = 0; s < KC / 2; ++s) {
+                const uint32_t c0 = get_code<BITS, CW>(w, 2 * s), c1 = get_code<BITS, CW>(w, 2 * s + 1);
+                const int i = 2 * s + (int)par;  // coordinate within the chunk
+                float bv = slev[par ? c1 : c0];
+                if constexpr (RES) {
+                    const float sg = ((sw[i >> 5] >> (i & 31)) & 1u) ? nb : -nb;
+                    bv = fmaf(na, bv, sg);
+                }
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qc[i * QS + qcol], bv, acc, 0, 0, 0);
+            }
+        }
+        if (valid) {
+            const float sc = RES ? 1.0f : a.norms[key] * a.key_mult;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qrow = 8 * (r / 4) + 4 * (int)par + (r % 4);
+                const int qq = grp * QG + qrow;
+                if (qrow < QG && qq < a.m) stream_store(acc[r] * sc, a.logits + (int64_t)qq * a.n + key);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Scoring on the fp16 matrix cores at fp32-level accuracy (d <= 128).
 // logits[q][k] = f_k 2^-e_q sum_i Qs[q][i] C[k][i]: Qs = 2^e_q (H D q) with e_q
 // putting the largest |coordinate| of query q in [2^14, 2^15), split into fp16
@@ -1597,9 +1688,8 @@ constexpr int vecs_per_block() { return kWaves * (64 / lanes_per_vec(D)); }
 template <int D, int G, bool F16, int BITS, int KIND>
 hipError_t run_q(const QuantArgs &a, hipStream_t s) {
     static const int per_cu = resident_blocks(k_quantize<D, G, F16, BITS, KIND>);
-    hipLaunchKernelGGL((k_quantize<D, G, F16, BITS, KIND>), dim3(grid_for(a.n, vecs_per_block<D>(), per_cu)),
-                       dim3(kBlock), 0, s, a);
-    return hipGetLastError();
+    return launch(k_quantize<D, G, F16, BITS, KIND>, dim3(grid_for(a.n, vecs_per_block<D>(), per_cu)),
+                  dim3(kBlock), s, a);
 }
 
 // grid_for with a kernel's own cap on resident blocks per CU, below the
@@ -1614,25 +1704,22 @@ hipError_t run_dq(const DequantArgs &a, hipStream_t s) {
     // the decoder's traffic is mostly writes, and HBM write throughput drops
     // with many concurrent writers: two blocks per CU (DRIVE d = 1024 fp32
     // decode: 0.054 -> 0.052 ms)
-    hipLaunchKernelGGL((k_dequantize<D, G, F16, BITS, KIND>),
-                       dim3(capped_grid(a.n, vecs_per_block<D>(), per_cu, 2)), dim3(kBlock), 0, s, a);
-    return hipGetLastError();
+    return launch(k_dequantize<D, G, F16, BITS, KIND>, dim3(capped_grid(a.n, vecs_per_block<D>(), per_cu, 2)),
+                  dim3(kBlock), s, a);
 }
 
 template <int CB>
 hipError_t run_res256_cb(const QuantArgs &a, hipStream_t s) {
     static const int per_cu = resident_blocks(k_residual_quantize_mfma256<CB>);
-    hipLaunchKernelGGL(k_residual_quantize_mfma256<CB>, dim3(grid_for(a.n, kWaves * kR256Rows, per_cu)), dim3(kBlock),
-                       0, s, a);
-    return hipGetLastError();
+    return launch(k_residual_quantize_mfma256<CB>, dim3(grid_for(a.n, kWaves * kR256Rows, per_cu)), dim3(kBlock),
+                  s, a);
 }
 
 template <int CB>
 hipError_t run_rdq256_cb(const DequantArgs &a, hipStream_t s) {
     static const int per_cu = resident_blocks(k_residual_dequantize_mfma256<CB>);
-    hipLaunchKernelGGL(k_residual_dequantize_mfma256<CB>, dim3(grid_for(a.n, kWaves * kR256Rows, per_cu)),
-                       dim3(kBlock), 0, s, a);
-    return hipGetLastError();
+    return launch(k_residual_dequantize_mfma256<CB>, dim3(grid_for(a.n, kWaves * kR256Rows, per_cu)),
+                  dim3(kBlock), s, a);
 }
 
 hipError_t run_res256(int cb, const QuantArgs &a, hipStream_t s) {
@@ -1737,8 +1824,7 @@ hipError_t run_score(const ScoreArgs &a, hipStream_t s) {
     const int64_t cap = (int64_t)device_cu_count() * 2;
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL((k_score<D, BITS, RES>), dim3((int)blocks), dim3(kBlock), 0, s, a);
-    return hipGetLastError();
+    return launch(k_score<D, BITS, RES>, dim3((int)blocks), dim3(kBlock), s, a);
 }
 
 template <int D, int BITS, bool RES, bool EXACT>
@@ -1752,8 +1838,42 @@ hipError_t run_score_mfma(const ScoreArgs &a, hipStream_t s) {
     // keys; MSE and residual codes unchanged)
     int blocks = capped_grid(items, kWaves, per_cu, 2);
     if (rh == 2) blocks = (blocks + 15) / 16 * 16;  // the kernel pairs blocks b and b + 8
-    hipLaunchKernelGGL((k_score_mfma<D, BITS, RES, EXACT>), dim3(blocks), dim3(kBlock), 0, s, a);
-    return hipGetLastError();
+    return launch(k_score_mfma<D, BITS, RES, EXACT>, dim3(blocks), dim3(kBlock), s, a);
+}
+
+template <int D, int BITS, bool RES>
+hipError_t run_score_wide(const ScoreArgs &a, hipStream_t s) {
+    static const int per_cu = resident_blocks(k_score_wide<D, BITS, RES>);
+    constexpr int QG = wide_score_group<D>();
+    const int64_t G = (a.m + QG - 1) / QG;
+    const int64_t tiles = (a.n + 31) / 32;
+    // tile-blocks (kWaves tiles per round each), a multiple of 8 so every
+    // group of a tile-block sits on the same XCD; at most what is resident
+    int64_t tbs = (tiles + kWaves - 1) / kWaves;
+    const int64_t cap_tbs = (int64_t)device_cu_count() * min(per_cu, 2) / G;
+    if (tbs > cap_tbs) tbs = cap_tbs;
+    tbs = (tbs + 7) / 8 * 8;
+    if (tbs < 8) tbs = 8;
+    return launch(k_score_wide<D, BITS, RES>, dim3((unsigned)(tbs * G)), dim3(kBlock), s, a);
+}
+
+template <int D>
+hipError_t score_wide_d(int bits, bool residual, const ScoreArgs &a, hipStream_t s) {
+    if (residual) {
+        switch (bits) {
+        case 1: return run_score_wide<D, 1, true>(a, s);
+        case 2: return run_score_wide<D, 2, true>(a, s);
+        case 3: return run_score_wide<D, 3, true>(a, s);
+        }
+        return hipErrorInvalidValue;
+    }
+    switch (bits) {
+    case 1: return run_score_wide<D, 1, false>(a, s);
+    case 2: return run_score_wide<D, 2, false>(a, s);
+    case 3: return run_score_wide<D, 3, false>(a, s);
+    case 4: return run_score_wide<D, 4, false>(a, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int D>
@@ -1831,9 +1951,14 @@ hipError_t launch_dequantize(int d, bool f16out, int bits, Kind kind, int layout
 
 hipError_t launch_score(int d, int bits, bool residual, const ScoreArgs &a, hipStream_t s) {
     switch (d) {
+    case 32: return score_d<32>(bits, residual, a, s);
     case 64: return score_d<64>(bits, residual, a, s);
     case 128: return score_d<128>(bits, residual, a, s);
     case 256: return score_d<256>(bits, residual, a, s);
+    case 512: return score_wide_d<512>(bits, residual, a, s);
+    case 1024: return score_wide_d<1024>(bits, residual, a, s);
+    case 2048: return score_wide_d<2048>(bits, residual, a, s);
+    case 4096: return score_wide_d<4096>(bits, residual, a, s);
     }
     return hipErrorInvalidValue;
 }

@@ -346,14 +346,12 @@ __global__ __launch_bounds__(kBlock) void k_dequantize_mfma128(const DequantArgs
 
 hipError_t launch_quantize_kv128(const QuantArgs &a, hipStream_t s) {
     static const int per_cu = resident_blocks(k_quantize_mfma128);
-    hipLaunchKernelGGL(k_quantize_mfma128, dim3(grid_for(a.n, kWaves * kRowsPerWave, per_cu)), dim3(kBlock), 0, s, a);
-    return hipGetLastError();
+    return launch(k_quantize_mfma128, dim3(grid_for(a.n, kWaves * kRowsPerWave, per_cu)), dim3(kBlock), s, a);
 }
 
 hipError_t launch_dequantize_kv128(const DequantArgs &a, hipStream_t s) {
     static const int per_cu = resident_blocks(k_dequantize_mfma128);
-    hipLaunchKernelGGL(k_dequantize_mfma128, dim3(grid_for(a.n, kWaves * kRowsPerWave, per_cu)), dim3(kBlock), 0, s, a);
-    return hipGetLastError();
+    return launch(k_dequantize_mfma128, dim3(grid_for(a.n, kWaves * kRowsPerWave, per_cu)), dim3(kBlock), s, a);
 }
 
 }  // namespace rht

@@ -110,7 +110,8 @@ def test_other_entry_points_validate(lib):
     assert L.rht_residual_dequantize(FAKE, FAKE, FAKE, FAKE + 2, 1, 256, 3, 1, FAKE, 1, None) == E_ALIGN
     assert L.rht_score(FAKE, 65, FAKE, FAKE, 1, 128, 4, 1, FAKE, None) == E_COUNT
     assert L.rht_score(FAKE, -1, FAKE, FAKE, 1, 128, 4, 1, FAKE, None) == E_COUNT
-    assert L.rht_score(FAKE, 8, FAKE, FAKE, 1, 512, 4, 1, FAKE, None) == E_DIM
+    assert L.rht_score(FAKE, 8, FAKE, FAKE, 1, 8192, 4, 1, FAKE, None) == E_DIM
+    assert L.rht_score(FAKE, 8, FAKE, FAKE, 1, 16, 4, 1, FAKE, None) == E_DIM
     assert L.rht_score(FAKE, 8, FAKE, FAKE, 1, 128, 0, 1, FAKE, None) == E_BITS
     assert L.rht_score(0, 0, 0, 0, 5, 128, 4, 1, 0, None) == OK
     assert L.rht_codebook(0, None, None) == E_BITS
@@ -193,13 +194,14 @@ def test_sign_and_residual_score_validation(lib):
     S = lib.rht_score_sign
     assert S(FAKE, 65, FAKE, FAKE, 10, 128, 1, FAKE, None) == E_COUNT
     assert S(FAKE, 4, FAKE, FAKE, -1, 128, 1, FAKE, None) == E_COUNT
-    assert S(FAKE, 4, FAKE, FAKE, 10, 32, 1, FAKE, None) == E_DIM
+    for d in (16, 100, 8192):
+        assert S(FAKE, 4, FAKE, FAKE, 10, d, 1, FAKE, None) == E_DIM
     assert S(0, 0, 0, 0, 10, 128, 1, 0, None) == OK
     assert S(FAKE, 4, 0, FAKE, 10, 128, 1, FAKE, None) == E_NULL
     assert S(FAKE, 4, FAKE + 4, FAKE, 10, 128, 1, FAKE, None) == E_ALIGN
     R = lib.rht_residual_score
     assert R(FAKE, 65, FAKE, FAKE, FAKE, FAKE, 10, 128, 3, 1, FAKE, None) == E_COUNT
-    assert R(FAKE, 4, FAKE, FAKE, FAKE, FAKE, 10, 512, 3, 1, FAKE, None) == E_DIM
+    assert R(FAKE, 4, FAKE, FAKE, FAKE, FAKE, 10, 96, 3, 1, FAKE, None) == E_DIM
     for b in (1, 5):
         assert R(FAKE, 4, FAKE, FAKE, FAKE, FAKE, 10, 128, b, 1, FAKE, None) == E_BITS
     assert R(FAKE, 4, FAKE, FAKE, FAKE, FAKE, 0, 128, 3, 1, FAKE, None) == OK

@@ -169,7 +169,7 @@ SCORE_N = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 511, 512, 513, 1025]
 
 @pytest.mark.parametrize("kind", ["mse4", "mse2", "sign", "res3"])
 @pytest.mark.parametrize("m", [1, 32, 33, 64])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128, 1024])
 def test_score_key_counts(d, m, kind):
     """Logits [m][n] for key counts around the 32-key tiles and 64-key items; the
     buffer carries sentinel bytes past m * n.  Every logit <q, k^> must be within

@@ -1,6 +1,8 @@
 """GPU parity of scoring on sign-coded and residual-coded keys (rht_score_sign,
 rht_residual_score, through the C ABI) against the CPU oracle on identical
-code bytes produced by the oracle's encoders.  Rule: relative L2 <= SCORE_TOL
+code bytes produced by the oracle's encoders, at every d the encoders accept
+(32 ... 4096; d >= 512 runs the query-group kernel), and at the sizes of the
+scoring and the DRIVE workloads.  Rule: relative L2 <= SCORE_TOL
 per query row and over all logits, as for MSE-coded keys; keys whose scale is
 0 (zero vectors) must score exactly 0."""
 import sys
@@ -48,8 +50,11 @@ def check(got, ref, what):
     assert np.all(got[:, ~nz] == 0)
 
 
+ALL_D = [32, 64, 128, 256, 512, 1024, 2048, 4096]
+
+
 @pytest.mark.parametrize("unbiased", [False, True])
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", ALL_D)
 @pytest.mark.parametrize("m,n", [(1, 1), (17, 100), (64, 1037), (33, 31), (40, 65), (32, 64)])
 def test_sign_score_grid(unbiased, d, m, n):
     seed = 31 + d
@@ -64,7 +69,7 @@ def test_sign_score_grid(unbiased, d, m, n):
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", ALL_D)
 @pytest.mark.parametrize("m,n", [(1, 1), (17, 100), (64, 1037), (33, 31), (40, 65), (32, 64)])
 def test_residual_score_grid(bits, d, m, n):
     seed = 41 + d
@@ -98,3 +103,21 @@ def test_sign_and_residual_scores_at_the_scoring_workload_size():
     ref = np.concatenate(chunked(lambda lo, hi: oracle.score_residual(q, c[lo:hi], g[lo:hi], nr[lo:hi],
                                                                       rs[lo:hi], d, 3, seed), wk.n), axis=1)
     check(got, ref, "residual score, 131072 keys")
+
+
+def test_sign_scores_of_the_drive_workload():
+    """The DRIVE workload's own codes (65536 x 1024 Student-t rows, 1-bit signs
+    with the unbiased scale) scored against 64 queries: d = 1024 runs the
+    query-group kernel, 4 groups of 16 queries over every key."""
+    w = testdata.WORKLOADS["c3"]
+    x = testdata.generate(w)
+    d, seed = w.d, w.rot_seed
+    parts = chunked(lambda lo, hi: oracle.sign_quantize(x[lo:hi], True, seed), w.n)
+    b = np.concatenate([p[0] for p in parts])
+    S = np.concatenate([p[1] for p in parts])
+    del x
+    q = np.random.default_rng(1004).standard_normal((64, d)).astype(np.float32)
+    say("sign codes of the DRIVE workload from the oracle")
+    got = host(rht.score_sign(dev(q), dev(b), dev(S), d, seed))
+    ref = np.concatenate(chunked(lambda lo, hi: oracle.score_sign(q, b[lo:hi], S[lo:hi], d, seed), w.n), axis=1)
+    check(got, ref, "sign score, DRIVE workload (65536 keys d=1024)")
