@@ -63,7 +63,7 @@ def chunked(fn, n: int, parts: int | None = None):
     """Run fn(lo, hi) over row ranges in threads (the oracle releases the GIL)."""
     parts = parts or threads()
     edges = np.linspace(0, n, parts + 1).astype(np.int64)
-    with concurrent.futures.ThreadPoolExecutor(parts) as ex:
+    with concurrent.futures.ThreadPoolExecutor(min(parts, threads())) as ex:
         return list(ex.map(lambda i: fn(int(edges[i]), int(edges[i + 1])), range(parts)))
 
 
@@ -118,6 +118,38 @@ def check_recon(gpu: np.ndarray, ref: np.ndarray, tol: float, what: str):
     # rows whose reference is exactly zero must decode to exactly zero
     assert np.all(gpu[~nz] == 0), "%s: zero rows not decoded to zero" % what
     return float(glob), float(per_row.max()) if per_row.size else 0.0
+
+
+def check_recon_all(gpu: np.ndarray, ref_rows, tol: float, what: str, rows_per_part: int = 1 << 16):
+    """check_recon over every row of a large output without a second full copy:
+    ref_rows(lo, hi) -> the oracle's rows [lo, hi); parts run in threads (the
+    oracle releases the GIL).  Same rules: per-row and global relative L2 <= tol,
+    zero reference rows decode to exactly zero.  Returns (global, worst row)."""
+    n = gpu.shape[0]
+    edges = list(range(0, n, rows_per_part)) + [n]
+
+    def part(i):
+        lo, hi = edges[i], edges[i + 1]
+        ref = ref_rows(lo, hi).astype(np.float64)
+        g = gpu[lo:hi].astype(np.float64)
+        den = (ref ** 2).sum(1)
+        num = ((g - ref) ** 2).sum(1)
+        nz = den > 0
+        worst = float(np.sqrt(num[nz] / den[nz]).max()) if nz.any() else 0.0
+        zero_ok = bool(np.all(g[~nz] == 0))
+        return float(num.sum()), float(den.sum()), worst, zero_ok, lo + (int(np.argmax(np.where(nz, num / np.maximum(den, 1e-300), 0))) if nz.any() else 0)
+
+    with concurrent.futures.ThreadPoolExecutor(threads()) as ex:
+        res = list(ex.map(part, range(len(edges) - 1)))
+    num = sum(r[0] for r in res)
+    den = sum(r[1] for r in res)
+    worst = max(r[2] for r in res)
+    at = max(res, key=lambda r: r[2])[4]
+    assert all(r[3] for r in res), "%s: zero rows not decoded to zero" % what
+    assert worst <= tol, "%s: worst row rel L2 %.3g > %.1g (row %d)" % (what, worst, tol, at)
+    glob = math.sqrt(num / max(den, 1e-300))
+    assert glob <= tol, "%s: global rel L2 %.3g > %.1g" % (what, glob, tol)
+    return glob, worst
 
 
 def check_rel(gpu: np.ndarray, ref: np.ndarray, rtol: float, what: str):

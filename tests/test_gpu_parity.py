@@ -18,7 +18,8 @@ import oracle
 import rotation_vector_quantization_amd as rht
 import testdata
 from parity import (RECON_F16, RECON_F32, NORM_RTOL, SCALE_RTOL, SCORE_TOL, NEAR_REL,
-                    MAX_NEAR_FRAC, check_codes, check_recon, check_rel, chunked, rel_l2, unpack)
+                    MAX_NEAR_FRAC, check_codes, check_recon, check_recon_all, check_rel, chunked, rel_l2,
+                    unpack)
 
 pytestmark = pytest.mark.gpu
 
@@ -265,7 +266,7 @@ def test_residual_decode_arbitrary_inputs(bits, n):
 
 # ------------------------------------------------------------------ scoring
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", [32, 64, 128, 256, 512, 1024, 2048, 4096])
 @pytest.mark.parametrize("m,n", [(1, 1), (17, 100), (64, 1037), (33, 31), (40, 65), (32, 64)])
 def test_score_grid(d, bits, m, n):
     seed = 5 + d
@@ -355,13 +356,12 @@ def test_workload_c2_kv_cache(name):
     w = testdata.WORKLOADS[name]
     x, codes, norms = _mse_workload(w, check_all_codes=True)
     del x
-    y = rht.dequantize(dev(codes), dev(norms), w.d, w.bits, w.rot_seed, dtype=torch.float16)
-    rows = np.sort(np.random.default_rng(w.seed + 1).choice(w.n, size=1 << 15, replace=False))
-    yr = host(y[torch.from_numpy(rows).to("cuda:0")])
-    del y
-    ref = oracle.dequantize(codes[rows], norms[rows], w.d, w.bits, w.rot_seed, np.float16)
-    glob, worst = check_recon(yr, ref, RECON_F16, name + " decode")
-    say("%s decode: global rel L2 %.2e, worst row %.2e" % (name, glob, worst))
+    # every row of the decode, on the GPU's own codes
+    y = host(rht.dequantize(dev(codes), dev(norms), w.d, w.bits, w.rot_seed, dtype=torch.float16))
+    glob, worst = check_recon_all(y, lambda lo, hi: oracle.dequantize(codes[lo:hi], norms[lo:hi], w.d, w.bits,
+                                                                      w.rot_seed, np.float16), RECON_F16,
+                                  name + " decode")
+    say("%s decode, all %d rows: global rel L2 %.2e, worst row %.2e" % (name, w.n, glob, worst))
 
 
 @pytest.mark.parametrize("mode", [rht.SCALE_SIGN_BIASED, rht.SCALE_SIGN_UNBIASED])
@@ -390,17 +390,19 @@ def test_workload_c4_residual():
     x = testdata.generate(w)
     say("c4 generated")
     codes, sg, norms, rs = [host(t) for t in rht.residual_quantize(dev(x), w.bits, w.rot_seed)]
-    rows = np.sort(np.random.default_rng(5).choice(w.n, size=1 << 15, replace=False))
-    check_residual(x, w.bits, w.rot_seed, codes, sg, norms, rs, rows=rows, what="c4")
+    # every row: stage-1 codes and norms against the oracle's, sign bits and S_r
+    # against the oracle run on the GPU's stage-1 codes (row shards in threads)
+    chunked(lambda lo, hi: check_residual(x, w.bits, w.rot_seed, codes, sg, norms, rs, rows=np.arange(lo, hi),
+                                          what="c4 rows %d-%d" % (lo, hi)), w.n, parts=64)
+    say("c4: all %d rows encoded as the oracle encodes them" % w.n)
     for odt, tol in (("f16", RECON_F16), ("f32", RECON_F32)):
-        y = rht.residual_dequantize(dev(codes), dev(sg), dev(norms), dev(rs), w.d, w.bits, w.rot_seed,
-                                    dtype=tdtype(odt))
-        yr = host(y[torch.from_numpy(rows[:4096]).to("cuda:0")])
+        y = host(rht.residual_dequantize(dev(codes), dev(sg), dev(norms), dev(rs), w.d, w.bits, w.rot_seed,
+                                         dtype=tdtype(odt)))
+        glob, worst = check_recon_all(y, lambda lo, hi: oracle.residual_dequantize(
+            codes[lo:hi], sg[lo:hi], norms[lo:hi], rs[lo:hi], w.d, w.bits, w.rot_seed, np_dtype(odt)), tol,
+            "c4 decode %s" % odt)
         del y
-        r4 = rows[:4096]
-        ref = oracle.residual_dequantize(codes[r4], sg[r4], norms[r4], rs[r4], w.d, w.bits, w.rot_seed,
-                                         np_dtype(odt))
-        check_recon(yr, ref, tol, "c4 decode %s" % odt)
+        say("c4 decode %s, all rows: global rel L2 %.2e, worst row %.2e" % (odt, glob, worst))
 
 
 def test_workload_c5_scoring():
