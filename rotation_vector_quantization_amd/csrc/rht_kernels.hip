@@ -491,8 +491,8 @@ __global__ __launch_bounds__(kBlock) void k_quantize(const QuantArgs a) {
             float S;
             if constexpr (KIND == kDriveBiased)
                 S = l1 / ((float)D * sqrt_d);
-            else
-                S = l1 > 0.0f ? ss * sqrt_d / l1 : 0.0f;
+            else  // ||x||^2 / ||Pi x||_1; ||x||^2 sqrt(d) could overflow where the result does not
+                S = l1 > 0.0f ? ss / (l1 / sqrt_d) : 0.0f;
             if (valid) {
                 uint32_t *dst = reinterpret_cast<uint32_t *>(a.codes) + vec * ROWW;
 #pragma unroll
