@@ -246,10 +246,11 @@ def other_workloads(torch, rht, dev, stream):
     return out
 
 
-def attention_workload(torch, rht, dev, stream, ck, nk, cv, nv, n_vec, d):
+def attention_workload(torch, rht, dev, stream, ck, nk, cv, nv, n_vec, d, k_bits=4, v_bits=4):
     """Decode attention over the KV block just encoded: 32 layers x 8 KV heads
     = 256 heads of 32768 tokens, 4 queries per KV head (grouped-query), scale
-    1/sqrt(d), logits and value sums in the rotated domains (rht_attention)."""
+    1/sqrt(d), logits and value sums in the rotated domains (rht_attention);
+    k_bits / v_bits are the widths of the key and value codes."""
     heads, m = 256, 4
     n = n_vec // heads
     g = torch.Generator(device=dev)
@@ -261,16 +262,16 @@ def attention_workload(torch, rht, dev, stream, ck, nk, cv, nv, n_vec, d):
     sh = stream.cuda_stream
     scale = 1.0 / math.sqrt(d)
     times = time_launches(torch, stream, lambda i: rht.rht_attention(
-        q.data_ptr(), m, ck.data_ptr(), nk.data_ptr(), cv.data_ptr(), nv.data_ptr(), heads, n, d, 4,
-        42, 43, scale, out.data_ptr(), ws.data_ptr(), need, sh), 1)
+        q.data_ptr(), m, ck.data_ptr(), nk.data_ptr(), cv.data_ptr(), nv.data_ptr(), heads, n, d, k_bits,
+        v_bits, 42, 43, scale, out.data_ptr(), ws.data_ptr(), need, sh), 1)
     st = stats(times)
     ms = st["ms_median"]
     # codes and norms of K and V, the queries and the outputs
-    alg = 2 * n_vec * (d // 2 + 4) + 2 * heads * m * d * 4
+    alg = n_vec * (d * k_bits // 8 + 4 + d * v_bits // 8 + 4) + 2 * heads * m * d * 4
     gbs = alg / (ms / 1e3) / 1e9
     flops = 2.0 * 2 * heads * m * n * d  # logits and value sums, counted once
     return dict(st, **{"workload": "decode attention over the KV block: 256 heads x 32768 tokens, "
-                                   "4-bit K and V, 4 queries per head, d=128",
+                                   "%d-bit K and %d-bit V, 4 queries per head, d=128" % (k_bits, v_bits),
                        "algorithmic_bytes": alg, "GB_per_s": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS,
                        "bound": "hbm", "tokens_per_s": heads * n / (ms / 1e3),
                        "algorithmic_TFLOP_per_s": flops / (ms / 1e3) / 1e12,
@@ -528,6 +529,10 @@ def main():
     if not args.no_other_workloads:
         print("timing attention over the KV block", file=sys.stderr, flush=True)
         attn = attention_workload(torch, rht, dev, stream, ck, nk, cv, nv, n, d)
+        # the pages' KV-cache pairing: the same values coded with 3 bits
+        cv3, nv3 = rht.quantize(xv, 3, wv.rot_seed)
+        attn_k4v3 = attention_workload(torch, rht, dev, stream, ck, nk, cv3, nv3, n, d, 4, 3)
+        del cv3, nv3
     print("timing the streaming ceiling kernels", file=sys.stderr, flush=True)
     out["shape_ceiling"] = ceiling(torch, dev, stream, xk, ck, nk, yk, n)
     if not args.no_other_workloads:
@@ -536,6 +541,7 @@ def main():
         print("timing the DRIVE, residual and scoring workloads", file=sys.stderr, flush=True)
         out["other_workloads"] = other_workloads(torch, rht, dev, stream)
         out["other_workloads"]["attention"] = attn
+        out["other_workloads"]["attention_k4v3"] = attn_k4v3
     if not args.no_cpu_baseline:
         print("timing the CPU oracle on %d vectors" % args.cpu_rows, file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(xk_host, min(args.cpu_rows, n))

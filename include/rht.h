@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define RHT_ABI_VERSION 5
+#define RHT_ABI_VERSION 6
 
 typedef enum {
     RHT_OK = 0,
@@ -168,25 +168,30 @@ rht_status rht_residual_score(const float *q, int32_t m, const uint8_t *codes, c
  * weighted sum of decoded values is one inverse rotation of the weighted sum
  * of their codes).  For every head h and query i:
  *   out[h][i] = sum_j softmax_j(scale * <q[h][i], k~[h][j]>) v~[h][j]
- * where k~, v~ are the vectors rht_dequantize would decode (keys with seed_k,
- * values with seed_v).  No mask; scale is applied as given (e.g. 1/sqrt(d)).
+ * where k~, v~ are the vectors rht_dequantize would decode (keys with seed_k
+ * and k_bits, values with seed_v and v_bits).  No mask; scale is applied as
+ * given (e.g. 1/sqrt(d)).  Keys and values take their own code widths ("Random-
+ * rotation quantization", "Practical use in llama.cpp": separate K and V cache
+ * types, e.g. 4-bit keys with 3-bit values).
  *   q          [heads][m][d] fp32, 1 <= m <= 16, heads * m <= 2^24
  *              (RHT_E_COUNT otherwise).
- *   k_codes, v_codes [heads][n][bits*d/8] and k_norms, v_norms [heads][n]
- *              fp32, as written by rht_quantize(..., RHT_SCALE_NORM, seed, ...).
+ *   k_codes    [heads][n][k_bits*d/8], v_codes [heads][n][v_bits*d/8] and
+ *              k_norms, v_norms [heads][n] fp32, as written by
+ *              rht_quantize(..., RHT_SCALE_NORM or RHT_SCALE_EDEN, seed, ...).
  *   out        [heads][m][d] fp32, written.
  *   workspace  device scratch of at least rht_attention_workspace_bytes(heads,
  *              m, n, d) bytes, owned by the caller; its contents on entry are
  *              ignored and on return unspecified.  Calls that may run at the
  *              same time must not share it.
- *   d = 128 and bits = 4 only.  1 <= n <= 2^26 keys per head when heads > 0
+ *   d = 128 only; k_bits and v_bits 2, 3 or 4 (RHT_E_BITS otherwise).
+ *   1 <= n <= 2^26 keys per head when heads > 0
  *   (RHT_E_COUNT otherwise); heads = 0 is a no-op.
  * Returns RHT_E_WORKSPACE (after the other checks) when workspace_bytes is
  * too small. */
 rht_status rht_attention(const float *q, int32_t m, const uint8_t *k_codes, const float *k_norms,
                          const uint8_t *v_codes, const float *v_norms, int64_t heads, int64_t n,
-                         int32_t d, int32_t bits, uint64_t seed_k, uint64_t seed_v, float scale,
-                         float *out, void *workspace, size_t workspace_bytes, void *stream);
+                         int32_t d, int32_t k_bits, int32_t v_bits, uint64_t seed_k, uint64_t seed_v,
+                         float scale, float *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Device workspace bytes rht_attention needs for these sizes; 0 when
  * rht_attention would reject them or has nothing to do.  Host-only. */
@@ -213,8 +218,8 @@ size_t rht_attention_workspace_bytes(int64_t heads, int32_t m, int64_t n, int32_
 #define RHT_ATTENTION_NOALLOC_MAX_BYTES ((size_t)32 << 20)
 rht_status rht_attention_noalloc(const float *q, int32_t m, const uint8_t *k_codes, const float *k_norms,
                                  const uint8_t *v_codes, const float *v_norms, int64_t heads, int64_t n,
-                                 int32_t d, int32_t bits, uint64_t seed_k, uint64_t seed_v, float scale,
-                                 float *out, void *stream);
+                                 int32_t d, int32_t k_bits, int32_t v_bits, uint64_t seed_k, uint64_t seed_v,
+                                 float scale, float *out, void *stream);
 
 /* ---- host-side helpers: HOST pointers, synchronous, no GPU needed ---- */
 

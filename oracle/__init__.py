@@ -67,7 +67,7 @@ def lib():
         L.rho_score_residual.argtypes = [vp, i32, vp, vp, vp, vp, i64, i32, i32, u64, vp]
         L.rho_score_residual_dense.argtypes = [vp, i32, vp, vp, vp, vp, i64, i32, i32, u64, vp]
         for f in (L.rho_attention, L.rho_attention_rotated):
-            f.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i32, i32, u64, u64, ctypes.c_double, vp]
+            f.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i32, i32, i32, u64, u64, ctypes.c_double, vp]
         L.rho_dequantize.argtypes = [vp, vp, i64, i32, i32, u64, vp, i32]
         L.rho_sign_quantize.argtypes = [vp, i32, i64, i32, i32, u64, vp, vp, vp]
         L.rho_sign_dequantize.argtypes = [vp, vp, i64, i32, u64, vp, i32]
@@ -293,7 +293,7 @@ def score_dense(q: np.ndarray, codes: np.ndarray, norms: np.ndarray, d: int, bit
     return out
 
 
-def _attention(fn, name, q, kc, kn, vc, vn, d, bits, seed_k, seed_v, scale):
+def _attention(fn, name, q, kc, kn, vc, vn, d, k_bits, v_bits, seed_k, seed_v, scale):
     q = np.ascontiguousarray(q, dtype=np.float32)
     kc = np.ascontiguousarray(kc, dtype=np.uint8)
     vc = np.ascontiguousarray(vc, dtype=np.uint8)
@@ -302,26 +302,27 @@ def _attention(fn, name, q, kc, kn, vc, vn, d, bits, seed_k, seed_v, scale):
     heads, m = q.shape[0], q.shape[1]
     n = kn.shape[1]
     assert q.shape == (heads, m, d) and kn.shape == (heads, n) and vn.shape == (heads, n)
-    assert kc.shape == (heads, n, bits * d // 8) and vc.shape == kc.shape
+    assert kc.shape == (heads, n, k_bits * d // 8) and vc.shape == (heads, n, v_bits * d // 8)
     out = np.zeros((heads, m, d), np.float64)
-    _check(fn(_p(q), m, _p(kc), _p(kn), _p(vc), _p(vn), heads, n, d, bits, seed_k, seed_v,
+    _check(fn(_p(q), m, _p(kc), _p(kn), _p(vc), _p(vn), heads, n, d, k_bits, v_bits, seed_k, seed_v,
               float(scale), _p(out)), name)
     return out
 
 
-def attention(q, kc, kn, vc, vn, d, bits, seed_k, seed_v, scale):
+def attention(q, kc, kn, vc, vn, d, k_bits, v_bits, seed_k, seed_v, scale):
     """Attention over coded keys and values, plain definition (fp64):
-    softmax(scale * q . dequant(K)^T) . dequant(V) per head.
+    softmax(scale * q . dequant(K)^T) . dequant(V) per head, keys decoded with
+    the k_bits codebook, values with the v_bits one.
     q [heads][m][d], codes [heads][n][bits*d/8], norms [heads][n]."""
-    return _attention(lib().rho_attention, "attention", q, kc, kn, vc, vn, d, bits, seed_k, seed_v,
-                      scale)
+    return _attention(lib().rho_attention, "attention", q, kc, kn, vc, vn, d, k_bits, v_bits, seed_k,
+                      seed_v, scale)
 
 
-def attention_rotated(q, kc, kn, vc, vn, d, bits, seed_k, seed_v, scale):
+def attention_rotated(q, kc, kn, vc, vn, d, k_bits, v_bits, seed_k, seed_v, scale):
     """The same attention in the rotated domains: logits on the codes, value
     sum kept rotated, one inverse transform per query (fp64)."""
-    return _attention(lib().rho_attention_rotated, "attention_rotated", q, kc, kn, vc, vn, d, bits,
-                      seed_k, seed_v, scale)
+    return _attention(lib().rho_attention_rotated, "attention_rotated", q, kc, kn, vc, vn, d, k_bits,
+                      v_bits, seed_k, seed_v, scale)
 
 
 def score_sign(q, bits, scale, d: int, seed: int, dense: bool = False):

@@ -759,8 +759,12 @@ int rho_score_dense(const float *q, int m, const uint8_t *codes, const float *no
  * [RRQ decoders] (MSE decoder for the KV cache).  The plain definition:
  * decode every key and value in fp64 (x~ = D H c ||x|| / d, no rounding),
  * logits s_j = scale <q, k~_j>, p = softmax(s), out = sum_j p_j v~_j.
- * q [heads][m][d] fp32, codes [heads][n][bits d / 8], norms [heads][n],
- * out [heads][m][d] fp64.  n >= 1.                                          */
+ * Keys and values may use different code widths (page "Random-rotation
+ * quantization", "Practical use in llama.cpp": the K and V caches take their
+ * own code types, e.g. 4-bit keys with 3-bit values); each is decoded with the
+ * Lloyd-Max codebook of its own width.
+ * q [heads][m][d] fp32, codes [heads][n][kbits d / 8] and [heads][n][vbits d / 8],
+ * norms [heads][n], out [heads][m][d] fp64.  n >= 1.                        */
 static void decode_row_f64(const uint8_t *crow, double norm, int d, int bits, const double *lv,
                            const int8_t *s, double *out)
 {
@@ -771,18 +775,21 @@ static void decode_row_f64(const uint8_t *crow, double norm, int d, int bits, co
 }
 
 int rho_attention(const float *q, int m, const uint8_t *kc, const float *kn, const uint8_t *vc,
-                  const float *vn, int64_t heads, int64_t n, int d, int bits, uint64_t seed_k,
+                  const float *vn, int64_t heads, int64_t n, int d, int kbits, int vbits, uint64_t seed_k,
                   uint64_t seed_v, double scale, double *out)
 {
-    double lv[16], th[15];
+    double lk[16], lvv[16], th[15];
     int8_t *sk, *sv;
     double *kd, *vd, *logit;
     int64_t b, j;
-    int i, t, row_bytes;
-    if (!valid_dim(d) || bits < 1 || bits > 4 || n < 1 || m < 0 || heads < 0) return -1;
-    if ((int64_t)bits * d % 8) return -1;
-    row_bytes = bits * d / 8;
-    rho_lloyd_max(bits, lv, th, NULL, NULL);
+    int i, t, krow, vrow;
+    if (!valid_dim(d) || kbits < 1 || kbits > 4 || vbits < 1 || vbits > 4 || n < 1 || m < 0 || heads < 0)
+        return -1;
+    if ((int64_t)kbits * d % 8 || (int64_t)vbits * d % 8) return -1;
+    krow = kbits * d / 8;
+    vrow = vbits * d / 8;
+    rho_lloyd_max(kbits, lk, th, NULL, NULL);
+    rho_lloyd_max(vbits, lvv, th, NULL, NULL);
     sk = (int8_t *)malloc((size_t)d);
     sv = (int8_t *)malloc((size_t)d);
     kd = (double *)malloc(sizeof(double) * (size_t)(n * d));
@@ -792,8 +799,8 @@ int rho_attention(const float *q, int m, const uint8_t *kc, const float *kn, con
     rho_signs(seed_v, d, sv);
     for (b = 0; b < heads; ++b) {
         for (j = 0; j < n; ++j) {
-            decode_row_f64(kc + (b * n + j) * row_bytes, kn[b * n + j], d, bits, lv, sk, kd + j * d);
-            decode_row_f64(vc + (b * n + j) * row_bytes, vn[b * n + j], d, bits, lv, sv, vd + j * d);
+            decode_row_f64(kc + (b * n + j) * krow, kn[b * n + j], d, kbits, lk, sk, kd + j * d);
+            decode_row_f64(vc + (b * n + j) * vrow, vn[b * n + j], d, vbits, lvv, sv, vd + j * d);
         }
         for (i = 0; i < m; ++i) {
             const float *qi = q + (b * m + i) * d;
@@ -829,17 +836,20 @@ int rho_attention(const float *q, int m, const uint8_t *kc, const float *kn, con
  * out = D_v H z (Pi_v^T is linear, so it moves out of the sum).             */
 int rho_attention_rotated(const float *q, int m, const uint8_t *kc, const float *kn,
                           const uint8_t *vc, const float *vn, int64_t heads, int64_t n, int d,
-                          int bits, uint64_t seed_k, uint64_t seed_v, double scale, double *out)
+                          int kbits, int vbits, uint64_t seed_k, uint64_t seed_v, double scale, double *out)
 {
-    double lv[16], th[15];
+    double lk[16], lvv[16], th[15];
     int8_t *sk, *sv;
     double *qt, *logit;
     int64_t b, j;
-    int i, t, row_bytes;
-    if (!valid_dim(d) || bits < 1 || bits > 4 || n < 1 || m < 0 || heads < 0) return -1;
-    if ((int64_t)bits * d % 8) return -1;
-    row_bytes = bits * d / 8;
-    rho_lloyd_max(bits, lv, th, NULL, NULL);
+    int i, t, krow, vrow;
+    if (!valid_dim(d) || kbits < 1 || kbits > 4 || vbits < 1 || vbits > 4 || n < 1 || m < 0 || heads < 0)
+        return -1;
+    if ((int64_t)kbits * d % 8 || (int64_t)vbits * d % 8) return -1;
+    krow = kbits * d / 8;
+    vrow = vbits * d / 8;
+    rho_lloyd_max(kbits, lk, th, NULL, NULL);
+    rho_lloyd_max(vbits, lvv, th, NULL, NULL);
     sk = (int8_t *)malloc((size_t)d);
     sv = (int8_t *)malloc((size_t)d);
     qt = (double *)malloc(sizeof(double) * (size_t)d);
@@ -854,19 +864,19 @@ int rho_attention_rotated(const float *q, int m, const uint8_t *kc, const float 
             for (t = 0; t < d; ++t) qt[t] = sk[t] * (double)qi[t];
             rho_fwht(qt, d);
             for (j = 0; j < n; ++j) {
-                const uint8_t *crow = kc + (b * n + j) * row_bytes;
+                const uint8_t *crow = kc + (b * n + j) * krow;
                 double acc = 0.0;
-                for (t = 0; t < d; ++t) acc += qt[t] * lv[get_field(crow, t, bits)];
+                for (t = 0; t < d; ++t) acc += qt[t] * lk[get_field(crow, t, kbits)];
                 logit[j] = scale * ((double)kn[b * n + j] / d) * acc;
                 if (logit[j] > mx) mx = logit[j];
             }
             for (t = 0; t < d; ++t) z[t] = 0.0;
             for (j = 0; j < n; ++j) {
-                const uint8_t *crow = vc + (b * n + j) * row_bytes;
+                const uint8_t *crow = vc + (b * n + j) * vrow;
                 double p = exp(logit[j] - mx), w;
                 sum += p;
                 w = p * ((double)vn[b * n + j] / d);
-                for (t = 0; t < d; ++t) z[t] += w * lv[get_field(crow, t, bits)];
+                for (t = 0; t < d; ++t) z[t] += w * lvv[get_field(crow, t, vbits)];
             }
             for (t = 0; t < d; ++t) z[t] /= sum;
             rho_fwht(z, d);

@@ -37,7 +37,7 @@ _LIB_PATH = os.path.join(_HERE, "librht.so")
 
 F32, F16 = 0, 1
 SCALE_NORM, SCALE_SIGN_BIASED, SCALE_SIGN_UNBIASED, SCALE_EDEN, SCALE_NORM_BETA = 0, 1, 2, 3, 4
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _lib = None
 
@@ -69,10 +69,10 @@ def load():
     L.rht_score.argtypes = [vp, i32, vp, vp, i64, i32, i32, u64, vp, vp]
     L.rht_score_sign.argtypes = [vp, i32, vp, vp, i64, i32, u64, vp, vp]
     L.rht_residual_score.argtypes = [vp, i32, vp, vp, vp, vp, i64, i32, i32, u64, vp, vp]
-    L.rht_attention.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i32, i32, u64, u64, ctypes.c_float,
+    L.rht_attention.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i32, i32, i32, u64, u64, ctypes.c_float,
                                 vp, vp, ctypes.c_size_t, vp]
-    L.rht_attention_noalloc.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i32, i32, u64, u64, ctypes.c_float,
-                                        vp, vp]
+    L.rht_attention_noalloc.argtypes = [vp, i32, vp, vp, vp, vp, i64, i64, i32, i32, i32, u64, u64,
+                                        ctypes.c_float, vp, vp]
     L.rht_attention_workspace_bytes.argtypes = [i64, i32, i64, i32]
     L.rht_attention_workspace_bytes.restype = ctypes.c_size_t
     L.rht_codebook.argtypes = [i32, vp, vp]
@@ -130,16 +130,16 @@ def rht_residual_score(q, m, codes, signs, norms, res_scale, n, d, bits, seed, l
         "rht_residual_score")
 
 
-def rht_attention(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, bits, seed_k, seed_v, scale,
-                  out, workspace, workspace_bytes, stream=0):
-    _ok(load().rht_attention(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, bits, seed_k, seed_v,
-                             scale, out, workspace, workspace_bytes, stream), "rht_attention")
+def rht_attention(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, k_bits, v_bits, seed_k, seed_v,
+                  scale, out, workspace, workspace_bytes, stream=0):
+    _ok(load().rht_attention(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, k_bits, v_bits, seed_k,
+                             seed_v, scale, out, workspace, workspace_bytes, stream), "rht_attention")
 
 
-def rht_attention_noalloc(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, bits, seed_k, seed_v, scale,
-                          out, stream=0):
-    _ok(load().rht_attention_noalloc(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, bits, seed_k,
-                                     seed_v, scale, out, stream), "rht_attention_noalloc")
+def rht_attention_noalloc(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, k_bits, v_bits, seed_k,
+                          seed_v, scale, out, stream=0):
+    _ok(load().rht_attention_noalloc(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, k_bits, v_bits,
+                                     seed_k, seed_v, scale, out, stream), "rht_attention_noalloc")
 
 
 def rht_attention_workspace_bytes(heads, m, n, d) -> int:
@@ -294,19 +294,23 @@ def residual_score(q, codes, signs, norms, res_scale, d: int, bits: int, seed: i
     return logits
 
 
-def attention(q, k_codes, k_norms, v_codes, v_norms, bits: int, seed_k: int, seed_v: int, scale: float,
-              workspace=None):
-    """q [heads][m][d] fp32 over coded keys/values [heads][n][...] -> out fp32 [heads][m][d].
-    A workspace tensor of at least rht_attention_workspace_bytes bytes may be passed in."""
+def attention(q, k_codes, k_norms, v_codes, v_norms, k_bits: int, v_bits: int, seed_k: int, seed_v: int,
+              scale: float, workspace=None):
+    """q [heads][m][d] fp32 over coded keys [heads][n][k_bits*d/8] and values
+    [heads][n][v_bits*d/8] -> out fp32 [heads][m][d].  A workspace tensor of at
+    least rht_attention_workspace_bytes bytes may be passed in."""
     torch = _torch()
     _check_gpu(q, k_codes, k_norms, v_codes, v_norms)
     heads, m, d = q.shape
     n = k_norms.shape[1]
+    if (tuple(k_codes.shape) != (heads, n, k_bits * d // 8) or tuple(v_codes.shape) != (heads, n, v_bits * d // 8)
+            or tuple(k_norms.shape) != (heads, n) or tuple(v_norms.shape) != (heads, n)):
+        raise ValueError("attention: code and norm shapes do not match q [heads][m][d], k_bits and v_bits")
     out = torch.empty((heads, m, d), dtype=torch.float32, device=q.device)
     need = rht_attention_workspace_bytes(heads, m, n, d)
     if workspace is None:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
     rht_attention(q.data_ptr(), m, k_codes.data_ptr(), k_norms.data_ptr(), v_codes.data_ptr(),
-                  v_norms.data_ptr(), heads, n, d, bits, seed_k, seed_v, scale, out.data_ptr(),
+                  v_norms.data_ptr(), heads, n, d, k_bits, v_bits, seed_k, seed_v, scale, out.data_ptr(),
                   workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q.device))
     return out

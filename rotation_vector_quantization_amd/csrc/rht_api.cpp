@@ -515,10 +515,10 @@ namespace {
 // the workspace: the checks and their order documented for rht_attention.
 rht_status attention_check(const float *q, int32_t m, const uint8_t *k_codes, const float *k_norms,
                            const uint8_t *v_codes, const float *v_norms, int64_t heads, int64_t n, int32_t d,
-                           int32_t bits, const float *out) {
+                           int32_t k_bits, int32_t v_bits, const float *out) {
     if (!attention_args_ok(heads, m, n)) return RHT_E_COUNT;
     if (d != 128) return RHT_E_DIM;
-    if (bits != 4) return RHT_E_BITS;
+    if (k_bits < 2 || k_bits > 4 || v_bits < 2 || v_bits > 4) return RHT_E_BITS;
     if (heads == 0) return RHT_OK;
     if (!q || !k_codes || !k_norms || !v_codes || !v_norms || !out) return RHT_E_NULL;
     if (!aligned(q) || !aligned(k_codes) || !aligned(k_norms) || !aligned(v_codes) || !aligned(v_norms) ||
@@ -529,8 +529,8 @@ rht_status attention_check(const float *q, int32_t m, const uint8_t *k_codes, co
 
 rht_status attention_launch(const float *q, int32_t m, const uint8_t *k_codes, const float *k_norms,
                             const uint8_t *v_codes, const float *v_norms, int64_t heads, int64_t n, int32_t d,
-                            int32_t bits, uint64_t seed_k, uint64_t seed_v, float scale, float *out, float *ws,
-                            void *stream) {
+                            int32_t k_bits, int32_t v_bits, uint64_t seed_k, uint64_t seed_v, float scale,
+                            float *out, float *ws, void *stream) {
     AttnArgs a;
     std::memset(&a, 0, sizeof(a));
     a.q = q;
@@ -545,7 +545,10 @@ rht_status attention_launch(const float *q, int32_t m, const uint8_t *k_codes, c
     a.m = m;
     a.chunks = (int)attention_chunks(heads, n);
     a.scale = scale;
-    std::memcpy(a.lev, book(bits).lev, sizeof(a.lev));
+    a.kbits = k_bits;
+    a.vbits = v_bits;
+    std::memcpy(a.lev_k, book(k_bits).lev, sizeof(a.lev_k));
+    std::memcpy(a.lev_v, book(v_bits).lev, sizeof(a.lev_v));
     sign_words(seed_k, d, a.dsign_k);
     sign_words(seed_v, d, a.dsign_v);
     return launched(launch_attention(a, (hipStream_t)stream));
@@ -555,28 +558,30 @@ rht_status attention_launch(const float *q, int32_t m, const uint8_t *k_codes, c
 
 rht_status rht_attention(const float *q, int32_t m, const uint8_t *k_codes, const float *k_norms,
                          const uint8_t *v_codes, const float *v_norms, int64_t heads, int64_t n,
-                         int32_t d, int32_t bits, uint64_t seed_k, uint64_t seed_v, float scale,
+                         int32_t d, int32_t k_bits, int32_t v_bits, uint64_t seed_k, uint64_t seed_v, float scale,
                          float *out, void *workspace, size_t workspace_bytes, void *stream) {
-    const rht_status st = attention_check(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, bits, out);
+    const rht_status st =
+        attention_check(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, k_bits, v_bits, out);
     if (st != RHT_OK || heads == 0) return st;
     if (!workspace) return RHT_E_NULL;
     if (!aligned(workspace)) return RHT_E_ALIGN;
     if (workspace_bytes < rht_attention_workspace_bytes(heads, m, n, d)) return RHT_E_WORKSPACE;
-    return attention_launch(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, bits, seed_k, seed_v, scale,
-                            out, static_cast<float *>(workspace), stream);
+    return attention_launch(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, k_bits, v_bits, seed_k, seed_v,
+                            scale, out, static_cast<float *>(workspace), stream);
 }
 
 rht_status rht_attention_noalloc(const float *q, int32_t m, const uint8_t *k_codes, const float *k_norms,
                                  const uint8_t *v_codes, const float *v_norms, int64_t heads, int64_t n,
-                                 int32_t d, int32_t bits, uint64_t seed_k, uint64_t seed_v, float scale,
-                                 float *out, void *stream) {
-    const rht_status st = attention_check(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, bits, out);
+                                 int32_t d, int32_t k_bits, int32_t v_bits, uint64_t seed_k, uint64_t seed_v,
+                                 float scale, float *out, void *stream) {
+    const rht_status st =
+        attention_check(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, k_bits, v_bits, out);
     if (st != RHT_OK || heads == 0) return st;
     if (rht_attention_workspace_bytes(heads, m, n, d) > kAttnScratchBytes) return RHT_E_WORKSPACE;
     void *ws = nullptr;
     if (attention_scratch(&ws) != hipSuccess) return RHT_E_DEVICE;
-    return attention_launch(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, bits, seed_k, seed_v, scale,
-                            out, static_cast<float *>(ws), stream);
+    return attention_launch(q, m, k_codes, k_norms, v_codes, v_norms, heads, n, d, k_bits, v_bits, seed_k, seed_v,
+                            scale, out, static_cast<float *>(ws), stream);
 }
 
 }  // extern "C"

@@ -1,5 +1,6 @@
 // rht_attn.hip -- attention of a few queries over MSE-coded keys and values
-// (d = 128, 4-bit codes), computed in the rotated domains.
+// (d = 128; keys and values each with 2-, 3- or 4-bit codes), computed in the
+// rotated domains.
 //
 // Method: page "Attn-rot: TurboQuant lite in llama.cpp" (opening section: the
 // keys and values of the KV cache are rotated and quantized and attention
@@ -32,6 +33,15 @@
 // as stored instead of transposed.
 // Lane layout of the 16x16x32 instruction (lane l, g = l / 16): A holds
 // A[l % 16][8 g + t], B holds B[8 g + t][l % 16], C holds C[4 g + r][l % 16].
+//
+// Code widths (page "Random-rotation quantization", "Practical use in
+// llama.cpp": the K and V caches take their own code types, e.g. 4-bit keys
+// with 3-bit values).  Codes narrower than 4 bits are widened to one code per
+// nibble as they arrive (key pieces in registers, value rows on their way
+// into LDS), so everything after that sees the 4-bit layout: a byte holds two
+// neighbouring codes.  The level tables are indexed by such a byte and built
+// from each operand's own codebook; keys and values share one table when
+// their widths agree.
 #include "rht_device.h"
 
 #include <atomic>
@@ -51,7 +61,6 @@ std::atomic<void *> g_scratch[kMaxDevices];
 std::mutex g_scratch_mu;
 
 constexpr int kAD = 128;           // coordinates per vector
-constexpr int kACodeBytes = 64;    // 4-bit codes per row
 constexpr int kVRow = 80;          // LDS row stride of a staged value tile (bank spread)
 // Blocks of RHT_ATTN_WAVES wavefronts share one copy of the level tables; one
 // block fills a CU up to the register limit (3 waves per SIMD).
@@ -128,33 +137,99 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// Global loads of one 32-key tile for a lane: K code bytes 16g..16g+15 of keys
-// key0 + l%16 and key0 + 16 + l%16; the lane's two 16-byte pieces of the value
-// tile (chunks l and 64 + l of the 32 x 64-byte tile); one norm (lanes 0-31:
-// key norm of key0 + l, lanes 32-63: value norm of key0 + l - 32).  Offsets are
-// 32-bit from per-head bases; FULL tiles need no clamping, the last partial
-// tile repeats key n-1 (its logits are masked).
+// Global loads of one 32-key tile for a lane (KB, VB: key and value code
+// widths; a row of b-bit codes is 16 b bytes).  Keys: the piece of keys
+// key0 + l%16 and key0 + 16 + l%16 holding coordinates 32g .. 32g + 31 (4 KB
+// bytes each).  Values, 4-bit: the lane's two 16-byte pieces of the 32 x
+// 64-byte value tile (chunks l and 64 + l); narrower: half l%2 of the row of
+// key key0 + l/2 (8 VB bytes).  One norm (lanes 0-31: key norm of key0 + l,
+// lanes 32-63: value norm of key0 + l - 32).  Offsets are 32-bit from
+// per-head bases; FULL tiles need no clamping, the last partial tile repeats
+// key n-1 (its logits are masked).
+template <int KB, int VB>
 struct TileRegs {
-    u32x4_t k0, k1, v0, v1;
+    uint32_t k0[KB], k1[KB];
+    uint32_t v[VB == 4 ? 8 : 2 * VB];
     float nrm;
 };
 
-template <bool FULL>
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// W words from p, p aligned to ALIGN bytes, in the widest accesses that allows
+// (non-temporal: the code rows are read once per launch, measured 0.329 ->
+// 0.323 ms with 4-bit codes).
+template <int W, int ALIGN>
+__device__ __forceinline__ void load_piece(const uint8_t *p, uint32_t (&w)[W]) {
+    if constexpr (ALIGN >= 16 && W % 4 == 0) {
+#pragma unroll
+        for (int k = 0; k < W / 4; ++k) {
+            const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p) + k);
+            w[4 * k] = t[0]; w[4 * k + 1] = t[1]; w[4 * k + 2] = t[2]; w[4 * k + 3] = t[3];
+        }
+    } else if constexpr (ALIGN >= 8 && W % 2 == 0) {
+#pragma unroll
+        for (int k = 0; k < W / 2; ++k) {
+            const u32x2_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p) + k);
+            w[2 * k] = t[0]; w[2 * k + 1] = t[1];
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < W; ++k) w[k] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p) + k);
+    }
+}
+
+template <bool FULL, int KB, int VB>
 __device__ __forceinline__ void load_tile(const uint8_t *kc, const uint8_t *vc, const float *kn, const float *vn,
-                                          int64_t n, int64_t key0, uint32_t lane, TileRegs &t) {
+                                          int64_t n, int64_t key0, uint32_t lane, TileRegs<KB, VB> &t) {
+    constexpr uint32_t KR = 16 * KB, VR = 16 * VB;  // code bytes per key and per value row
     const uint32_t j = lane & 15u, g = lane >> 4;
-    uint32_t r0 = (uint32_t)key0 + j, r1 = r0 + 16, r2 = (uint32_t)key0 + lane / 4, r3 = r2 + 16;
+    uint32_t r0 = (uint32_t)key0 + j, r1 = r0 + 16;
+    uint32_t r2 = (uint32_t)key0 + (VB == 4 ? lane / 4 : lane / 2), r3 = r2 + 16;
     uint32_t rn = (uint32_t)key0 + (lane & 31u);
     if (!FULL) {
         const uint32_t last = (uint32_t)(n - 1);
         r0 = min(r0, last); r1 = min(r1, last); r2 = min(r2, last); r3 = min(r3, last); rn = min(rn, last);
     }
-    // the code rows are read once per launch: non-temporal loads (measured 0.329 -> 0.323 ms)
-    t.k0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(kc + r0 * kACodeBytes + 16 * g));
-    t.k1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(kc + r1 * kACodeBytes + 16 * g));
-    t.v0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(vc + r2 * kACodeBytes + 16 * (lane % 4)));
-    t.v1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(vc + r3 * kACodeBytes + 16 * (lane % 4)));
+    constexpr int KALIGN = KB == 4 ? 16 : KB == 2 ? 8 : 4;  // of 16 KB r + 4 KB g
+    load_piece<KB, KALIGN>(kc + r0 * KR + 4 * KB * g, t.k0);
+    load_piece<KB, KALIGN>(kc + r1 * KR + 4 * KB * g, t.k1);
+    if constexpr (VB == 4) {
+        uint32_t a[4], b[4];
+        load_piece<4, 16>(vc + r2 * VR + 16 * (lane % 4), a);
+        load_piece<4, 16>(vc + r3 * VR + 16 * (lane % 4), b);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            t.v[k] = a[k];
+            t.v[4 + k] = b[k];
+        }
+    } else {
+        load_piece<2 * VB, VB == 2 ? 16 : 8>(vc + r2 * VR + 8 * VB * (lane % 2), t.v);
+    }
     t.nrm = (lane < 32 ? kn : vn)[rn];
+}
+
+// 32 codes of B bits (an LSB-first bitstream in w[OFF .. OFF + B - 1]) as one
+// code per nibble: code i at bits [4 i, 4 i + 4) of the result.
+template <int B, int OFF, int N>
+__device__ __forceinline__ u32x4_t widen_codes(const uint32_t (&w)[N]) {
+    if constexpr (B == 4) {
+        return u32x4_t{w[OFF], w[OFF + 1], w[OFF + 2], w[OFF + 3]};
+    } else {
+        uint32_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t acc = 0;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int p = B * (8 * k + t), wi = OFF + p / 32, sh = p % 32;
+                uint32_t c = w[wi] >> sh;
+                if (sh + B > 32) c |= w[wi + 1] << (32 - sh);
+                acc |= (c & ((1u << B) - 1u)) << (4 * t);
+            }
+            o[k] = acc;
+        }
+        return u32x4_t{o[0], o[1], o[2], o[3]};
+    }
 }
 
 // Per code byte, the fp16 hi and lo parts of its two levels, low nibble in
@@ -171,18 +246,18 @@ __device__ __forceinline__ void load_tile(const uint8_t *kc, const uint8_t *vc, 
 constexpr int kTabCopies = 32;
 constexpr uint32_t kTabRow = 256;  // bytes per entry
 
-struct LevelTables {
-    uint32_t w[256 * kTabRow / 4];
-};
+// Rows a table needs for b-bit codes widened to nibbles: bytes up to
+// (2^b - 1) * 0x11.
+__host__ __device__ constexpr int tab_rows(int b) { return ((1 << b) - 1) * 17 + 1; }
 
 // The A operands for four code bytes: hi parts and lo parts, byte i in word i.
 // copy4 = 4 * (lane % kTabCopies).  The reads go through volatile pointers so
 // the compiler keeps them as single ds_read_b32 into the operand registers
 // instead of pairing them into two-register reads that then need moves.
-__device__ __forceinline__ void level_operands(const LevelTables &tb, uint32_t copy4, uint32_t w, u32x4_t &ah,
+__device__ __forceinline__ void level_operands(const uint32_t *tb, uint32_t copy4, uint32_t w, u32x4_t &ah,
                                                u32x4_t &al) {
     typedef __attribute__((address_space(3))) const volatile uint32_t lds_word;
-    const char __attribute__((address_space(3))) *base = (const char __attribute__((address_space(3))) *)tb.w;
+    const char __attribute__((address_space(3))) *base = (const char __attribute__((address_space(3))) *)tb;
     // result bytes: [0] = copy4, [1] = code byte k, [2], [3] = 0
     const uint32_t o0 = __builtin_amdgcn_perm(w, copy4, 0x0C0C0400u);
     const uint32_t o1 = __builtin_amdgcn_perm(w, copy4, 0x0C0C0500u);
@@ -218,10 +293,9 @@ template <> struct QueryOps<16> { typedef QueryTriple type; };
 
 // {hi, lo} words of code byte k of w, from the pair-layout table (entry b,
 // copy r at byte b * 256 + 8 r); copy8 = 8 * (lane % 32).
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint2 level_pair(const LevelTables &tb, uint32_t copy8, uint32_t w, uint32_t sel) {
+__device__ __forceinline__ uint2 level_pair(const uint32_t *tb, uint32_t copy8, uint32_t w, uint32_t sel) {
     typedef __attribute__((address_space(3))) const volatile u32x2_t lds_pair;
-    const char __attribute__((address_space(3))) *base = (const char __attribute__((address_space(3))) *)tb.w;
+    const char __attribute__((address_space(3))) *base = (const char __attribute__((address_space(3))) *)tb;
     const u32x2_t v = *(const lds_pair *)(base + __builtin_amdgcn_perm(w, copy8, sel));
     return make_uint2(v.x, v.y);
 }
@@ -234,7 +308,7 @@ __device__ __forceinline__ float row_ror8(float v) {
 
 // Logits of 16 keys against the queries, pair layout (QG = 4): K step (ks, h)
 // covers code bytes 2h, 2h + 1 of word ks, slots {hi, lo} of each.
-__device__ __forceinline__ floatx4 key_logits_pairs(const LevelTables &tb, uint32_t copy8, u32x4_t kc,
+__device__ __forceinline__ floatx4 key_logits_pairs(const uint32_t *tb, uint32_t copy8, u32x4_t kc,
                                                     const QueryPairs &qo) {
     floatx4 c[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
@@ -253,7 +327,7 @@ __device__ __forceinline__ floatx4 key_logits_pairs(const LevelTables &tb, uint3
 
 // Logits of 16 keys (one 16-byte code piece per lane) against the queries,
 // layout QG = 16 (split table, three products per K step).
-__device__ __forceinline__ floatx4 key_logits_triple(const LevelTables &tb, uint32_t copy4, u32x4_t kc,
+__device__ __forceinline__ floatx4 key_logits_triple(const uint32_t *tb, uint32_t copy4, u32x4_t kc,
                                                      const QueryTriple &qo) {
     // two independent accumulation chains (even and odd K steps)
     floatx4 c[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
@@ -306,12 +380,22 @@ struct SoftmaxState {
     floatx4 z[kZ];       // rotated value sums in the accumulator layout above
 };
 
-// Copy a tile's value codes (key r at vb + r * kVRow) and norms into LDS.
-// Done before the next tile's loads are issued: waiting for this tile's
-// registers then does not wait for the prefetch behind them.
-__device__ __forceinline__ void stage_tile(uint8_t *vb, float *nb, const TileRegs &t, uint32_t lane) {
-    *reinterpret_cast<u32x4_t *>(vb + (lane / 4) * kVRow + 16 * (lane % 4)) = t.v0;
-    *reinterpret_cast<u32x4_t *>(vb + (16 + lane / 4) * kVRow + 16 * (lane % 4)) = t.v1;
+// Copy a tile's value codes (key r at vb + r * kVRow, one code per nibble) and
+// norms into LDS.  Done before the next tile's loads are issued: waiting for
+// this tile's registers then does not wait for the prefetch behind them.
+template <int KB, int VB>
+__device__ __forceinline__ void stage_tile(uint8_t *vb, float *nb, const TileRegs<KB, VB> &t, uint32_t lane) {
+    if constexpr (VB == 4) {
+        *reinterpret_cast<u32x4_t *>(vb + (lane / 4) * kVRow + 16 * (lane % 4)) =
+            u32x4_t{t.v[0], t.v[1], t.v[2], t.v[3]};
+        *reinterpret_cast<u32x4_t *>(vb + (16 + lane / 4) * kVRow + 16 * (lane % 4)) =
+            u32x4_t{t.v[4], t.v[5], t.v[6], t.v[7]};
+    } else {
+        // half lane % 2 of key lane / 2: 64 codes, 32 bytes once widened
+        uint8_t *row = vb + (lane / 2) * kVRow + 32 * (lane % 2);
+        *reinterpret_cast<u32x4_t *>(row) = widen_codes<VB, 0>(t.v);
+        *reinterpret_cast<u32x4_t *>(row + 16) = widen_codes<VB, VB>(t.v);
+    }
     nb[lane] = t.nrm;
 }
 
@@ -321,7 +405,7 @@ __device__ __forceinline__ void stage_tile(uint8_t *vb, float *nb, const TileReg
 // the {hi, lo} pair of byte T of the key's code dword j, i.e. coordinates
 // 8j + 2T and 8j + 2T + 1.  B: the lane's fp16 part of that key's P in the
 // half of the word its parity names, the same word for the hi and lo slots.
-__device__ __forceinline__ void value_sums_by_parity(const LevelTables &tb, uint32_t copy8, const uint32_t (&a)[8],
+__device__ __forceinline__ void value_sums_by_parity(const uint32_t *tb, uint32_t copy8, const uint32_t (&a)[8],
                                                      const float (&P)[8], uint2 psel, floatx4 (&z)[4]) {
     const uint2 q0 = split2(P[0], P[1]), q1 = split2(P[2], P[3]);
     const uint2 q2 = split2(P[4], P[5]), q3 = split2(P[6], P[7]);
@@ -352,7 +436,7 @@ __device__ __forceinline__ void value_sums_by_parity(const LevelTables &tb, uint
 // 8j + n of keys 2w, 2w+1: one table entry each (SPLIT_N: a {hi, lo} pair, two
 // bytes per K step, each weight word twice).
 template <bool SPLIT_N>
-__device__ __forceinline__ void value_sums_transposed(const LevelTables &tb, uint32_t copy4, uint32_t (&a)[8],
+__device__ __forceinline__ void value_sums_transposed(const uint32_t *tb, uint32_t copy4, uint32_t (&a)[8],
                                                       const float (&P)[8], uint32_t j, floatx4 (&z)[8]) {
     const uint2 s0 = split2(P[0], P[1]), s1 = split2(P[2], P[3]);
     const uint2 s2 = split2(P[4], P[5]), s3 = split2(P[6], P[7]);
@@ -395,8 +479,9 @@ __device__ __forceinline__ void value_sums_transposed(const LevelTables &tb, uin
 // psel (QG = 4): per-lane byte selectors that place the lane's fp16 part of an
 // even or odd weight of a pair in the half of the B word its parity names.
 template <bool FULL, int QG>
-__device__ __forceinline__ void attend_tile(const LevelTables &tb, const uint8_t *vb, const float *nb,
-                                            u32x4_t k0, u32x4_t k1, const typename QueryOps<QG>::type &qo,
+__device__ __forceinline__ void attend_tile(const uint32_t *tbk, const uint32_t *tbv, const uint8_t *vb,
+                                            const float *nb, u32x4_t k0, u32x4_t k1,
+                                            const typename QueryOps<QG>::type &qo,
                                             uint2 psel, float fq, int64_t key0, int64_t n, uint32_t lane,
                                             SoftmaxState<QG> &st) {
     constexpr bool SPLIT_N = QG <= 8;
@@ -406,11 +491,11 @@ __device__ __forceinline__ void attend_tile(const LevelTables &tb, const uint8_t
     const uint32_t copy4 = 4 * (lane % kTabCopies);
     floatx4 c0, c1;
     if constexpr (SPLIT_N) {
-        c0 = key_logits_pairs(tb, 2 * copy4, k0, qo);
-        c1 = key_logits_pairs(tb, 2 * copy4, k1, qo);
+        c0 = key_logits_pairs(tbk, 2 * copy4, k0, qo);
+        c1 = key_logits_pairs(tbk, 2 * copy4, k1, qo);
     } else {
-        c0 = key_logits_triple(tb, copy4, k0, qo);
-        c1 = key_logits_triple(tb, copy4, k1, qo);
+        c0 = key_logits_triple(tbk, copy4, k0, qo);
+        c1 = key_logits_triple(tbk, copy4, k1, qo);
     }
     const float4 kn0 = *reinterpret_cast<const float4 *>(nb + 4 * g);
     const float4 kn1 = *reinterpret_cast<const float4 *>(nb + 16 + 4 * g);
@@ -470,23 +555,29 @@ __device__ __forceinline__ void attend_tile(const LevelTables &tb, const uint8_t
         a[tt] = *reinterpret_cast<const uint32_t *>(vb + key * kVRow + 4 * j);
     }
     if constexpr (QG == 4)
-        value_sums_by_parity(tb, 2 * copy4, a, P, psel, st.z);
+        value_sums_by_parity(tbv, 2 * copy4, a, P, psel, st.z);
     else
-        value_sums_transposed<SPLIT_N>(tb, copy4, a, P, j, st.z);
+        value_sums_transposed<SPLIT_N>(tbv, copy4, a, P, j, st.z);
 }
 
-template <int QG>
+template <int QG, int KB, int VB>
 __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
     constexpr bool SPLIT_N = QG <= 8;
-    __shared__ LevelTables tb;
+    constexpr bool SHARED = KB == VB;  // one codebook, one table
+    constexpr uint32_t WK = tab_rows(KB) * kTabRow / 4, WV = tab_rows(VB) * kTabRow / 4;  // table words
+    __shared__ __attribute__((aligned(16))) uint32_t tabs[WK + (SHARED ? 0 : WV)];
     __shared__ __attribute__((aligned(16))) uint8_t vbuf[kAWaves][32 * kVRow];
     __shared__ __attribute__((aligned(16))) float nbuf[kAWaves][64];
-    for (uint32_t k = threadIdx.x; k < 256u * kTabRow / 4; k += kABlock) {
-        const uint32_t v = k / (kTabRow / 4), r = k % (kTabRow / 4);
-        const uint2 e = split2(a.lev[v & 15u], a.lev[v >> 4]);
-        tb.w[k] = SPLIT_N ? ((r & 1u) ? e.y : e.x) : (r < kTabCopies ? e.x : e.y);
+    for (uint32_t k = threadIdx.x; k < WK + (SHARED ? 0 : WV); k += kABlock) {
+        const bool vtab = k >= WK;
+        const uint32_t kk = vtab ? k - WK : k;
+        const uint32_t v = kk / (kTabRow / 4), r = kk % (kTabRow / 4);
+        const float *lev = vtab ? a.lev_v : a.lev_k;
+        const uint2 e = split2(lev[v & 15u], lev[v >> 4]);
+        tabs[k] = SPLIT_N ? ((r & 1u) ? e.y : e.x) : (r < kTabCopies ? e.x : e.y);
     }
     __syncthreads();
+    const uint32_t *tbk = tabs, *tbv = SHARED ? tabs : tabs + WK;
 
     const uint32_t lane = lane_id(), j = lane & 15u, g = lane >> 4;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -554,8 +645,8 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
     // logits in base-2 units: s = C * ||k|| * fq
     const float fq = a.scale * 1.4426950408889634f / ((float)kAD * qscale_mine);
 
-    const uint8_t *kc = a.kc + head * n * kACodeBytes;
-    const uint8_t *vc = a.vc + head * n * kACodeBytes;
+    const uint8_t *kc = a.kc + head * n * (16 * KB);
+    const uint8_t *vc = a.vc + head * n * (16 * VB);
     const float *kn = a.kn + head * n;
     const float *vn = a.vn + head * n;
     uint8_t *vb = vbuf[wave];
@@ -581,23 +672,26 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
     // full tiles with the next one's loads in flight (two register sets), then
     // the partial last tile if n is not a multiple of 32
     const int64_t t_full = min(t_end, n / 32);
-    TileRegs ra, rb;
+    TileRegs<KB, VB> ra, rb;
     int64_t tile = t_begin;
     if (tile < t_full) load_tile<true>(kc, vc, kn, vn, n, tile * 32, lane, ra);
     while (tile < t_full) {
         stage_tile(vb, nb, ra, lane);
         if (tile + 1 < t_full) load_tile<true>(kc, vc, kn, vn, n, (tile + 1) * 32, lane, rb);
-        attend_tile<true, QG>(tb, vb, nb, ra.k0, ra.k1, qo, psel, fq, tile * 32, n, lane, st);
+        attend_tile<true, QG>(tbk, tbv, vb, nb, widen_codes<KB, 0>(ra.k0), widen_codes<KB, 0>(ra.k1), qo, psel,
+                              fq, tile * 32, n, lane, st);
         if (++tile >= t_full) break;
         stage_tile(vb, nb, rb, lane);
         if (tile + 1 < t_full) load_tile<true>(kc, vc, kn, vn, n, (tile + 1) * 32, lane, ra);
-        attend_tile<true, QG>(tb, vb, nb, rb.k0, rb.k1, qo, psel, fq, tile * 32, n, lane, st);
+        attend_tile<true, QG>(tbk, tbv, vb, nb, widen_codes<KB, 0>(rb.k0), widen_codes<KB, 0>(rb.k1), qo, psel,
+                              fq, tile * 32, n, lane, st);
         ++tile;
     }
     if (t_full < t_end) {
         load_tile<false>(kc, vc, kn, vn, n, t_full * 32, lane, ra);
         stage_tile(vb, nb, ra, lane);
-        attend_tile<false, QG>(tb, vb, nb, ra.k0, ra.k1, qo, psel, fq, t_full * 32, n, lane, st);
+        attend_tile<false, QG>(tbk, tbv, vb, nb, widen_codes<KB, 0>(ra.k0), widen_codes<KB, 0>(ra.k1), qo, psel,
+                               fq, t_full * 32, n, lane, st);
     }
 
     // SPLIT_N: column j + 8 holds the lo-part sums of column j (DPP, all lanes)
@@ -686,6 +780,18 @@ __global__ __launch_bounds__(kBlock) void k_attn_combine(const AttnArgs a) {
 
 }  // namespace
 
+namespace {
+
+// The partial kernel for the queries per head (one of three operand layouts).
+template <int KB, int VB>
+hipError_t launch_partial(const AttnArgs &a, dim3 grid, hipStream_t s) {
+    if (a.m <= 4) return launch(k_attn_partial<4, KB, VB>, grid, dim3(kABlock), s, a);
+    if (a.m <= 8) return launch(k_attn_partial<8, KB, VB>, grid, dim3(kABlock), s, a);
+    return launch(k_attn_partial<16, KB, VB>, grid, dim3(kABlock), s, a);
+}
+
+}  // namespace
+
 hipError_t attention_scratch(void **ptr) {
     int dev = -1;
     hipError_t e = hipGetDevice(&dev);
@@ -710,9 +816,18 @@ hipError_t attention_scratch(void **ptr) {
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
     const int64_t waves = a.heads * a.chunks;
     const dim3 grid((unsigned)((waves + kAWaves - 1) / kAWaves));
-    const hipError_t e = a.m <= 4   ? launch(k_attn_partial<4>, grid, dim3(kABlock), s, a)
-                         : a.m <= 8 ? launch(k_attn_partial<8>, grid, dim3(kABlock), s, a)
-                                    : launch(k_attn_partial<16>, grid, dim3(kABlock), s, a);
+    hipError_t e = hipErrorInvalidValue;
+    switch (a.kbits * 8 + a.vbits) {
+    case 4 * 8 + 4: e = launch_partial<4, 4>(a, grid, s); break;
+    case 4 * 8 + 3: e = launch_partial<4, 3>(a, grid, s); break;
+    case 4 * 8 + 2: e = launch_partial<4, 2>(a, grid, s); break;
+    case 3 * 8 + 4: e = launch_partial<3, 4>(a, grid, s); break;
+    case 3 * 8 + 3: e = launch_partial<3, 3>(a, grid, s); break;
+    case 3 * 8 + 2: e = launch_partial<3, 2>(a, grid, s); break;
+    case 2 * 8 + 4: e = launch_partial<2, 4>(a, grid, s); break;
+    case 2 * 8 + 3: e = launch_partial<2, 3>(a, grid, s); break;
+    case 2 * 8 + 2: e = launch_partial<2, 2>(a, grid, s); break;
+    }
     if (e != hipSuccess) return e;
     const int64_t rows = a.heads * a.m;
     return launch(k_attn_combine, dim3((unsigned)((rows + kWaves - 1) / kWaves)), dim3(kBlock), s, a);

@@ -60,7 +60,8 @@ struct ScoreArgs {
     uint32_t dsign[kMaxD / 32];
 };
 
-// Attention of m <= 16 queries over 4-bit coded keys and values, d = 128.
+// Attention of m <= 16 queries over coded keys and values, d = 128, key and
+// value codes of 2, 3 or 4 bits each.
 // One partial record (rotated value sum z[128], running max M, running sum l,
 // two pad floats) per (head, chunk, query) in `ws`.
 constexpr int kAttnRecord = 132;
@@ -79,7 +80,7 @@ constexpr size_t kAttnScratchBytes = size_t(32) << 20;
 
 struct AttnArgs {
     const float *q;      // [heads][m][128]
-    const uint8_t *kc;   // [heads][n][64]
+    const uint8_t *kc;   // [heads][n][16 kbits]
     const uint8_t *vc;
     const float *kn;     // [heads][n]
     const float *vn;
@@ -87,8 +88,10 @@ struct AttnArgs {
     float *out;          // [heads][m][128]
     int64_t heads, n;
     int m, chunks;
+    int kbits, vbits;    // code widths of keys and values
     float scale;
-    float lev[16];
+    float lev_k[16];     // Lloyd-Max levels of the key codes
+    float lev_v[16];     // of the value codes
     uint32_t dsign_k[4], dsign_v[4];
 };
 

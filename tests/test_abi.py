@@ -46,7 +46,7 @@ def test_binding_has_every_declared_function():
 
 
 def test_abi_version(lib):
-    assert rht.rht_abi_version() == 5
+    assert rht.rht_abi_version() == 6
     for s in range(10):
         assert isinstance(rht.rht_status_str(s), str) and rht.rht_status_str(s)
 
@@ -125,9 +125,10 @@ def test_binding_rejects_cpu_tensors(lib):
         rht.quantize(torch.zeros(4, 128), 4, 1)
 
 
-def _att(lib, q=FAKE, m=4, kc=FAKE, kn=FAKE, vc=FAKE, vn=FAKE, heads=2, n=100, d=128, bits=4, out=FAKE,
-         ws=FAKE, wsb=1 << 40):
-    return lib.rht_attention(q, m, kc, kn, vc, vn, heads, n, d, bits, 1, 2, 0.1, out, ws, wsb, None)
+def _att(lib, q=FAKE, m=4, kc=FAKE, kn=FAKE, vc=FAKE, vn=FAKE, heads=2, n=100, d=128, bits=4, vbits=None,
+         out=FAKE, ws=FAKE, wsb=1 << 40):
+    vbits = bits if vbits is None else vbits
+    return lib.rht_attention(q, m, kc, kn, vc, vn, heads, n, d, bits, vbits, 1, 2, 0.1, out, ws, wsb, None)
 
 
 def test_attention_validation_order(lib):
@@ -142,8 +143,12 @@ def test_attention_validation_order(lib):
     assert _att(lib, heads=(1 << 63) - 1, m=16, d=64) == E_COUNT
     for d in (64, 256, 100):
         assert _att(lib, d=d, bits=2) == E_DIM
-    for b in (1, 2, 3, 5):
+    for b in (0, 1, 5):
         assert _att(lib, bits=b) == E_BITS
+        assert _att(lib, bits=4, vbits=b) == E_BITS
+        assert _att(lib, bits=b, vbits=3) == E_BITS
+    for kb, vb in ((2, 2), (3, 4), (4, 3), (4, 2)):    # every width 2..4 for keys and for values
+        assert _att(lib, bits=kb, vbits=vb, q=0) == E_NULL
     assert _att(lib, heads=0, q=0, kc=0, kn=0, vc=0, vn=0, out=0, ws=0, n=0) == OK  # no-op
     for kw in ("q", "kc", "kn", "vc", "vn", "out", "ws"):
         assert _att(lib, **{kw: 0}) == E_NULL, kw
@@ -155,7 +160,7 @@ def test_attention_validation_order(lib):
 
 
 def _att_na(lib, q=FAKE, m=4, kc=FAKE, kn=FAKE, vc=FAKE, vn=FAKE, heads=2, n=100, d=128, bits=4, out=FAKE):
-    return lib.rht_attention_noalloc(q, m, kc, kn, vc, vn, heads, n, d, bits, 1, 2, 0.1, out, None)
+    return lib.rht_attention_noalloc(q, m, kc, kn, vc, vn, heads, n, d, bits, 3, 1, 2, 0.1, out, None)
 
 
 def test_attention_noalloc_validation_order(lib):
@@ -166,7 +171,7 @@ def test_attention_noalloc_validation_order(lib):
         assert _att_na(lib, m=m, d=64) == E_COUNT
     assert _att_na(lib, n=(1 << 26) + 1, d=64) == E_COUNT
     assert _att_na(lib, d=64) == E_DIM
-    assert _att_na(lib, bits=3) == E_BITS
+    assert _att_na(lib, bits=1) == E_BITS
     assert _att_na(lib, heads=0, q=0, kc=0, kn=0, vc=0, vn=0, out=0, n=0) == OK
     for kw in ("q", "kc", "kn", "vc", "vn", "out"):
         assert _att_na(lib, **{kw: 0}) == E_NULL, kw

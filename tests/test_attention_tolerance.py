@@ -79,7 +79,7 @@ def test_bound_separates_rounding_from_a_lost_term(scale, qmul):
     kc, vc = kc.reshape(heads, n, -1), vc.reshape(heads, n, -1)
     kn, vn = kn.reshape(heads, n), vn.reshape(heads, n)
     q = (qmul * rng.standard_normal((heads, m, D))).astype(np.float32)
-    ref = oracle.attention(q, kc, kn, vc, vn, D, BITS, 81, 82, scale)
+    ref = oracle.attention(q, kc, kn, vc, vn, D, BITS, BITS, 81, 82, scale)
     qt, kterm = attention_terms(q, kc, kn, D, BITS, 81, oracle.lloyd_max(BITS)[0],
                                 oracle.signs(81, D).astype(np.float64), scipy.linalg.hadamard(D))
     bound = attention_bound(q, qt, kterm, decoded(kc, kn, 81), decoded(vc, vn, 82), ref, scale)
@@ -105,7 +105,7 @@ def test_value_scale_follows_the_weights():
     q = rng.standard_normal((heads, m, D)).astype(np.float32)
     q[:, 1] *= 1e4
     scale = 1 / math.sqrt(D)
-    ref = oracle.attention(q, kc, kn, vc, vn, D, BITS, 91, 92, scale)
+    ref = oracle.attention(q, kc, kn, vc, vn, D, BITS, BITS, 91, 92, scale)
     qt, kterm = attention_terms(q, kc, kn, D, BITS, 91, oracle.lloyd_max(BITS)[0],
                                 oracle.signs(91, D).astype(np.float64), scipy.linalg.hadamard(D))
     bound = attention_bound(q, qt, kterm, decoded(kc, kn, 91), decoded(vc, vn, 92), ref, scale)

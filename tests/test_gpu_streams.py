@@ -45,7 +45,7 @@ def pipeline(x, q, seed):
     logits = rht.score(q, codes, norms, D, BITS, seed)
     n = x.shape[0]
     att = rht.attention(q[None], codes.view(1, n, -1), norms.view(1, n), codes.view(1, n, -1),
-                        norms.view(1, n), BITS, seed, seed, 0.1)
+                        norms.view(1, n), BITS, BITS, seed, seed, 0.1)
     return [codes, norms, y, logits, att]
 
 
@@ -93,7 +93,7 @@ def test_graph_replays_match_eager_calls():
                            rht.F16, st)
         rht.rht_score(q.data_ptr(), 4, codes.data_ptr(), norms.data_ptr(), n, D, BITS, seed, logits.data_ptr(), st)
         rht.rht_attention(q.data_ptr(), 4, codes.data_ptr(), norms.data_ptr(), codes.data_ptr(), norms.data_ptr(),
-                          1, n, D, BITS, seed, seed, 0.1, att.data_ptr(), ws.data_ptr(), need, st)
+                          1, n, D, BITS, BITS, seed, seed, 0.1, att.data_ptr(), ws.data_ptr(), need, st)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())

@@ -502,34 +502,37 @@ def _dense_decode(codes, norms, d, bits, seed):
     return (y * norms[..., None].astype(np.float64)) @ (dense_rotation(d, seed) / math.sqrt(d))
 
 
-@pytest.mark.parametrize("bits,d", [(4, 128), (2, 64), (3, 32), (1, 16)])
-def test_attention_matches_library_softmax_on_dense_decodes(bits, d):
-    # scipy's softmax over logits against an independently decoded K, V
-    rng = np.random.default_rng(bits * 100 + d)
+@pytest.mark.parametrize("kbits,vbits,d", [(4, 4, 128), (2, 2, 64), (3, 3, 32), (1, 1, 16), (4, 3, 128),
+                                           (3, 4, 64), (4, 2, 32), (2, 3, 128)])
+def test_attention_matches_library_softmax_on_dense_decodes(kbits, vbits, d):
+    # scipy's softmax over logits against an independently decoded K, V (each
+    # with the codebook of its own width: 4-bit keys with 3-bit values is the
+    # KV-cache pairing of "Practical use in llama.cpp")
+    rng = np.random.default_rng(kbits * 100 + vbits * 10 + d)
     heads, m, n = 3, 4, 37
-    kc, kn = _coded_heads(rng, heads, n, d, bits, 7)
-    vc, vn = _coded_heads(rng, heads, n, d, bits, 9)
+    kc, kn = _coded_heads(rng, heads, n, d, kbits, 7)
+    vc, vn = _coded_heads(rng, heads, n, d, vbits, 9)
     q = rng.standard_normal((heads, m, d)).astype(np.float32)
     scale = 1.0 / math.sqrt(d)
-    got = oracle.attention(q, kc, kn, vc, vn, d, bits, 7, 9, scale)
+    got = oracle.attention(q, kc, kn, vc, vn, d, kbits, vbits, 7, 9, scale)
     for b in range(heads):
-        kd = _dense_decode(kc[b], kn[b], d, bits, 7)
-        vd = _dense_decode(vc[b], vn[b], d, bits, 9)
+        kd = _dense_decode(kc[b], kn[b], d, kbits, 7)
+        vd = _dense_decode(vc[b], vn[b], d, vbits, 9)
         p = scipy.special.softmax(scale * (q[b].astype(np.float64) @ kd.T), axis=1)
         np.testing.assert_allclose(got[b], p @ vd, rtol=1e-11, atol=1e-12)
 
 
-@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("kbits,vbits", [(1, 1), (2, 2), (3, 3), (4, 4), (4, 3), (2, 4), (3, 1)])
 @pytest.mark.parametrize("d", [32, 128, 256])
-def test_attention_rotated_domain_equals_definition(bits, d):
+def test_attention_rotated_domain_equals_definition(kbits, vbits, d):
     # logits on the codes, value sum kept rotated, one inverse transform per query
-    rng = np.random.default_rng(bits + d)
+    rng = np.random.default_rng(kbits + 8 * vbits + d)
     heads, m, n = 2, 5, 61
-    kc, kn = _coded_heads(rng, heads, n, d, bits, 21)
-    vc, vn = _coded_heads(rng, heads, n, d, bits, 22)
+    kc, kn = _coded_heads(rng, heads, n, d, kbits, 21)
+    vc, vn = _coded_heads(rng, heads, n, d, vbits, 22)
     q = (3 * rng.standard_normal((heads, m, d))).astype(np.float32)
-    a = oracle.attention(q, kc, kn, vc, vn, d, bits, 21, 22, 0.2)
-    r = oracle.attention_rotated(q, kc, kn, vc, vn, d, bits, 21, 22, 0.2)
+    a = oracle.attention(q, kc, kn, vc, vn, d, kbits, vbits, 21, 22, 0.2)
+    r = oracle.attention_rotated(q, kc, kn, vc, vn, d, kbits, vbits, 21, 22, 0.2)
     np.testing.assert_allclose(r, a, rtol=1e-12, atol=1e-12 * np.abs(a).max())
 
 
@@ -539,7 +542,7 @@ def test_attention_single_key_is_its_value():
     kc, kn = _coded_heads(rng, 2, 1, d, bits, 3)
     vc, vn = _coded_heads(rng, 2, 1, d, bits, 4)
     q = rng.standard_normal((2, 3, d)).astype(np.float32)
-    got = oracle.attention_rotated(q, kc, kn, vc, vn, d, bits, 3, 4, 0.5)
+    got = oracle.attention_rotated(q, kc, kn, vc, vn, d, bits, bits, 3, 4, 0.5)
     for b in range(2):
         want = _dense_decode(vc[b], vn[b], d, bits, 4)[0]
         np.testing.assert_allclose(got[b], np.broadcast_to(want, (3, d)), rtol=1e-12, atol=1e-13)
@@ -555,22 +558,22 @@ def test_attention_uniform_weights_give_the_mean_value():
     q0 = np.zeros((1, 2, d), np.float32)
     q1 = rng.standard_normal((1, 2, d)).astype(np.float32)
     for q, s in ((q0, 1.0), (q1, 0.0)):
-        got = oracle.attention_rotated(q, kc, kn, vc, vn, d, bits, 13, 14, s)
+        got = oracle.attention_rotated(q, kc, kn, vc, vn, d, bits, bits, 13, 14, s)
         np.testing.assert_allclose(got[0], np.broadcast_to(want, (2, d)), rtol=1e-12, atol=1e-13)
 
 
 def test_attention_large_scale_selects_the_best_key():
     rng = np.random.default_rng(8)
-    d, bits, n = 64, 4, 25
+    d, bits, vbits, n = 64, 4, 3, 25
     kc, kn = _coded_heads(rng, 1, n, d, bits, 31)
-    vc, vn = _coded_heads(rng, 1, n, d, bits, 32)
+    vc, vn = _coded_heads(rng, 1, n, d, vbits, 32)
     q = rng.standard_normal((1, 1, d)).astype(np.float32)
     kd = _dense_decode(kc[0], kn[0], d, bits, 31)
     logits = kd @ q[0, 0].astype(np.float64)
     best = int(np.argmax(logits))
     gap = np.sort(logits)[-1] - np.sort(logits)[-2]
-    got = oracle.attention_rotated(q, kc, kn, vc, vn, d, bits, 31, 32, 60.0 / gap)
-    want = _dense_decode(vc[0], vn[0], d, bits, 32)[best]
+    got = oracle.attention_rotated(q, kc, kn, vc, vn, d, bits, vbits, 31, 32, 60.0 / gap)
+    want = _dense_decode(vc[0], vn[0], d, vbits, 32)[best]
     np.testing.assert_allclose(got[0, 0], want, rtol=1e-9, atol=1e-9 * np.abs(want).max())
 
 
@@ -580,16 +583,16 @@ def test_attention_key_permutation_and_value_scaling():
     kc, kn = _coded_heads(rng, 1, n, d, bits, 41)
     vc, vn = _coded_heads(rng, 1, n, d, bits, 42)
     q = rng.standard_normal((1, 3, d)).astype(np.float32)
-    base = oracle.attention_rotated(q, kc, kn, vc, vn, d, bits, 41, 42, 0.3)
+    base = oracle.attention_rotated(q, kc, kn, vc, vn, d, bits, bits, 41, 42, 0.3)
     perm = rng.permutation(n)
-    got = oracle.attention_rotated(q, kc[:, perm], kn[:, perm], vc[:, perm], vn[:, perm], d, bits, 41,
-                                   42, 0.3)
+    got = oracle.attention_rotated(q, kc[:, perm], kn[:, perm], vc[:, perm], vn[:, perm], d, bits, bits,
+                                   41, 42, 0.3)
     np.testing.assert_allclose(got, base, rtol=1e-12, atol=1e-14)
     # values enter linearly: doubling every value norm doubles the output
-    got2 = oracle.attention_rotated(q, kc, kn, vc, 2 * vn, d, bits, 41, 42, 0.3)
+    got2 = oracle.attention_rotated(q, kc, kn, vc, 2 * vn, d, bits, bits, 41, 42, 0.3)
     np.testing.assert_allclose(got2, 2 * base, rtol=1e-12, atol=1e-14)
     # swapping the key and value seeds changes the result
-    other = oracle.attention_rotated(q, kc, kn, vc, vn, d, bits, 42, 41, 0.3)
+    other = oracle.attention_rotated(q, kc, kn, vc, vn, d, bits, bits, 42, 41, 0.3)
     assert np.abs(other - base).max() > 1e-3 * np.abs(base).max()
 
 
