@@ -209,17 +209,6 @@ void sign_words(uint64_t seed, int d, uint32_t *words) {
 bool pow2_dim(int32_t d) { return d >= kMinD && d <= kMaxD && (d & (d - 1)) == 0; }
 bool aligned(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Coordinate-to-lane layout of the MSE kernels: 1 (default) interleaves the
-// lanes of a vector in chunks that own one code word each; 0 gives every lane
-// one contiguous run.  RHT_LAYOUT overrides it (a tuning knob).
-int layout_choice() {
-    static const int v = [] {
-        const char *e = std::getenv("RHT_LAYOUT");
-        return e ? std::atoi(e) : 1;
-    }();
-    return v;
-}
-
 rht_status launched(hipError_t e) { return e == hipSuccess ? RHT_OK : RHT_E_DEVICE; }
 
 // Key chunks per head for attention: enough (head, chunk) wavefronts to fill
@@ -246,14 +235,6 @@ bool hadamard_on_mfma() {
     static const bool v = [] {
         const char *e = std::getenv("RHT_HADAMARD");
         return !(e && std::strcmp(e, "valu") == 0);
-    }();
-    return v;
-}
-
-int blocks_per_cu_cap() {
-    static const int v = [] {
-        const char *e = std::getenv("RHT_BLOCKS_PER_CU");
-        return e ? std::atoi(e) : 0;
     }();
     return v;
 }
@@ -346,7 +327,7 @@ rht_status rht_quantize(const void *x, rht_dtype xt, int64_t n, int32_t d, int32
     const Kind kind = (mode == RHT_SCALE_NORM || mode == RHT_SCALE_NORM_BETA) ? kMse
                       : mode == RHT_SCALE_EDEN ? kEden
                       : mode == RHT_SCALE_SIGN_BIASED ? kDriveBiased : kDriveUnbiased;
-    return launched(launch_quantize(d, xt == RHT_F16, bits, kind, layout_choice(), a, (hipStream_t)stream));
+    return launched(launch_quantize(d, xt == RHT_F16, bits, kind, a, (hipStream_t)stream));
 }
 
 rht_status rht_dequantize(const uint8_t *codes, const float *scale, int64_t n, int32_t d,
@@ -375,7 +356,7 @@ rht_status rht_dequantize(const uint8_t *codes, const float *scale, int64_t n, i
     // an EDEN scale decodes exactly like ||x||: x^ = D H (c * scale / d)
     const Kind kind = (mode == RHT_SCALE_NORM || mode == RHT_SCALE_EDEN || mode == RHT_SCALE_NORM_BETA) ? kMse
                       : mode == RHT_SCALE_SIGN_BIASED ? kDriveBiased : kDriveUnbiased;
-    return launched(launch_dequantize(d, yt == RHT_F16, bits, kind, layout_choice(), a, (hipStream_t)stream));
+    return launched(launch_dequantize(d, yt == RHT_F16, bits, kind, a, (hipStream_t)stream));
 }
 
 rht_status rht_residual_quantize(const void *x, rht_dtype xt, int64_t n, int32_t d, int32_t bits,
@@ -402,7 +383,7 @@ rht_status rht_residual_quantize(const void *x, rht_dtype xt, int64_t n, int32_t
     std::memcpy(a.lev, b.lev, sizeof(a.lev));
     std::memcpy(a.thr, b.thr, sizeof(a.thr));
     sign_words(seed, d, a.dsign);
-    return launched(launch_quantize(d, xt == RHT_F16, bits, kResidual, 0, a, (hipStream_t)stream));
+    return launched(launch_quantize(d, xt == RHT_F16, bits, kResidual, a, (hipStream_t)stream));
 }
 
 rht_status rht_residual_dequantize(const uint8_t *codes, const uint8_t *signs, const float *norms,
@@ -427,7 +408,7 @@ rht_status rht_residual_dequantize(const uint8_t *codes, const uint8_t *signs, c
     a.n = n;
     std::memcpy(a.lev, book(bits - 1).lev, sizeof(a.lev));
     sign_words(seed, d, a.dsign);
-    return launched(launch_dequantize(d, yt == RHT_F16, bits, kResidual, 0, a, (hipStream_t)stream));
+    return launched(launch_dequantize(d, yt == RHT_F16, bits, kResidual, a, (hipStream_t)stream));
 }
 
 rht_status rht_score(const float *q, int32_t m, const uint8_t *codes, const float *norms, int64_t n,

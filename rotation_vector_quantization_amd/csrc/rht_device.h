@@ -97,9 +97,7 @@ int resident_blocks(K kernel) {
 constexpr int kDefaultBlocksPerCU = 3;
 
 inline int grid_for(int64_t n, int vpb, int per_cu) {
-    const int cap_env = blocks_per_cu_cap();
-    const int cap_cu = cap_env > 0 ? cap_env : kDefaultBlocksPerCU;
-    if (per_cu > cap_cu) per_cu = cap_cu;
+    if (per_cu > kDefaultBlocksPerCU) per_cu = kDefaultBlocksPerCU;
     const int64_t want = (n + vpb - 1) / vpb;
     const int64_t cap = (int64_t)device_cu_count() * per_cu;
     return (int)(want < cap ? (want > 0 ? want : 1) : cap);

@@ -95,15 +95,13 @@ struct AttnArgs {
     uint32_t dsign_k[4], dsign_v[4];
 };
 
-// Launchers.  `layout` selects the coordinate-to-lane mapping of the MSE
-// kernels (0: each lane owns a contiguous run of the row; 1: the lanes of a
-// vector interleave in chunks of 32/bits coordinates, one code word each);
-// the DRIVE and residual kernels always use contiguous runs.
+// Launchers.  The MSE kernels interleave the lanes of a vector in chunks of
+// 32/bits coordinates (one code word each) at 1, 2 and 4 bits and give every
+// lane a contiguous run of the row at 3 bits; the DRIVE, residual and EDEN
+// kernels always use contiguous runs.
 // Return hipErrorInvalidValue when no kernel exists for the combination.
-hipError_t launch_quantize(int d, bool f16, int bits, Kind kind, int layout, const QuantArgs &a,
-                           hipStream_t s);
-hipError_t launch_dequantize(int d, bool f16out, int bits, Kind kind, int layout,
-                             const DequantArgs &a, hipStream_t s);
+hipError_t launch_quantize(int d, bool f16, int bits, Kind kind, const QuantArgs &a, hipStream_t s);
+hipError_t launch_dequantize(int d, bool f16out, int bits, Kind kind, const DequantArgs &a, hipStream_t s);
 // bits = code width of a.codes; residual: scores the chain of stage-1 codes
 // plus the sign plane.
 hipError_t launch_score(int d, int bits, bool residual, const ScoreArgs &a, hipStream_t s);
@@ -119,10 +117,6 @@ hipError_t launch_dequantize_kv128(const DequantArgs &a, hipStream_t s);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
-
-// Upper bound on resident blocks per CU used to size grids (0 = occupancy
-// limit); read once from RHT_BLOCKS_PER_CU, a launch-shape tuning knob.
-int blocks_per_cu_cap();
 
 // Whether the d = 128, fp16, 4-bit MSE kernels run the H_32 factor of the
 // transform on MFMA (default) or as register/DPP butterflies (RHT_HADAMARD=valu).

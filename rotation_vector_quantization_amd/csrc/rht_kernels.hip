@@ -1692,11 +1692,8 @@ hipError_t run_q(const QuantArgs &a, hipStream_t s) {
                   dim3(kBlock), s, a);
 }
 
-// grid_for with a kernel's own cap on resident blocks per CU, below the
-// default, unless RHT_BLOCKS_PER_CU sets the cap for every kernel.
-inline int capped_grid(int64_t n, int vpb, int per_cu, int cap) {
-    return grid_for(n, vpb, blocks_per_cu_cap() > 0 ? per_cu : min(per_cu, cap));
-}
+// grid_for with a kernel's own cap on resident blocks per CU, below the default.
+inline int capped_grid(int64_t n, int vpb, int per_cu, int cap) { return grid_for(n, vpb, min(per_cu, cap)); }
 
 template <int D, int G, bool F16, int BITS, int KIND>
 hipError_t run_dq(const DequantArgs &a, hipStream_t s) {
@@ -1732,24 +1729,17 @@ hipError_t run_res256(int cb, const QuantArgs &a, hipStream_t s) {
 }
 
 template <int D>
-hipError_t quant_d(bool f16, int bits, Kind kind, int layout, const QuantArgs &a, hipStream_t s) {
+hipError_t quant_d(bool f16, int bits, Kind kind, const QuantArgs &a, hipStream_t s) {
     constexpr int E = D / lanes_per_vec(D);
     switch (kind) {
     case kMse:
         if (D == 128 && f16 && bits == 4 && hadamard_on_mfma()) return launch_quantize_kv128(a, s);
-        // chunked layout: one 32-bit code word per lane-group (G = 32 / bits)
-        if (layout == 1) {
-            switch (bits) {
-            case 1: return f16 ? run_q<D, 32, true, 1, kMse>(a, s) : run_q<D, 32, false, 1, kMse>(a, s);
-            case 2: return f16 ? run_q<D, 16, true, 2, kMse>(a, s) : run_q<D, 16, false, 2, kMse>(a, s);
-            case 4: return f16 ? run_q<D, 8, true, 4, kMse>(a, s) : run_q<D, 8, false, 4, kMse>(a, s);
-            }
-        }
+        // one 32-bit code word per lane-group (G = 32 / bits); 3-bit codes: contiguous runs
         switch (bits) {
-        case 1: return f16 ? run_q<D, E, true, 1, kMse>(a, s) : run_q<D, E, false, 1, kMse>(a, s);
-        case 2: return f16 ? run_q<D, E, true, 2, kMse>(a, s) : run_q<D, E, false, 2, kMse>(a, s);
+        case 1: return f16 ? run_q<D, 32, true, 1, kMse>(a, s) : run_q<D, 32, false, 1, kMse>(a, s);
+        case 2: return f16 ? run_q<D, 16, true, 2, kMse>(a, s) : run_q<D, 16, false, 2, kMse>(a, s);
         case 3: return f16 ? run_q<D, E, true, 3, kMse>(a, s) : run_q<D, E, false, 3, kMse>(a, s);
-        case 4: return f16 ? run_q<D, E, true, 4, kMse>(a, s) : run_q<D, E, false, 4, kMse>(a, s);
+        case 4: return f16 ? run_q<D, 8, true, 4, kMse>(a, s) : run_q<D, 8, false, 4, kMse>(a, s);
         }
         break;
     case kDriveBiased:
@@ -1778,23 +1768,16 @@ hipError_t quant_d(bool f16, int bits, Kind kind, int layout, const QuantArgs &a
 }
 
 template <int D>
-hipError_t dequant_d(bool f16, int bits, Kind kind, int layout, const DequantArgs &a, hipStream_t s) {
+hipError_t dequant_d(bool f16, int bits, Kind kind, const DequantArgs &a, hipStream_t s) {
     constexpr int E = D / lanes_per_vec(D);
     switch (kind) {
     case kMse:
         if (D == 128 && f16 && bits == 4 && hadamard_on_mfma()) return launch_dequantize_kv128(a, s);
-        if (layout == 1) {
-            switch (bits) {
-            case 1: return f16 ? run_dq<D, 32, true, 1, kMse>(a, s) : run_dq<D, 32, false, 1, kMse>(a, s);
-            case 2: return f16 ? run_dq<D, 16, true, 2, kMse>(a, s) : run_dq<D, 16, false, 2, kMse>(a, s);
-            case 4: return f16 ? run_dq<D, 8, true, 4, kMse>(a, s) : run_dq<D, 8, false, 4, kMse>(a, s);
-            }
-        }
         switch (bits) {
-        case 1: return f16 ? run_dq<D, E, true, 1, kMse>(a, s) : run_dq<D, E, false, 1, kMse>(a, s);
-        case 2: return f16 ? run_dq<D, E, true, 2, kMse>(a, s) : run_dq<D, E, false, 2, kMse>(a, s);
+        case 1: return f16 ? run_dq<D, 32, true, 1, kMse>(a, s) : run_dq<D, 32, false, 1, kMse>(a, s);
+        case 2: return f16 ? run_dq<D, 16, true, 2, kMse>(a, s) : run_dq<D, 16, false, 2, kMse>(a, s);
         case 3: return f16 ? run_dq<D, E, true, 3, kMse>(a, s) : run_dq<D, E, false, 3, kMse>(a, s);
-        case 4: return f16 ? run_dq<D, E, true, 4, kMse>(a, s) : run_dq<D, E, false, 4, kMse>(a, s);
+        case 4: return f16 ? run_dq<D, 8, true, 4, kMse>(a, s) : run_dq<D, 8, false, 4, kMse>(a, s);
         }
         break;
     case kDriveBiased:
@@ -1919,32 +1902,30 @@ hipError_t score_d(int bits, bool residual, const ScoreArgs &a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_quantize(int d, bool f16, int bits, Kind kind, int layout, const QuantArgs &a,
-                           hipStream_t s) {
+hipError_t launch_quantize(int d, bool f16, int bits, Kind kind, const QuantArgs &a, hipStream_t s) {
     switch (d) {
-    case 32: return quant_d<32>(f16, bits, kind, layout, a, s);
-    case 64: return quant_d<64>(f16, bits, kind, layout, a, s);
-    case 128: return quant_d<128>(f16, bits, kind, layout, a, s);
-    case 256: return quant_d<256>(f16, bits, kind, layout, a, s);
-    case 512: return quant_d<512>(f16, bits, kind, layout, a, s);
-    case 1024: return quant_d<1024>(f16, bits, kind, layout, a, s);
-    case 2048: return quant_d<2048>(f16, bits, kind, layout, a, s);
-    case 4096: return quant_d<4096>(f16, bits, kind, layout, a, s);
+    case 32: return quant_d<32>(f16, bits, kind, a, s);
+    case 64: return quant_d<64>(f16, bits, kind, a, s);
+    case 128: return quant_d<128>(f16, bits, kind, a, s);
+    case 256: return quant_d<256>(f16, bits, kind, a, s);
+    case 512: return quant_d<512>(f16, bits, kind, a, s);
+    case 1024: return quant_d<1024>(f16, bits, kind, a, s);
+    case 2048: return quant_d<2048>(f16, bits, kind, a, s);
+    case 4096: return quant_d<4096>(f16, bits, kind, a, s);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_dequantize(int d, bool f16out, int bits, Kind kind, int layout,
-                             const DequantArgs &a, hipStream_t s) {
+hipError_t launch_dequantize(int d, bool f16out, int bits, Kind kind, const DequantArgs &a, hipStream_t s) {
     switch (d) {
-    case 32: return dequant_d<32>(f16out, bits, kind, layout, a, s);
-    case 64: return dequant_d<64>(f16out, bits, kind, layout, a, s);
-    case 128: return dequant_d<128>(f16out, bits, kind, layout, a, s);
-    case 256: return dequant_d<256>(f16out, bits, kind, layout, a, s);
-    case 512: return dequant_d<512>(f16out, bits, kind, layout, a, s);
-    case 1024: return dequant_d<1024>(f16out, bits, kind, layout, a, s);
-    case 2048: return dequant_d<2048>(f16out, bits, kind, layout, a, s);
-    case 4096: return dequant_d<4096>(f16out, bits, kind, layout, a, s);
+    case 32: return dequant_d<32>(f16out, bits, kind, a, s);
+    case 64: return dequant_d<64>(f16out, bits, kind, a, s);
+    case 128: return dequant_d<128>(f16out, bits, kind, a, s);
+    case 256: return dequant_d<256>(f16out, bits, kind, a, s);
+    case 512: return dequant_d<512>(f16out, bits, kind, a, s);
+    case 1024: return dequant_d<1024>(f16out, bits, kind, a, s);
+    case 2048: return dequant_d<2048>(f16out, bits, kind, a, s);
+    case 4096: return dequant_d<4096>(f16out, bits, kind, a, s);
     }
     return hipErrorInvalidValue;
 }
