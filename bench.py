@@ -383,6 +383,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip timing the DRIVE, residual and scoring workloads")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip timing the streaming ceiling kernels (shorter profiled runs)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_c2_kv.json from rocprofv3 PMC runs and exit")
     args = ap.parse_args()
@@ -533,8 +535,9 @@ def main():
         cv3, nv3 = rht.quantize(xv, 3, wv.rot_seed)
         attn_k4v3 = attention_workload(torch, rht, dev, stream, ck, nk, cv3, nv3, n, d, 4, 3)
         del cv3, nv3
-    print("timing the streaming ceiling kernels", file=sys.stderr, flush=True)
-    out["shape_ceiling"] = ceiling(torch, dev, stream, xk, ck, nk, yk, n)
+    if not args.no_ceiling:
+        print("timing the streaming ceiling kernels", file=sys.stderr, flush=True)
+        out["shape_ceiling"] = ceiling(torch, dev, stream, xk, ck, nk, yk, n)
     if not args.no_other_workloads:
         del xk, xv, ck, cv, nk, nv, yk, yv
         torch.cuda.empty_cache()
