@@ -85,7 +85,7 @@ def traffic_from(fetch_dir, write_dir):
         allv = [x for h in hits for x in h]
         return sum(allv) / len(allv)
 
-    copy_key = "copy"  # torch's elementwise copy kernel
+    copy_key = "copy"  # torch's copy_ between contiguous device tensors runs __amd_rocclr_copyBuffer
     f_copy, w_copy = pick(fetch, copy_key) * 1024, pick(write, copy_key) * 1024
     kf, kw = COPY_BYTES / f_copy, COPY_BYTES / w_copy
     rec = {"source_digest": source_digest(), "copy_bytes_each_way": COPY_BYTES,
@@ -100,14 +100,23 @@ def traffic_from(fetch_dir, write_dir):
     print(json.dumps(rec, indent=1))
 
 
-def time_launches(torch, stream, fn, sets, iters=20, warm_ms=50.0):
+def time_launches(torch, stream, fn, sets, iters=20, warm_ms=100.0):
     """Per-launch times (ms) of fn(set_index), cycling through `sets` buffer
     sets, from HIP events recorded on `stream` between launches.  The kernel
-    first runs untimed for about warm_ms of GPU time, so clocks that dropped
+    first runs untimed for at least warm_ms of GPU time, so clocks that dropped
     during host-side set-up have ramped up again.  Kernels shorter than 0.1 ms
     are timed in groups of 8 launches per event interval (each value is the
     group's mean): with an event after every launch the host's submission
-    rate, not the GPU, would set the interval."""
+    rate, not the GPU, would set the interval.
+
+    The first launch of a kernel also loads its code object, so it is left out
+    of the launch-time estimate, and the warm-up is measured rather than
+    counted: batches of launches run until their event-timed total reaches
+    warm_ms.  A heavy kernel's time drifts for tens of milliseconds after it
+    starts (the clock settles under the new load), so a warm-up sized from a
+    slow first launch would leave the timed launches inside that drift."""
+    fn(0)
+    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(3):
@@ -115,8 +124,16 @@ def time_launches(torch, stream, fn, sets, iters=20, warm_ms=50.0):
     e1.record(stream)
     torch.cuda.synchronize()
     est = max(e0.elapsed_time(e1) / 3, 1e-3)
-    for i in range(min(int(warm_ms / est), 5000)):
-        fn(i % sets)
+    batch = max(1, min(int(5.0 / est), 1000))  # about 5 ms of launches per batch
+    warmed, k = 0.0, 0
+    while warmed < warm_ms and k < 20000:
+        e0.record(stream)
+        for _ in range(batch):
+            fn(k % sets)
+            k += 1
+        e1.record(stream)
+        torch.cuda.synchronize()
+        warmed += e0.elapsed_time(e1)
     group = 8 if est < 0.1 else 1
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
     torch.cuda.synchronize()
@@ -377,7 +394,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=25)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--cpu-rows", type=int, default=1 << 20,
                     help="rows of the single-thread oracle leg (the all-cores leg takes every K row)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
