@@ -607,16 +607,53 @@ __device__ __forceinline__ void load_res256(const uint16_t *x, int64_t row0, int
     for (int a = 0; a < 8; ++a) raw[a] = stream_load(p + 4 * a);
 }
 
+// Stage-1 codebooks of 1 or 2 bits have equally spaced thresholds: {0} and
+// {-t, 0, t} (the codebook is symmetric).  With step = t (2 bits) or 1 (1 bit)
+// and v = y / step + off, off = 1 (2 bits) or 0 (1 bit), threshold k sits at
+// v = k exactly, so floor(v) alone picks the code: cell i = floor(v) holds
+// code clamp(i + 1, 0, 2^CB - 1).  A value exactly at a threshold lands in the
+// cell above it, as the nearest-level rule breaks ties; y = 0 gives v = off
+// exactly.  The table stores (code, 16 c[code]) for cells -kEvenLow ..
+// kEvenCells - kEvenLow - 1, which covers |y| <= sqrt(256) = 16 (the largest
+// rotated coordinate of a normalized d = 256 vector) for any step >= 0.9.
+constexpr int kEvenLow = 20, kEvenCells = 44;
+
+template <int CB>
+__device__ __forceinline__ void build_even_table(uint2 *tab, const float *lev) {
+    constexpr int kMaxCode = (1 << CB) - 1;
+    for (int k = threadIdx.x; k < kEvenCells; k += kBlock) {
+        const int code = min(max(k - kEvenLow + 1, 0), kMaxCode);
+        tab[k] = make_uint2((uint32_t)code, __builtin_bit_cast(uint32_t, 16.0f * lev[code]));
+    }
+}
+
+// floor(v) as an integer (one v_cvt_flr_i32_f32)
+__device__ __forceinline__ int floor_to_int(float v) {
+    int i;
+    asm("v_cvt_flr_i32_f32 %0, %1" : "=v"(i) : "v"(v));
+    return i;
+}
+
 template <int CB>
 __global__ __launch_bounds__(kBlock) void k_residual_quantize_mfma256(const QuantArgs a) {
     constexpr int D = 256, VPB = kWaves * kR256Rows;
     constexpr int CROW = D * CB / 8, SROW = D / 8;  // code and sign bytes per row
     using LT = Lut256Full;
-    __shared__ u32x4_t lutl[LT::kCells];
+    constexpr bool kEven = CB <= 2;
+    // the nearest-level table: the floor-indexed one for 1- and 2-bit codes,
+    // the threshold-carrying one otherwise
+    __shared__ u32x4_t lutl[kEven ? 1 : LT::kCells];
+    __shared__ uint2 etab[kEvenCells];
     __shared__ __attribute__((aligned(16))) uint8_t ctile[kWaves][kR256Rows * CROW];
     __shared__ __attribute__((aligned(16))) uint8_t stile[kWaves][kR256Rows * SROW];
-    build_lut_lev<LT::kCells, LT::kOff>(lutl, a.thr, a.lev, (1 << CB) - 1);
+    if constexpr (kEven)
+        build_even_table<CB>(etab, a.lev);
+    else
+        build_lut_lev<LT::kCells, LT::kOff>(lutl, a.thr, a.lev, (1 << CB) - 1);
     __syncthreads();
+    // v = y16 * estep + eoff (y16 = 16 y)
+    const float estep = CB == 2 ? 1.0f / (16.0f * a.thr[2]) : 1.0f / 16.0f;
+    const float eoff = CB == 2 ? 1.0f : 0.0f;
 
     const uint32_t lane = lane_id(), j = lane & 15u, g = lane >> 4;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -695,29 +732,45 @@ __global__ __launch_bounds__(kBlock) void k_residual_quantize_mfma256(const Quan
 
         const float nrm = sqrtf(ss);
         const float inv16 = ss > 0.0f ? 16.0f / nrm : 0.0f;
+        const float ev = inv16 * estep;
         float r2 = 0.0f, r1 = 0.0f;
 #pragma unroll
         for (int blk = 0; blk < 8; ++blk) {
-            // coordinates 32 blk + 8 g + 4 mh + r, in order t = 4 mh + r; the
-            // eight table reads of a block are issued together, then used
-            float y[8];
-            u32x4_t e[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                y[t] = c[blk][t >> 2][t & 3] * inv16;
-                e[t] = lut_cell<LT::kCells, LT::kOff, false>(lutl, y[t]);
-            }
+            // coordinates 32 blk + 8 g + 4 mh + r, in order t = 4 mh + r
             uint32_t code = 0u, neg = 0u;
+            if constexpr (kEven) {
+                // the eight table reads of a block are issued together, then used
+                uint2 e[8];
 #pragma unroll
-            for (int t = 7; t >= 0; --t) {
-                const float y16 = y[t];
-                float l16;
-                const uint32_t cd = code_in_cell(e[t], y16, l16);
-                code |= cd << (CB * t);
-                const float rho = y16 - l16;
-                r2 = fmaf(rho, rho, r2);
-                r1 += fabsf(rho);
-                neg = (neg << 1) | (__builtin_bit_cast(uint32_t, rho) >> 31);
+                for (int t = 0; t < 8; ++t)
+                    e[t] = etab[floor_to_int(fmaf(c[blk][t >> 2][t & 3], ev, eoff)) + kEvenLow];
+#pragma unroll
+                for (int t = 7; t >= 0; --t) {
+                    code |= e[t].x << (CB * t);
+                    const float rho = fmaf(c[blk][t >> 2][t & 3], inv16, -__builtin_bit_cast(float, e[t].y));
+                    r2 = fmaf(rho, rho, r2);
+                    r1 += fabsf(rho);
+                    neg = (neg << 1) | (__builtin_bit_cast(uint32_t, rho) >> 31);
+                }
+            } else {
+                float y[8];
+                u32x4_t e[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    y[t] = c[blk][t >> 2][t & 3] * inv16;
+                    e[t] = lut_cell<LT::kCells, LT::kOff, false>(lutl, y[t]);
+                }
+#pragma unroll
+                for (int t = 7; t >= 0; --t) {
+                    const float y16 = y[t];
+                    float l16;
+                    const uint32_t cd = code_in_cell(e[t], y16, l16);
+                    code |= cd << (CB * t);
+                    const float rho = y16 - l16;
+                    r2 = fmaf(rho, rho, r2);
+                    r1 += fabsf(rho);
+                    neg = (neg << 1) | (__builtin_bit_cast(uint32_t, rho) >> 31);
+                }
             }
             // a zero vector has residual 0 everywhere, whose sign bit is +1
             const uint32_t sbits = ss > 0.0f ? (~neg & 0xFFu) : 0xFFu;
