@@ -208,6 +208,27 @@ __device__ __forceinline__ void load_tile(const uint8_t *kc, const uint8_t *vc, 
     t.nrm = (lane < 32 ? kn : vn)[rn];
 }
 
+// Eight B-bit codes (bits [0, 8B) of x, the bits above zero)
+// spread to one code per nibble, by halving the field groups: 4 + 4 codes to
+// the two 16-bit halves, 2 + 2 to the bytes of each half, 1 + 1 to the
+// nibbles of each byte.  Each step moves the upper group of every pair up by
+// s bits as t + (2^s - 1) (t & M), M the upper groups' bits: the fields do not
+// overlap, so the sum carries nothing.
+template <int B>
+__device__ __forceinline__ uint32_t spread8(uint32_t x) {
+    static_assert(B == 2 || B == 3, "2- and 3-bit codes");
+    if constexpr (B == 3) {
+        uint32_t t = x + 15u * (x & 0x00FFF000u);   // c4..c7: bits 12-23 -> 16-27
+        const uint32_t m = t & 0x0FC00FC0u;         // pairs: bits 6-11 -> 8-13 of each half
+        t += (m << 1) + m;
+        return t + (t & 0x38383838u);               // codes: bits 3-5 -> 4-6 of each byte
+    } else {
+        uint32_t t = x + 255u * (x & 0x0000FF00u);  // c4..c7: bits 8-15 -> 16-23
+        t += 15u * (t & 0x00F000F0u);               // pairs: bits 4-7 -> 8-11 of each half
+        return t + 3u * (t & 0x0C0C0C0Cu);          // codes: bits 2-3 -> 4-5 of each byte
+    }
+}
+
 // 32 codes of B bits (an LSB-first bitstream in w[OFF .. OFF + B - 1]) as one
 // code per nibble: code i at bits [4 i, 4 i + 4) of the result.
 template <int B, int OFF, int N>
@@ -218,15 +239,13 @@ __device__ __forceinline__ u32x4_t widen_codes(const uint32_t (&w)[N]) {
         uint32_t o[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            uint32_t acc = 0;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int p = B * (8 * k + t), wi = OFF + p / 32, sh = p % 32;
-                uint32_t c = w[wi] >> sh;
-                if (sh + B > 32) c |= w[wi + 1] << (32 - sh);
-                acc |= (c & ((1u << B) - 1u)) << (4 * t);
-            }
-            o[k] = acc;
+            // codes 8k .. 8k + 7: bits [8Bk, 8Bk + 8B) of the stream
+            constexpr int W = 8 * B;
+            const int p = W * k, wi = OFF + p / 32, sh = p % 32;
+            uint32_t x = sh + W > 32 ? __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) : w[wi] >> sh;
+            // the bits above the field belong to the next codes unless it ends the word
+            if (sh + W != 32) x &= (1u << W) - 1u;
+            o[k] = spread8<B>(x);
         }
         return u32x4_t{o[0], o[1], o[2], o[3]};
     }
