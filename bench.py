@@ -85,8 +85,16 @@ def traffic_from(fetch_dir, write_dir):
         allv = [x for h in hits for x in h]
         return sum(allv) / len(allv)
 
-    copy_key = "copy"  # torch's copy_ between contiguous device tensors runs __amd_rocclr_copyBuffer
-    f_copy, w_copy = pick(fetch, copy_key) * 1024, pick(write, copy_key) * 1024
+    def pick_copy(vals):
+        # torch's copy_ between contiguous device tensors runs __amd_rocclr_copyBuffer; the
+        # copy of known size is the largest of them (host -> device uploads use it too)
+        allv = [x for k, v in vals.items() if "copyBuffer" in k for x in v]
+        if not allv:
+            raise SystemExit("no copyBuffer dispatches in the counter files")
+        big = [x for x in allv if x > 0.9 * max(allv)]
+        return sum(big) / len(big)
+
+    f_copy, w_copy = pick_copy(fetch) * 1024, pick_copy(write) * 1024
     kf, kw = COPY_BYTES / f_copy, COPY_BYTES / w_copy
     rec = {"source_digest": source_digest(), "copy_bytes_each_way": COPY_BYTES,
            "fetch_scale": kf, "write_scale": kw, "kernels": {}}
