@@ -226,38 +226,73 @@ __global__ __launch_bounds__(kBlock) void k_quantize_mfma128(const QuantArgs a) 
     }
 }
 
-// Direct global -> LDS copy of the 32 code rows at row0 (2 KiB; rows past the
-// end repeat the last row).
-__device__ __forceinline__ void stage_codes(const uint8_t *codes, int64_t row0, int64_t n, char *tile,
-                                            uint32_t lane) {
+// Direct global -> LDS copy of the 32 code rows at row0 (2 KiB) and their
+// scales (bytes 2048 + 4 r; lanes 32-63 repeat lanes 0-31's, filling bytes
+// 2176-2303).  Rows past the end repeat the last row.
+constexpr int kScaleOff = kCodeTileBytes;
+constexpr int kDecTileBytes = kCodeTileBytes + 256;
+
+__device__ __forceinline__ void stage_codes(const DequantArgs &a, int64_t row0, char *tile, uint32_t lane) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const uint32_t r = 16u * k + (lane >> 2), pos = lane & 3u;
-        const int64_t row = row0 + r < n ? row0 + r : n - 1;
-        const uint4 *src = reinterpret_cast<const uint4 *>(codes + row * 64) + (pos ^ (r & 3u));
+        const int64_t row = row0 + r < a.n ? row0 + r : a.n - 1;
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.codes + row * 64) + (pos ^ (r & 3u));
         __builtin_amdgcn_global_load_lds(src, (lds_void *)(tile + 1024 * k), 16, 0, 0);
     }
+    const int64_t row = row0 + (lane & 31u) < a.n ? row0 + (lane & 31u) : a.n - 1;
+    __builtin_amdgcn_global_load_lds(a.scale + row, (lds_void *)(tile + kScaleOff), 4, 0, 0);
 }
 
 // One tile of the decoder: codes from the staged `tile`, the next tile's codes
 // copied into `next` meanwhile, output transposed through `yt` into coalesced
-// stores.
+// stores.  WHOLE: this tile and the wave's previous one have all 32 rows below
+// n.  The previous tile then issued all eight of its stores after this tile's
+// copies (codes and scales), so waiting until at most eight memory operations are
+// outstanding covers the copies and leaves the stores in flight (vmcnt counts
+// loads and stores together and retires them in order); with a full wait each
+// tile began by waiting for the previous tile's stores to complete (decoder on
+// the KV block, two boxes: 0.520 -> 0.513 ms and 0.514-0.516 -> 0.512-0.513 ms).  The staged code reads then sit in the
+// same asm block as that wait: the compiler would otherwise put a full wait in
+// front of ordinary LDS reads that follow direct copies.  This tile's stores
+// need no row check.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) const char lds_cchar;
+template <bool WHOLE>
 __device__ __forceinline__ void dequantize_tile128(const DequantArgs &a, const uint2 *tab, const u32x4_t (&A)[4],
                                                    const uint32_t (&om)[4][8], const char *tile, char *next,
-                                                   char *yt, int64_t v0, int64_t v0_next, uint32_t lane,
-                                                   float &scale) {
+                                                   char *yt, int64_t v0, int64_t v0_next, uint32_t lane) {
     constexpr int D = 128;
     const uint32_t j = lane & 31u, h = lane >> 5;
     uint2 cw[4];
-    wait_lds_copies();
+    float scale;
+    if constexpr (WHOLE) {
+        const uint32_t base = (uint32_t)(uintptr_t)(lds_cchar *)tile;  // LDS byte address
+        u32x2_t r0, r1, r2, r3;
+        asm volatile("s_waitcnt vmcnt(8)\n\t"
+                     "ds_read_b64 %0, %5\n\t"
+                     "ds_read_b64 %1, %6\n\t"
+                     "ds_read_b64 %2, %7\n\t"
+                     "ds_read_b64 %3, %8\n\t"
+                     "ds_read_b32 %4, %9\n\t"
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=v"(r0), "=v"(r1), "=v"(r2), "=v"(r3), "=v"(scale)
+                     : "v"(base + 16 * c_chunk(j, 0) + 8 * h), "v"(base + 16 * c_chunk(j, 1) + 8 * h),
+                       "v"(base + 16 * c_chunk(j, 2) + 8 * h), "v"(base + 16 * c_chunk(j, 3) + 8 * h),
+                       "v"(base + kScaleOff + 4 * j)
+                     : "memory");
+        cw[0] = make_uint2(r0.x, r0.y); cw[1] = make_uint2(r1.x, r1.y);
+        cw[2] = make_uint2(r2.x, r2.y); cw[3] = make_uint2(r3.x, r3.y);
+    } else {
+        wait_lds_copies();
 #pragma unroll
-    for (int ap = 0; ap < 4; ++ap)  // code bytes 16 ap + 8 h .. +8 of row j
-        cw[ap] = *reinterpret_cast<const uint2 *>(tile + 16 * c_chunk(j, ap) + 8 * h);
+        for (int ap = 0; ap < 4; ++ap)  // code bytes 16 ap + 8 h .. +8 of row j
+            cw[ap] = *reinterpret_cast<const uint2 *>(tile + 16 * c_chunk(j, ap) + 8 * h);
+        scale = *reinterpret_cast<const float *>(tile + kScaleOff + 4 * j);
+    }
     const float alpha = scale * (1.0f / D);
-    // the next tile's codes (LDS) and scales (registers) load during this one
-    stage_codes(a.codes, v0_next, a.n, next, lane);
-    const int64_t vnext = v0_next + j;
-    scale = a.scale[vnext < a.n ? vnext : a.n - 1];
+    // the next tile's codes and scales load into LDS during this one
+    stage_codes(a, v0_next, next, lane);
     floatx16 c[4];
 #pragma unroll
     for (int ap = 0; ap < 4; ++ap) {
@@ -292,7 +327,7 @@ __device__ __forceinline__ void dequantize_tile128(const DequantArgs &a, const u
     for (int k = 0; k < 8; ++k) {
         const uint32_t r = 4u * k + (lane >> 4), cc = lane & 15u;
         const uint4 val = *reinterpret_cast<const uint4 *>(yt + 16 * x_chunk(r, cc));
-        if (v0 + r < a.n) stream_store(val, reinterpret_cast<uint4 *>(y + (v0 + r) * D) + cc);
+        if (WHOLE || v0 + r < a.n) stream_store(val, reinterpret_cast<uint4 *>(y + (v0 + r) * D) + cc);
     }
 }
 
@@ -300,8 +335,8 @@ __global__ __launch_bounds__(kBlock) void k_dequantize_mfma128(const DequantArgs
     constexpr int VPB = kWaves * kRowsPerWave;
     // per code byte: (hi parts, lo parts) of its two levels as packed fp16
     __shared__ uint2 tab[256];
-    __shared__ __attribute__((aligned(16))) char cbuf0[kWaves][kCodeTileBytes];
-    __shared__ __attribute__((aligned(16))) char cbuf1[kWaves][kCodeTileBytes];
+    __shared__ __attribute__((aligned(16))) char cbuf0[kWaves][kDecTileBytes];
+    __shared__ __attribute__((aligned(16))) char cbuf1[kWaves][kDecTileBytes];
     __shared__ __attribute__((aligned(16))) char ybuf[kWaves][kTileBytes];
     {
         const uint32_t v = threadIdx.x;
@@ -331,14 +366,24 @@ __global__ __launch_bounds__(kBlock) void k_dequantize_mfma128(const DequantArgs
     const int64_t stride = (int64_t)gridDim.x * VPB;
     const int64_t first = (int64_t)blockIdx.x * VPB + wave * kRowsPerWave;
     const int64_t limit = a.n + wave * kRowsPerWave;
-    stage_codes(a.codes, first, a.n, cbuf0[wave], lane);
-    const int64_t vfirst = first + (lane & 31u);
-    float scale = a.scale[vfirst < a.n ? vfirst : a.n - 1];
+    stage_codes(a, first, cbuf0[wave], lane);
+    // the first tile, and a tile that or whose predecessor is partial, take
+    // the full wait
+    bool prev_whole = false;
     for (int64_t v0 = first; v0 < limit; v0 += 2 * stride) {
-        dequantize_tile128(a, tab, A, om, cbuf0[wave], cbuf1[wave], ybuf[wave], v0, v0 + stride, lane, scale);
+        const bool w0 = v0 + 32 <= a.n, w1 = v0 + stride + 32 <= a.n;
+        if (prev_whole && w0)
+            dequantize_tile128<true>(a, tab, A, om, cbuf0[wave], cbuf1[wave], ybuf[wave], v0, v0 + stride, lane);
+        else
+            dequantize_tile128<false>(a, tab, A, om, cbuf0[wave], cbuf1[wave], ybuf[wave], v0, v0 + stride, lane);
         if (v0 + stride >= limit) break;
-        dequantize_tile128(a, tab, A, om, cbuf1[wave], cbuf0[wave], ybuf[wave], v0 + stride, v0 + 2 * stride,
-                           lane, scale);
+        if (w0 && w1)
+            dequantize_tile128<true>(a, tab, A, om, cbuf1[wave], cbuf0[wave], ybuf[wave], v0 + stride, v0 + 2 * stride,
+                                     lane);
+        else
+            dequantize_tile128<false>(a, tab, A, om, cbuf1[wave], cbuf0[wave], ybuf[wave], v0 + stride, v0 + 2 * stride,
+                                      lane);
+        prev_whole = w1;
     }
 }
 
