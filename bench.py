@@ -268,6 +268,24 @@ def other_workloads(torch, rht, dev, stream):
                                 "keys_per_s": nk / (ms / 1e3), "TFLOP_per_s": tfs,
                                 "algorithmic_bytes": alg, "GB_per_s": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS,
                                 "bound": "hbm"})
+    del sets_b, sets_r, ls, bsg, ssg, rc, rg, rn, rr
+
+    # MSE scoring at 2^21 keys (673 MB per launch): at 131072 keys a launch
+    # takes 15-17 us and its fixed part (the launch and each block's query
+    # rotation) is a large share.  The keys are the 131072 encoded ones, 16 times.
+    nl = nk * 16
+    cl, nlr = c5.repeat(16, 1), n5.repeat(16)
+    ll = torch.empty((m, nl), dtype=torch.float32, device=dev)
+    st = stats(time_launches(torch, stream, lambda i: rht.rht_score(
+        q.data_ptr(), m, cl.data_ptr(), nlr.data_ptr(), nl, d5, b5, wk.rot_seed, ll.data_ptr(), sh), 1))
+    ms = st["ms_median"]
+    alg = nl * (d5 * b5 // 8 + 4) + m * d5 * 4 + m * nl * 4
+    gbs = alg / (ms / 1e3) / 1e9
+    out["score_large"] = dict(st, **{"workload": "2097152 keys d=128 4-bit codes + norms, 64 fp32 queries, fp32 logits",
+                                     "keys_per_s": nl / (ms / 1e3), "TFLOP_per_s": 2.0 * m * nl * d5 / (ms / 1e3) / 1e12,
+                                     "algorithmic_bytes": alg, "GB_per_s": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS,
+                                     "bound": "hbm"})
+    del cl, nlr, ll
     return out
 
 
