@@ -598,23 +598,33 @@ __device__ __forceinline__ floatx4 mfma16x16x32(u32x4_t a, u32x4_t b, floatx4 c)
 
 // Staging of a wave tile (16 x 256 fp16 = 8 KiB) in LDS, filled by direct
 // global -> LDS copies.  The 16-byte chunk c of tile row r sits at chunk
-// position c ^ (r mod 16) of the row, so that the 16 rows a read instruction
+// position c ^ r of the row (r < 16), so that the 16 rows a read instruction
 // touches at one chunk index land in distinct banks.  Copy instruction k fills
-// 1 KiB: tile rows 2k and 2k + 1, one chunk position per lane.  Rows past the
-// end repeat the last row.
+// 1 KiB: tile rows 2k and 2k + 1, one chunk position per lane.  The copies go
+// through a buffer resource that spans the tile's rows below n, so rows past
+// the end read as zeros (they are transformed but never stored).
 typedef __attribute__((address_space(3))) void lds_void_r;
 constexpr int kR256TileBytes = kR256Rows * 512;
+// Word 3 of a CDNA raw buffer resource: data format 32 bits, no swizzle, no
+// index stride (the offsets are byte offsets, range-checked against the
+// resource's size).
+constexpr int kRawBufferWord3 = 0x00020000;
 
 __device__ __forceinline__ void stage_res256(const uint16_t *x, int64_t row0, int64_t n, char *lds_tile,
                                              uint32_t lane) {
+    const int64_t rows = n - row0 < kR256Rows ? n - row0 : kR256Rows;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(x + row0 * 256), (short)0, (int)(rows * 512),
+                                          kRawBufferWord3);
+    // row r = 2k + h (h = lane / 32), chunk position p = lane % 32, source
+    // chunk p ^ r: byte 512 r + 16 (p ^ r) = (q ^ 32k) + 1024k with
+    // q = 512 h + 16 (p ^ h)
+    const uint32_t h = lane >> 5, q = 512u * h + 16u * ((lane & 31u) ^ h);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const uint32_t r = 2u * k + (lane >> 5), pos = lane & 31u;
-        const int64_t row = row0 + r < n ? row0 + r : n - 1;
-        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(x + row * 256) + (pos ^ (r & 15u));
+    for (int k = 0; k < 8; ++k)
         // cache policy: non-temporal (each input byte is read once)
-        __builtin_amdgcn_global_load_lds(src, (lds_void_r *)(lds_tile + 1024 * k), 16, 0, 2);
-    }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_r *)(lds_tile + 1024 * k), 16,
+                                                 (q ^ (32u * k)) + 1024u * k, 0, 0, 2);
 }
 // The staged chunk c of row r.
 __device__ __forceinline__ u32x4_t staged_chunk(const char *lds_tile, uint32_t r, uint32_t c) {
@@ -630,14 +640,17 @@ __device__ __forceinline__ u32x4_t staged_chunk(const char *lds_tile, uint32_t r
 // exactly.  The table stores (code, 16 c[code]) for cells -kEvenLow ..
 // kEvenCells - kEvenLow - 1, which covers |y| <= sqrt(256) = 16 (the largest
 // rotated coordinate of a normalized d = 256 vector) for any step >= 0.9.
+// It is held once per position t = 0..7 of a code in its group of eight, with
+// the code already shifted to bit CB t, so a group's codes combine by OR alone.
 constexpr int kEvenLow = 20, kEvenCells = 44;
 
 template <int CB>
-__device__ __forceinline__ void build_even_table(uint2 *tab, const float *lev) {
+__device__ __forceinline__ void build_even_table(uint2 (*tab)[kEvenCells], const float *lev) {
     constexpr int kMaxCode = (1 << CB) - 1;
-    for (int k = threadIdx.x; k < kEvenCells; k += kBlock) {
+    for (int i = threadIdx.x; i < 8 * kEvenCells; i += kBlock) {
+        const int t = i / kEvenCells, k = i % kEvenCells;
         const int code = min(max(k - kEvenLow + 1, 0), kMaxCode);
-        tab[k] = make_uint2((uint32_t)code, __builtin_bit_cast(uint32_t, 16.0f * lev[code]));
+        tab[t][k] = make_uint2((uint32_t)code << (CB * t), __builtin_bit_cast(uint32_t, 16.0f * lev[code]));
     }
 }
 
@@ -651,7 +664,8 @@ __device__ __forceinline__ int floor_to_int(float v) {
 // At most 168 VGPRs (three waves per SIMD): the input rows come through LDS,
 // so no registers hold the next tile, and the D masks are read from LDS.
 // Measured on the 2^20 x 256 fp16 2+1-bit workload: 0.146 ms with the rows
-// prefetched into registers (222 VGPRs, two waves per SIMD), 0.131 ms staged.
+// prefetched into registers (222 VGPRs, two waves per SIMD), 0.131 ms staged,
+// 0.124 ms with the pre-shifted code table and bounded buffer copies.
 template <int CB>
 __global__ __launch_bounds__(kBlock, 3) void k_residual_quantize_mfma256(const QuantArgs a) {
     constexpr int D = 256, VPB = kWaves * kR256Rows;
@@ -661,7 +675,7 @@ __global__ __launch_bounds__(kBlock, 3) void k_residual_quantize_mfma256(const Q
     // the nearest-level table: the floor-indexed one for 1- and 2-bit codes,
     // the threshold-carrying one otherwise
     __shared__ u32x4_t lutl[kEven ? 1 : LT::kCells];
-    __shared__ uint2 etab[kEvenCells];
+    __shared__ uint2 etab[kEven ? 8 : 1][kEvenCells];
     __shared__ __attribute__((aligned(16))) char xtile[kWaves][kR256TileBytes];
     __shared__ __attribute__((aligned(16))) uint8_t ctile[kWaves][kR256Rows * CROW];
     __shared__ __attribute__((aligned(16))) uint8_t stile[kWaves][kR256Rows * SROW];
@@ -759,6 +773,8 @@ __global__ __launch_bounds__(kBlock, 3) void k_residual_quantize_mfma256(const Q
         const float nrm = sqrtf(ss);
         const float inv16 = ss > 0.0f ? 16.0f / nrm : 0.0f;
         const float ev = inv16 * estep;
+        // a zero vector has residual 0 everywhere, whose sign bit is +1
+        const uint32_t live = ss > 0.0f ? 0xFFFFFFFFu : 0u;
         float r2 = 0.0f, r1 = 0.0f;
 #pragma unroll
         for (int blk = 0; blk < 8; ++blk) {
@@ -769,10 +785,10 @@ __global__ __launch_bounds__(kBlock, 3) void k_residual_quantize_mfma256(const Q
                 uint2 e[8];
 #pragma unroll
                 for (int t = 0; t < 8; ++t)
-                    e[t] = etab[floor_to_int(fmaf(c[blk][t >> 2][t & 3], ev, eoff)) + kEvenLow];
+                    e[t] = etab[t][floor_to_int(fmaf(c[blk][t >> 2][t & 3], ev, eoff)) + kEvenLow];
+                code = (e[0].x | e[1].x | e[2].x) | (e[3].x | e[4].x | e[5].x) | (e[6].x | e[7].x);
 #pragma unroll
                 for (int t = 7; t >= 0; --t) {
-                    code |= e[t].x << (CB * t);
                     const float rho = fmaf(c[blk][t >> 2][t & 3], inv16, -__builtin_bit_cast(float, e[t].y));
                     r2 = fmaf(rho, rho, r2);
                     r1 += fabsf(rho);
@@ -798,11 +814,15 @@ __global__ __launch_bounds__(kBlock, 3) void k_residual_quantize_mfma256(const Q
                     neg = (neg << 1) | (__builtin_bit_cast(uint32_t, rho) >> 31);
                 }
             }
-            // a zero vector has residual 0 everywhere, whose sign bit is +1
-            const uint32_t sbits = ss > 0.0f ? (~neg & 0xFFu) : 0xFFu;
+            // ~(neg & live) in one v_bitop3 (truth table over bit pairs:
+            // 1 unless both are 1)
+            const uint32_t sbits = __builtin_amdgcn_bitop3_b32(neg, live, 0u, 0x3F);
             uint8_t *cp = ct + j * CROW + CB * (4 * blk + g);
+            if constexpr (CB == 2)
+                *reinterpret_cast<uint16_t *>(cp) = (uint16_t)code;
+            else
 #pragma unroll
-            for (int by = 0; by < CB; ++by) cp[by] = (uint8_t)(code >> (8 * by));
+                for (int by = 0; by < CB; ++by) cp[by] = (uint8_t)(code >> (8 * by));
             st[j * SROW + 4 * blk + g] = (uint8_t)sbits;
         }
         r2 += __shfl_xor(r2, 16);
