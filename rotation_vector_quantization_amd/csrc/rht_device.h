@@ -20,6 +20,11 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63u; }
 
+// Word 3 of a CDNA raw buffer resource: data format 32 bits, no swizzle, no
+// index stride (the offsets are byte offsets, range-checked against the
+// resource's size: a load past it returns zeros).
+constexpr int kRawBufferWord3 = 0x00020000;
+
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
                                   false);

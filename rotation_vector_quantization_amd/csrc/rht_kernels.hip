@@ -605,10 +605,6 @@ __device__ __forceinline__ floatx4 mfma16x16x32(u32x4_t a, u32x4_t b, floatx4 c)
 // the end read as zeros (they are transformed but never stored).
 typedef __attribute__((address_space(3))) void lds_void_r;
 constexpr int kR256TileBytes = kR256Rows * 512;
-// Word 3 of a CDNA raw buffer resource: data format 32 bits, no swizzle, no
-// index stride (the offsets are byte offsets, range-checked against the
-// resource's size).
-constexpr int kRawBufferWord3 = 0x00020000;
 
 __device__ __forceinline__ void stage_res256(const uint16_t *x, int64_t row0, int64_t n, char *lds_tile,
                                              uint32_t lane) {
