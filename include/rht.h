@@ -13,7 +13,7 @@
  *   - Array arguments are DEVICE pointers owned by the caller (for example
  *     torch tensors); the library never allocates, frees or keeps them.
  *   - Row-major: one contiguous row per vector.  n = number of vectors (rows),
- *     d = row length, a power of two with 32 <= d <= 4096.
+ *     d = row length, a power of two with 16 <= d <= 4096.
  *   - Codes are an LSB-first bitstream per row: coordinate i occupies bits
  *     [b*i, b*i + b) of its row; a row of b-bit codes is b*d/8 bytes.
  *   - Every device pointer must be 16-byte aligned.
@@ -115,7 +115,7 @@ rht_status rht_dequantize(const uint8_t *codes, const float *scale, int64_t n, i
  *   x         [n][d] of type xt.
  *   codes     [n][(bits-1)*d/8] written;  signs [n][d/8] written;
  *   norms     [n] fp32 ||x||_2 written;   res_scale [n] fp32 S_r written.
- * Requires d >= 32 and (bits-1)*d/8 bytes per row; bits = 4 uses 3-bit codes. */
+ * (bits-1)*d/8 code bytes per row; bits = 4 uses 3-bit codes. */
 rht_status rht_residual_quantize(const void *x, rht_dtype xt, int64_t n, int32_t d, int32_t bits,
                                  uint64_t seed, uint8_t *codes, uint8_t *signs, float *norms,
                                  float *res_scale, void *stream);

@@ -7,7 +7,7 @@
 
 namespace rht {
 
-constexpr int kMinD = 32;
+constexpr int kMinD = 16;
 constexpr int kMaxD = 4096;
 
 // What a quantize launch computes.
@@ -109,6 +109,12 @@ hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
 // Device address of the current device's attention scratch array
 // (kAttnScratchBytes), looked up on the first call per device.
 hipError_t attention_scratch(void **ptr);
+
+// d = 16: one lane per vector, the transform in registers (launch_quantize,
+// launch_dequantize and launch_score pick them for that d).
+hipError_t launch_quantize_d16(bool f16, int bits, Kind kind, const QuantArgs &a, hipStream_t s);
+hipError_t launch_dequantize_d16(bool f16out, int bits, Kind kind, const DequantArgs &a, hipStream_t s);
+hipError_t launch_score_d16(int bits, bool residual, const ScoreArgs &a, hipStream_t s);
 
 // The d = 128, fp16, 4-bit MSE encoder and decoder with the H_32 factor on
 // MFMA (launch_quantize / launch_dequantize pick them for that case).

@@ -276,10 +276,13 @@ __device__ __forceinline__ u32x4_t lut_cell(const u32x4_t *lut, float y16) {
     if constexpr (CLAMP) b = min(max(b, 0x4B000000), 0x4B000000 + NCELL - 1);
     return lut[b - 0x4B000000];
 }
+// (Elements are copied to scalars before bit_cast: this compiler's bit_cast of
+// an ext-vector element itself can read another element.)
 __device__ __forceinline__ uint32_t code_in_cell(const u32x4_t &e, float y16, float &l16) {
-    const bool up = y16 >= __builtin_bit_cast(float, e[0]);
-    l16 = __builtin_bit_cast(float, up ? e[3] : e[2]);
-    return e[1] + (up ? 1u : 0u);
+    const uint32_t t = e[0], base = e[1], lo = e[2], hi = e[3];
+    const bool up = y16 >= __builtin_bit_cast(float, t);
+    l16 = __builtin_bit_cast(float, up ? hi : lo);
+    return base + (up ? 1u : 0u);
 }
 template <int NCELL, int OFF, bool CLAMP>
 __device__ __forceinline__ uint32_t nearest_code_lev_t(const u32x4_t *lut, float y16, float &l16) {
@@ -2001,6 +2004,7 @@ hipError_t score_d(int bits, bool residual, const ScoreArgs &a, hipStream_t s) {
 
 hipError_t launch_quantize(int d, bool f16, int bits, Kind kind, const QuantArgs &a, hipStream_t s) {
     switch (d) {
+    case 16: return launch_quantize_d16(f16, bits, kind, a, s);
     case 32: return quant_d<32>(f16, bits, kind, a, s);
     case 64: return quant_d<64>(f16, bits, kind, a, s);
     case 128: return quant_d<128>(f16, bits, kind, a, s);
@@ -2015,6 +2019,7 @@ hipError_t launch_quantize(int d, bool f16, int bits, Kind kind, const QuantArgs
 
 hipError_t launch_dequantize(int d, bool f16out, int bits, Kind kind, const DequantArgs &a, hipStream_t s) {
     switch (d) {
+    case 16: return launch_dequantize_d16(f16out, bits, kind, a, s);
     case 32: return dequant_d<32>(f16out, bits, kind, a, s);
     case 64: return dequant_d<64>(f16out, bits, kind, a, s);
     case 128: return dequant_d<128>(f16out, bits, kind, a, s);
@@ -2029,6 +2034,7 @@ hipError_t launch_dequantize(int d, bool f16out, int bits, Kind kind, const Dequ
 
 hipError_t launch_score(int d, int bits, bool residual, const ScoreArgs &a, hipStream_t s) {
     switch (d) {
+    case 16: return launch_score_d16(bits, residual, a, s);
     case 32: return score_d<32>(bits, residual, a, s);
     case 64: return score_d<64>(bits, residual, a, s);
     case 128: return score_d<128>(bits, residual, a, s);

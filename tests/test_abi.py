@@ -76,7 +76,7 @@ def _q(lib, x=FAKE, xt=0, n=1, d=128, bits=4, mode=0, codes=FAKE, scale=FAKE):
 
 def test_quantize_validation_order(lib):
     assert _q(lib, n=-1, d=100) == E_COUNT
-    for d in (0, 16, 100, 8192, -128):
+    for d in (0, 8, 100, 8192, -128):
         assert _q(lib, d=d) == E_DIM
     for b in (0, 5, -1):
         assert _q(lib, bits=b) == E_BITS
@@ -111,7 +111,7 @@ def test_other_entry_points_validate(lib):
     assert L.rht_score(FAKE, 65, FAKE, FAKE, 1, 128, 4, 1, FAKE, None) == E_COUNT
     assert L.rht_score(FAKE, -1, FAKE, FAKE, 1, 128, 4, 1, FAKE, None) == E_COUNT
     assert L.rht_score(FAKE, 8, FAKE, FAKE, 1, 8192, 4, 1, FAKE, None) == E_DIM
-    assert L.rht_score(FAKE, 8, FAKE, FAKE, 1, 16, 4, 1, FAKE, None) == E_DIM
+    assert L.rht_score(FAKE, 8, FAKE, FAKE, 1, 8, 4, 1, FAKE, None) == E_DIM
     assert L.rht_score(FAKE, 8, FAKE, FAKE, 1, 128, 0, 1, FAKE, None) == E_BITS
     assert L.rht_score(0, 0, 0, 0, 5, 128, 4, 1, 0, None) == OK
     assert L.rht_codebook(0, None, None) == E_BITS
@@ -199,7 +199,7 @@ def test_sign_and_residual_score_validation(lib):
     S = lib.rht_score_sign
     assert S(FAKE, 65, FAKE, FAKE, 10, 128, 1, FAKE, None) == E_COUNT
     assert S(FAKE, 4, FAKE, FAKE, -1, 128, 1, FAKE, None) == E_COUNT
-    for d in (16, 100, 8192):
+    for d in (8, 100, 8192):
         assert S(FAKE, 4, FAKE, FAKE, 10, d, 1, FAKE, None) == E_DIM
     assert S(0, 0, 0, 0, 10, 128, 1, 0, None) == OK
     assert S(FAKE, 4, 0, FAKE, 10, 128, 1, FAKE, None) == E_NULL
@@ -215,7 +215,7 @@ def test_sign_and_residual_score_validation(lib):
 
 
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
-@pytest.mark.parametrize("d", [32, 128, 1024, 4096])
+@pytest.mark.parametrize("d", [16, 32, 128, 1024, 4096])
 def test_beta_codebook_matches_oracle(lib, bits, d):
     lv, th = rht.rht_codebook_beta(bits, d)
     olv, oth, _, _ = oracle.lloyd_max_beta(bits, d)
@@ -229,5 +229,5 @@ def test_beta_codebook_matches_oracle(lib, bits, d):
 def test_beta_codebook_validation(lib):
     f = lambda b, d: lib.rht_codebook_beta(b, d, None, None)
     assert f(0, 128) == E_BITS and f(5, 128) == E_BITS
-    assert f(4, 100) == E_DIM and f(4, 16) == E_DIM and f(4, 8192) == E_DIM
+    assert f(4, 100) == E_DIM and f(4, 8) == E_DIM and f(4, 8192) == E_DIM
     assert f(4, 128) == OK

@@ -133,7 +133,7 @@ def check_drive(x, d, seed, what):
 
 # (d, bits) of the MSE encoders: the KV-block MFMA kernels (128, 4) and the
 # generic ones
-MSE_F16 = [(128, 4), (128, 2), (1024, 4), (256, 3)]
+MSE_F16 = [(128, 4), (128, 2), (1024, 4), (256, 3), (16, 3), (16, 4)]
 
 
 @pytest.mark.parametrize("d,bits", MSE_F16)
@@ -149,7 +149,7 @@ def test_mse_near_max_f16_rows(d, bits):
 
 
 @pytest.mark.parametrize("scale", [1e17, 1e-18])
-@pytest.mark.parametrize("d,bits", [(128, 4), (1024, 4), (256, 2)])
+@pytest.mark.parametrize("d,bits", [(128, 4), (1024, 4), (256, 2), (16, 2)])
 def test_mse_scaled_f32_rows(d, bits, scale):
     x = scaled_f32_rows(333, d, np.random.default_rng(d + int(np.log10(scale)) + 40), scale)
     assert np.all(np.isfinite((x.astype(np.float64) ** 2).sum(1).astype(np.float32)))
@@ -158,18 +158,18 @@ def test_mse_scaled_f32_rows(d, bits, scale):
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
-def test_residual_contract_edges(bits):
-    d = 256
-    rng = np.random.default_rng(90 + bits)
-    check_residual(subnormal_f16_rows(250, d, rng), d, bits, 21, "residual subnormal fp16 b=%d" % bits)
-    check_residual(near_max_f16_rows(250, d, rng), d, bits, 22, "residual near-65504 fp16 b=%d" % bits,
+@pytest.mark.parametrize("d", [256, 16])
+def test_residual_contract_edges(d, bits):
+    rng = np.random.default_rng(90 + bits + d)
+    check_residual(subnormal_f16_rows(250, d, rng), d, bits, 21, "residual subnormal fp16 d=%d b=%d" % (d, bits))
+    check_residual(near_max_f16_rows(250, d, rng), d, bits, 22, "residual near-65504 fp16 d=%d b=%d" % (d, bits),
                    f16_decode=False)
     for scale in (1e17, 1e-18):
-        check_residual(scaled_f32_rows(250, d, rng, scale), d, bits, 23, "residual fp32 x %g b=%d" % (scale, bits),
-                       f16_decode=False)
+        check_residual(scaled_f32_rows(250, d, rng, scale), d, bits, 23,
+                       "residual fp32 x %g d=%d b=%d" % (scale, d, bits), f16_decode=False)
 
 
-@pytest.mark.parametrize("d", [128, 1024])
+@pytest.mark.parametrize("d", [16, 128, 1024])
 def test_drive_contract_edges(d):
     rng = np.random.default_rng(300 + d)
     check_drive(subnormal_f16_rows(200, d, rng), d, 31, "drive subnormal fp16 d=%d" % d)

@@ -82,7 +82,7 @@ def gpu_quantize(x, bits, seed, mode=0):
 # ------------------------------------------------------------------ MSE code
 @pytest.mark.parametrize("xdt", ["f32", "f16"])
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
-@pytest.mark.parametrize("d", [32, 64, 128, 256, 512, 1024, 2048, 4096])
+@pytest.mark.parametrize("d", [16, 32, 64, 128, 256, 512, 1024, 2048, 4096])
 def test_mse_roundtrip_grid(d, bits, xdt):
     n = 777 if d <= 512 else 203
     seed = 1000 + d + bits
@@ -104,7 +104,7 @@ def test_mse_roundtrip_grid(d, bits, xdt):
 # ------------------------------------------------------------------ EDEN scale
 @pytest.mark.parametrize("xdt", ["f32", "f16"])
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
-@pytest.mark.parametrize("d", [32, 128, 256, 1024, 4096])
+@pytest.mark.parametrize("d", [16, 32, 128, 256, 1024, 4096])
 def test_eden_grid(d, bits, xdt):
     n = 555 if d <= 1024 else 131
     seed = 3000 + d + bits
@@ -128,7 +128,7 @@ def test_eden_grid(d, bits, xdt):
 # ------------------------------------------------------------------ finite-d codebook
 @pytest.mark.parametrize("xdt", ["f32", "f16"])
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
-@pytest.mark.parametrize("d", [32, 128, 1024])
+@pytest.mark.parametrize("d", [16, 32, 128, 1024])
 def test_beta_codebook_grid(d, bits, xdt):
     # d = 128, fp16, 4 bits runs the MFMA KV-block kernels with this codebook
     n = 555
@@ -150,7 +150,7 @@ def test_beta_codebook_grid(d, bits, xdt):
 # ------------------------------------------------------------------ DRIVE
 @pytest.mark.parametrize("mode", [rht.SCALE_SIGN_BIASED, rht.SCALE_SIGN_UNBIASED])
 @pytest.mark.parametrize("xdt", ["f32", "f16"])
-@pytest.mark.parametrize("d", [32, 128, 1024, 4096])
+@pytest.mark.parametrize("d", [16, 32, 128, 1024, 4096])
 def test_drive_grid(d, xdt, mode):
     n = 555 if d <= 1024 else 131
     seed = 77 + d
@@ -203,7 +203,7 @@ def check_residual(x, bits, seed, codes, sg, norms, rs, rows=None, what="residua
 
 @pytest.mark.parametrize("xdt", ["f32", "f16"])
 @pytest.mark.parametrize("bits", [2, 3, 4])
-@pytest.mark.parametrize("d", [32, 128, 256, 4096])
+@pytest.mark.parametrize("d", [16, 32, 128, 256, 4096])
 def test_residual_grid(d, bits, xdt):
     n = 444 if d <= 256 else 97
     seed = 31 + d + bits
@@ -266,7 +266,7 @@ def test_residual_decode_arbitrary_inputs(bits, n):
 
 # ------------------------------------------------------------------ scoring
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
-@pytest.mark.parametrize("d", [32, 64, 128, 256, 512, 1024, 2048, 4096])
+@pytest.mark.parametrize("d", [16, 32, 64, 128, 256, 512, 1024, 2048, 4096])
 @pytest.mark.parametrize("m,n", [(1, 1), (17, 100), (64, 1037), (33, 31), (40, 65), (32, 64)])
 def test_score_grid(d, bits, m, n):
     seed = 5 + d

@@ -54,7 +54,8 @@ def xcode(dt):
 
 
 @pytest.mark.parametrize("bits", [1, 3, 4])
-@pytest.mark.parametrize("d,dt", [(128, np.float16), (128, np.float32), (256, np.float16), (1024, np.float32)])
+@pytest.mark.parametrize("d,dt", [(16, np.float16), (16, np.float32), (128, np.float16), (128, np.float32),
+                                  (256, np.float16), (1024, np.float32)])
 def test_mse_row_counts(d, dt, bits):
     seed = 500 + d + bits
     X = small_input(max(EDGES), d, dt, seed)
@@ -83,7 +84,7 @@ def test_mse_row_counts(d, dt, bits):
 
 @pytest.mark.parametrize("bits", [2, 4])
 @pytest.mark.parametrize("mode", [rht.SCALE_EDEN, rht.SCALE_NORM_BETA])
-@pytest.mark.parametrize("d,dt", [(128, np.float16), (1024, np.float32)])
+@pytest.mark.parametrize("d,dt", [(16, np.float16), (128, np.float16), (1024, np.float32)])
 def test_eden_and_finite_d_row_counts(d, dt, mode, bits):
     seed = 700 + d + bits + mode
     X = small_input(max(EDGES), d, dt, seed)
@@ -118,15 +119,16 @@ def test_eden_and_finite_d_row_counts(d, dt, mode, bits):
 
 
 @pytest.mark.parametrize("mode", [rht.SCALE_SIGN_BIASED, rht.SCALE_SIGN_UNBIASED])
-def test_drive_row_counts(mode):
-    d, dt, seed = 1024, np.float32, 77
+@pytest.mark.parametrize("d,dt", [(16, np.float16), (1024, np.float32)])
+def test_drive_row_counts(d, dt, mode):
+    seed = 77
     X = small_input(max(EDGES), d, dt, seed)
     for n in EDGES:
-        say("drive row counts mode=%d n=%d" % (mode, n))
+        say("drive row counts d=%d mode=%d n=%d" % (d, mode, n))
         x = X[:n]
         xd = to_dev(x)
         bits, S = padded(n, d // 8), padded(n, 4)
-        rht.rht_quantize(xd.data_ptr(), rht.F32, n, d, 1, mode, seed, bits.data_ptr(), S.data_ptr(), stream())
+        rht.rht_quantize(xd.data_ptr(), xcode(dt), n, d, 1, mode, seed, bits.data_ptr(), S.data_ptr(), stream())
         gb, gS = split(bits, n, d // 8), split(S, n, 4, np.float32)[:, 0]
         ob, oS = oracle.sign_quantize(x, mode == rht.SCALE_SIGN_UNBIASED, seed)
         check_codes(unpack(gb, 1, d), unpack(ob, 1, d),
@@ -140,7 +142,7 @@ def test_drive_row_counts(mode):
 
 
 @pytest.mark.parametrize("bits", [2, 3])
-@pytest.mark.parametrize("d,dt", [(256, np.float16), (128, np.float32)])
+@pytest.mark.parametrize("d,dt", [(16, np.float16), (16, np.float32), (256, np.float16), (128, np.float32)])
 def test_residual_row_counts(d, dt, bits):
     seed = 900 + d + bits
     X = small_input(max(EDGES), d, dt, seed)
@@ -169,7 +171,7 @@ SCORE_N = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 511, 512, 513, 1025]
 
 @pytest.mark.parametrize("kind", ["mse4", "mse2", "sign", "res3"])
 @pytest.mark.parametrize("m", [1, 32, 33, 64])
-@pytest.mark.parametrize("d", [32, 64, 128, 1024])
+@pytest.mark.parametrize("d", [16, 32, 64, 128, 1024])
 def test_score_key_counts(d, m, kind):
     """Logits [m][n] for key counts around the 32-key tiles and 64-key items; the
     buffer carries sentinel bytes past m * n.  Every logit <q, k^> must be within

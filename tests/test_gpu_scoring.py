@@ -50,7 +50,7 @@ def check(got, ref, what):
     assert np.all(got[:, ~nz] == 0)
 
 
-ALL_D = [32, 64, 128, 256, 512, 1024, 2048, 4096]
+ALL_D = [16, 32, 64, 128, 256, 512, 1024, 2048, 4096]
 
 
 @pytest.mark.parametrize("unbiased", [False, True])
