@@ -134,7 +134,7 @@ rht_status rht_residual_dequantize(const uint8_t *codes, const uint8_t *signs, c
  * attention scale, no softmax.
  *   q      [m][d] fp32, 0 <= m <= 64;  codes [n][bits*d/8], norms [n] fp32 as
  *          written by rht_quantize(..., RHT_SCALE_NORM, seed, ...).
- *   logits [m][n] fp32 written.  d a power of two in [32, 4096]; bits 1..4. */
+ *   logits [m][n] fp32 written.  d a power of two in [16, 4096]; bits 1..4. */
 rht_status rht_score(const float *q, int32_t m, const uint8_t *codes, const float *norms, int64_t n,
                      int32_t d, int32_t bits, uint64_t seed, float *logits, void *stream);
 
@@ -146,7 +146,7 @@ rht_status rht_score(const float *q, int32_t m, const uint8_t *codes, const floa
  *   logits[j][k] = (S_k / sqrt(d)) * sum_i (H D q_j)_i sigma_{k,i},  sigma = +-1.
  * With the unbiased scale their mean over rotation seeds is <q_j, x_k>.
  *   q [m][d] fp32, 0 <= m <= 64; bits [n][d/8]; scale [n] fp32;
- *   logits [m][n] fp32 written.  d a power of two in [32, 4096]. */
+ *   logits [m][n] fp32 written.  d a power of two in [16, 4096]. */
 rht_status rht_score_sign(const float *q, int32_t m, const uint8_t *bits, const float *scale, int64_t n,
                           int32_t d, uint64_t seed, float *logits, void *stream);
 
@@ -156,7 +156,7 @@ rht_status rht_score_sign(const float *q, int32_t m, const uint8_t *bits, const 
  *                + (S_r,k / sqrt(d)) sum_i (H D q_j)_i sigma_{k,i}
  * = <q_j, x^_k> for the vectors rht_residual_dequantize returns.  Arguments
  * as written by rht_residual_quantize (total bits 2..4); q [m][d] fp32,
- * 0 <= m <= 64; logits [m][n] fp32 written; d a power of two in [32, 4096]. */
+ * 0 <= m <= 64; logits [m][n] fp32 written; d a power of two in [16, 4096]. */
 rht_status rht_residual_score(const float *q, int32_t m, const uint8_t *codes, const uint8_t *signs,
                               const float *norms, const float *res_scale, int64_t n, int32_t d, int32_t bits,
                               uint64_t seed, float *logits, void *stream);
@@ -232,7 +232,7 @@ rht_status rht_codebook(int32_t bits, float *levels, float *thresholds);
  * the Lloyd-Max quantizer of sqrt(d) times a coordinate of a uniformly
  * rotated unit vector ("Why rotation works": a Beta marginal), levels[2^bits]
  * ascending, thresholds[2^bits - 1] midpoints, the middle one 0.  bits 1..4,
- * d a power of two in [32, 4096].  Either pointer may be NULL. */
+ * d a power of two in [16, 4096].  Either pointer may be NULL. */
 rht_status rht_codebook_beta(int32_t bits, int32_t d, float *levels, float *thresholds);
 
 /* The diagonal D of the rotation for (seed, d): signs[i] = -1 when the top bit
