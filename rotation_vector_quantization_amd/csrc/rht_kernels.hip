@@ -1641,6 +1641,65 @@ __device__ __forceinline__ void score_tile(const uint2 *ptab, const u32x4_t *sta
     }
 }
 
+// The 32 queries q0 .. q0 + 31 of a block rotated (H D q), each scaled by
+// 2^e_q so that its largest |coordinate| lies in [2^14, 2^15), and split into
+// fp16 hi and lo parts: row q of `ah` / `al` (kQRow halves apart) holds them
+// for coordinates 0 .. 127; qinv[q] = 2^-e_q.  Four lanes per query, 32
+// consecutive coordinates each (the lanes of rotate_queries), and each lane
+// scales and splits its own coordinates, so the operands need no further
+// pass; queries past m repeat the last one.  after_load() runs once the
+// query loads are issued.
+constexpr int kQRow = 136;  // 272-byte rows: successive rows start four banks apart
+
+template <typename Hook>
+__device__ __forceinline__ void rotate_split_queries(const ScoreArgs &a, uint16_t *ah, uint16_t *al, float *qinv,
+                                                     int q0, Hook after_load) {
+    constexpr int D = 128, LPV = lanes_per_vec(D), E = D / LPV;
+    const uint32_t lane = lane_id(), q = lane % LPV, slot = lane / LPV, wave = threadIdx.x >> 6;
+    const int j = (int)(wave * (64 / LPV) + slot);  // query q0 + j; the block's first 32 are used
+    const uint64_t lsign = lane_sign_bits<D, E>(a.dsign, q);
+    const float fq = lane_factor(q);
+    float v[E];
+    {
+        uint32_t raw[Raw<D, false>::W], sw[Raw<D, false>::W];
+        load_raw<D, E, false>(a.q, q0 + j < a.m ? q0 + j : a.m - 1, q, raw);
+        after_load();
+        sign_words<D, false>(lsign, sw);
+        stage0<D, false>(raw, sw, v);
+    }
+    fwht_regs<E, 0>(v);
+    fwht_lanes<LPV>(v, q);
+    float mx = 0.0f;
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        v[r] *= fq;
+        mx = fmaxf(mx, fabsf(v[r]));
+    }
+#pragma unroll
+    for (int o = 1; o < LPV; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    int ex;
+    (void)frexpf(mx, &ex);
+    const int e = mx > 0.0f ? min(max(15 - ex, -126), 126) : 0;
+    if (j < 32) {
+        if (q == 0) qinv[j] = ldexpf(1.0f, -e);
+        uint32_t hw[E / 2], lw[E / 2];
+#pragma unroll
+        for (int r = 0; r < E; r += 2) {
+            const float v0 = ldexpf(v[r], e), v1 = ldexpf(v[r + 1], e);
+            const _Float16 a0 = (_Float16)v0, a1 = (_Float16)v1;
+            hw[r / 2] = pack_half2(a0, a1);
+            lw[r / 2] = pack_half2((_Float16)(v0 - (float)a0), (_Float16)(v1 - (float)a1));
+        }
+        uint4 *hrow = reinterpret_cast<uint4 *>(ah + j * kQRow + E * q);
+        uint4 *lrow = reinterpret_cast<uint4 *>(al + j * kQRow + E * q);
+#pragma unroll
+        for (int k = 0; k < E / 8; ++k) {
+            hrow[k] = make_uint4(hw[4 * k], hw[4 * k + 1], hw[4 * k + 2], hw[4 * k + 3]);
+            lrow[k] = make_uint4(lw[4 * k], lw[4 * k + 1], lw[4 * k + 2], lw[4 * k + 3]);
+        }
+    }
+}
+
 template <int D, int BITS, bool RES, bool EXACT>
 __global__ __launch_bounds__(kBlock) void k_score_mfma(const ScoreArgs a) {
     static_assert(D == 128, "a query half's operands stay in registers; code rows are whole 16-byte chunks");
@@ -1648,10 +1707,10 @@ __global__ __launch_bounds__(kBlock) void k_score_mfma(const ScoreArgs a) {
     constexpr int HC = D / 2;                 // coordinates per lane half
     constexpr int HW = HC * BITS / 32;        // code words per half row
     constexpr int ROWB = D * BITS / 8;        // code bytes per key
-    constexpr int QS = 33;                    // LDS row stride of the transposed queries
     constexpr int KI = 32 * kScoreTK;         // keys per wave item
-    __shared__ float qt[D * QS];              // this block's 32 queries
-    __shared__ float qmax[32];
+    // this block's 32 queries as the fp16 hi and lo parts of the A operands
+    __shared__ __attribute__((aligned(16))) uint16_t qah[32 * kQRow];
+    __shared__ __attribute__((aligned(16))) uint16_t qal[32 * kQRow];
     __shared__ __attribute__((aligned(16))) float qinv[32];  // 2^-e_q
     __shared__ uint2 ptab[1 << (2 * BITS)];   // code pair -> {hi parts, lo parts} of its two levels
     __shared__ u32x4_t stab[RES ? 256 : 1];   // sign byte -> eight +-1 halves
@@ -1698,39 +1757,19 @@ __global__ __launch_bounds__(kBlock) void k_score_mfma(const ScoreArgs a) {
         stab[sb] = u32x4_t{w[0], w[1], w[2], w[3]};
     }
     // the first item's keys are copied while the queries are rotated
-    rotate_queries<D, QS, 32>(a, qt, qmax, 32 * rh, [&] {
+    rotate_split_queries(a, qah, qal, qinv, 32 * rh, [&] {
         if (tile < ntiles) stage_keys<ROWB, RES>(a, tile, kc, ks, kn, lane);
     });
-    __syncthreads();
-    // e_q puts the largest |coordinate| of query q in [2^14, 2^15)
-    auto qexp = [&](int Q) {
-        int ex;
-        (void)frexpf(qmax[Q], &ex);
-        return qmax[Q] > 0.0f ? min(max(15 - ex, -126), 126) : 0;
-    };
-    if (threadIdx.x < 32) qinv[threadIdx.x] = ldexpf(1.0f, -qexp((int)threadIdx.x));
+    __syncthreads();  // every wave of the block reaches this barrier
 
-    // A operands of this block's query half: row i is query 32 rh + i (column i of qt)
+    // A operands of this block's query half: row i is query 32 rh + i; K slot t
+    // of lane half h in step s is coordinate HC h + 8 s + t
     u32x4_t Ah[S], Al[S];
-    {
-        const int Q = (int)i;
-        const int e = qexp(Q);
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            uint32_t hw[4], lw[4];
-#pragma unroll
-            for (int t = 0; t < 8; t += 2) {
-                const float v0 = ldexpf(qt[(HC * h + 8 * s + t) * QS + Q], e);
-                const float v1 = ldexpf(qt[(HC * h + 8 * s + t + 1) * QS + Q], e);
-                const _Float16 a0 = (_Float16)v0, a1 = (_Float16)v1;
-                hw[t / 2] = pack_half2(a0, a1);
-                lw[t / 2] = pack_half2((_Float16)(v0 - (float)a0), (_Float16)(v1 - (float)a1));
-            }
-            Ah[s] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
-            Al[s] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
-        }
+    for (int s = 0; s < S; ++s) {
+        Ah[s] = *reinterpret_cast<const u32x4_t *>(qah + i * kQRow + HC * h + 8 * s);
+        Al[s] = *reinterpret_cast<const u32x4_t *>(qal + i * kQRow + HC * h + 8 * s);
     }
-    __syncthreads();  // qinv; every wave of the block reaches this barrier
     if (tile >= ntiles) return;
 
     uint32_t w0[HW], w1[HW], sg0[2] = {0u, 0u}, sg1[2] = {0u, 0u};
