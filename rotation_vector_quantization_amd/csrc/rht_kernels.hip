@@ -1648,7 +1648,7 @@ __device__ __forceinline__ void score_tile(const uint2 *ptab, const u32x4_t *sta
 // consecutive coordinates each (the lanes of rotate_queries), and each lane
 // scales and splits its own coordinates, so the operands need no further
 // pass; queries past m repeat the last one.  after_load() runs once the
-// query loads are issued.
+// query rows are in registers.
 constexpr int kQRow = 136;  // 272-byte rows: successive rows start four banks apart
 
 template <typename Hook>
@@ -1663,10 +1663,18 @@ __device__ __forceinline__ void rotate_split_queries(const ScoreArgs &a, uint16_
     {
         uint32_t raw[Raw<D, false>::W], sw[Raw<D, false>::W];
         load_raw<D, E, false>(a.q, q0 + j < a.m ? q0 + j : a.m - 1, q, raw);
-        after_load();
         sign_words<D, false>(lsign, sw);
         stage0<D, false>(raw, sw, v);
     }
+    // what after_load() issues stays behind every use of the query loads, so their
+    // waits do not also cover it
+    static_assert(E % 8 == 0, "eight values per ordering statement");
+#pragma unroll
+    for (int k = 0; k < E; k += 8)
+        asm volatile("" ::"v"(v[k]), "v"(v[k + 1]), "v"(v[k + 2]), "v"(v[k + 3]), "v"(v[k + 4]), "v"(v[k + 5]),
+                     "v"(v[k + 6]), "v"(v[k + 7])
+                     : "memory");
+    after_load();
     fwht_regs<E, 0>(v);
     fwht_lanes<LPV>(v, q);
     float mx = 0.0f;

@@ -254,8 +254,9 @@ __device__ __forceinline__ void stage_codes(const DequantArgs &a, int64_t row0, 
 // tile began by waiting for the previous tile's stores to complete (decoder on
 // the KV block, two boxes: 0.520 -> 0.513 ms and 0.514-0.516 -> 0.512-0.513 ms).  The staged code reads then sit in the
 // same asm block as that wait: the compiler would otherwise put a full wait in
-// front of ordinary LDS reads that follow direct copies.  This tile's stores
-// need no row check.
+// front of ordinary LDS reads that follow direct copies.  Its outputs are
+// early-clobber: no read's data register may be an address register of a
+// later read in the block.  This tile's stores need no row check.
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) const char lds_cchar;
 template <bool WHOLE>
@@ -276,7 +277,7 @@ __device__ __forceinline__ void dequantize_tile128(const DequantArgs &a, const u
                      "ds_read_b64 %3, %8\n\t"
                      "ds_read_b32 %4, %9\n\t"
                      "s_waitcnt lgkmcnt(0)"
-                     : "=v"(r0), "=v"(r1), "=v"(r2), "=v"(r3), "=v"(scale)
+                     : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(scale)
                      : "v"(base + 16 * c_chunk(j, 0) + 8 * h), "v"(base + 16 * c_chunk(j, 1) + 8 * h),
                        "v"(base + 16 * c_chunk(j, 2) + 8 * h), "v"(base + 16 * c_chunk(j, 3) + 8 * h),
                        "v"(base + kScaleOff + 4 * j)
