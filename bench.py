@@ -13,7 +13,9 @@ slower of the two kernels, from HIP events on the stream the kernels run on;
 algorithmic bytes are 256 B in + 64 B codes + 4 B norm per vector for the
 encoder and the same 324 B for the decoder.  `shape_ceiling` times trivial
 streaming kernels with each direction's exact traffic (the achievable
-ceiling of these shapes).  `cpu_baseline` times the oracle on every host
+ceiling of these shapes); the two 4-bit scoring rows carry the same for
+their own traffic (`other_workloads.score.shape_ceiling`,
+`other_workloads.score_large.shape_ceiling`).  `cpu_baseline` times the oracle on every host
 thread over the whole K tensor (and on one thread over a bounded sample).
 """
 import argparse
@@ -162,7 +164,7 @@ def stats(ms):
             "ms_min": float(np.min(ms)), "ms_max": float(np.max(ms))}
 
 
-def other_workloads(torch, rht, dev, stream):
+def other_workloads(torch, rht, dev, stream, with_ceiling=True):
     """The other hot-path rows, each at its full workload size: DRIVE 1-bit
     (65536 x 1024 fp32, both scales), the residual chain (2^20 x 256 fp16,
     2+1 bits) and rotated-domain scoring (131072 4-bit keys x 64 queries).
@@ -243,6 +245,8 @@ def other_workloads(torch, rht, dev, stream):
                                "keys_per_s": nk / (sms / 1e3), "TFLOP_per_s": tfs,
                                "algorithmic_bytes": sbytes, "GB_per_s": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS,
                                "bound": "hbm"})
+    if with_ceiling:
+        out["score"]["shape_ceiling"] = score_ceiling(torch, stream, cs, ns, ls, nk, m)
     del cs, ns, ls
 
     # the same keys as 1-bit sign codes (unbiased scale) and as a 2+1-bit residual chain
@@ -285,6 +289,8 @@ def other_workloads(torch, rht, dev, stream):
                                      "keys_per_s": nl / (ms / 1e3), "TFLOP_per_s": 2.0 * m * nl * d5 / (ms / 1e3) / 1e12,
                                      "algorithmic_bytes": alg, "GB_per_s": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS,
                                      "bound": "hbm"})
+    if with_ceiling:
+        out["score_large"]["shape_ceiling"] = score_ceiling(torch, stream, [cl], [nlr], [ll], nl, m)
     del cl, nlr, ll
     return out
 
@@ -414,6 +420,34 @@ def ceiling(torch, dev, stream, xk, ck, nk, yk, n):
                       "bytes_per_launch": per_launch}
     del c2, n2
     return out
+
+
+def score_ceiling(torch, stream, codes, norms, logits, n, m):
+    """The trivial kernel with the 4-bit scorer's traffic (68 B read and m fp32
+    logits written per key) on the scorer's own buffer sets, at 1-4 blocks of
+    256 threads per CU; the fastest is the achievable ceiling of that shape."""
+    import ctypes
+
+    import rotation_vector_quantization_amd.build as rb
+
+    if not os.path.exists(rb.CEIL_LIB):
+        return None
+    L = ctypes.CDLL(rb.CEIL_LIB)
+    vp = ctypes.c_void_p
+    L.ceiling_score_shape.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, vp]
+    sh = stream.cuda_stream
+    sweep = {}
+    for bpc in (1, 2, 3, 4):
+        fn = lambda i: L.ceiling_score_shape(codes[i].data_ptr(), norms[i].data_ptr(), logits[i].data_ptr(), n, m,
+                                             bpc, sh)
+        if fn(0) != 0:
+            raise RuntimeError("score-shape ceiling kernel failed to launch")
+        sweep[bpc] = float(np.median(time_launches(torch, stream, fn, len(codes))))
+    best = min(sweep, key=sweep.get)
+    per_launch = n * 68 + m * n * 4
+    gbs = per_launch / (sweep[best] / 1e3) / 1e9
+    return {"ms_median_by_blocks_per_cu": sweep, "best_blocks_per_cu": best, "ms_median": sweep[best],
+            "GB_per_s": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS, "bytes_per_launch": per_launch}
 
 
 def main():
@@ -585,7 +619,7 @@ def main():
         del xk, xv, ck, cv, nk, nv, yk, yv
         torch.cuda.empty_cache()
         print("timing the DRIVE, residual and scoring workloads", file=sys.stderr, flush=True)
-        out["other_workloads"] = other_workloads(torch, rht, dev, stream)
+        out["other_workloads"] = other_workloads(torch, rht, dev, stream, not args.no_ceiling)
         out["other_workloads"]["attention"] = attn
         out["other_workloads"]["attention_k4v3"] = attn_k4v3
     if not args.no_cpu_baseline:
