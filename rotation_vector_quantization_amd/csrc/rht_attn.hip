@@ -618,8 +618,10 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int w = 0; w < 4; ++w) qp[ks][w][0] = qp[ks][w][1] = 0.0f;
-    for (int i = 0; i < a.m; ++i) {
-        const float2 qv = reinterpret_cast<const float2 *>(a.q + (head * a.m + i) * kAD)[lane];
+    // one query's rotation, scaling and hand-out of its operand words
+    auto rotate_query = [&](int i) {
+        const int iq = i < a.m ? i : a.m - 1;
+        const float2 qv = reinterpret_cast<const float2 *>(a.q + (head * a.m + iq) * kAD)[lane];
         const uint32_t sb = a.dsign_k[lane >> 4] >> ((2 * lane) & 31);
         float v0 = (sb & 1u) ? -qv.x : qv.x;
         float v1 = (sb & 2u) ? -qv.y : qv.y;
@@ -628,7 +630,7 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
         const float sc = mx > 0.0f ? pow2i(min(14 - exponent_above(mx), 126)) : 1.0f;
         v0 *= sc;
         v1 *= sc;
-        const bool mine = (uint32_t)i == j % (uint32_t)QG;
+        const bool mine = i < a.m && (uint32_t)i == j % (uint32_t)QG;
         if (mine) qscale_mine = sc;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
@@ -639,6 +641,15 @@ __global__ __launch_bounds__(kABlock) void k_attn_partial(const AttnArgs a) {
                 qp[ks][w][0] = mine ? p0 : qp[ks][w][0];
                 qp[ks][w][1] = mine ? p1 : qp[ks][w][1];
             }
+    };
+    if constexpr (QG == 4) {
+        // the four rotations unrolled (queries past m repeat the last one and
+        // are selected by no lane), so their shuffle chains overlap; with more
+        // queries the unrolled chains would not fit the registers
+#pragma unroll
+        for (int i = 0; i < QG; ++i) rotate_query(i);
+    } else {
+        for (int i = 0; i < a.m; ++i) rotate_query(i);
     }
     typename QueryOps<QG>::type qo;
 #pragma unroll
